@@ -1,0 +1,447 @@
+/*
+ * Plain CPU oracle for the decode-time sparse-attention block indexer
+ * (score plane -> per-row Top16 select -> merge of split-column Top16 lists).
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously-correct definition
+ * that the HIP library is checked against. Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg load it. It shares no source, header, table
+ * or helper with the HIP library, and the library never loads it.
+ *
+ * Sources (FlashInfer msa_ops API pages):
+ *   [P1] "flashinfer.msa_ops.msa_icp_decode_index_score_sharded": description
+ *        (written columns), index_q (token positions), index_k, block_table,
+ *        seq_lens, score_out (cols limits), page_size limits.
+ *   [P2] "flashinfer.msa_ops.prepare_msa_icp_indexer": decode chain
+ *        (score plane -> Top16 select -> owner merge); init_blocks/local_blocks
+ *        (forced begin/end blocks, sum at most 16).
+ *   [P3] "flashinfer.msa_ops.msa_icp_topk_select_publish": description (row =
+ *        16 raw scores + 16 ascending global ids, every row written including
+ *        padding rows); scores (K limit); num_valid_pages (global B128 block
+ *        counts).
+ *   OCP 8-bit Floating Point Specification (OFP8), E4M3 format: bias 7, no
+ *        infinities, S.1111.111 is NaN, exponent field 0 is subnormal.
+ *
+ * Readings where the pages leave a step open (both the oracle and the GPU path
+ * use them):
+ *   - block score = max over the block's keys at positions <= the token's
+ *     position of the raw q.k dot product; a block with no such key scores -inf;
+ *   - ranking = score descending, then lower block id; -0 and +0 compare equal;
+ *   - the Top16 row lists its entries by ascending id; unused slots hold
+ *     (score -inf, id -1);
+ *   - forced blocks of a row are [0, init) and [n - local, n) intersected with
+ *     the row's valid ids [0, n), n = num_valid_pages of the token.
+ *
+ * Arithmetic: every finite e4m3fn value is an integer multiple of 2^-9 of
+ * magnitude <= 448 = 229376 * 2^-9 < 2^18 * 2^-9. A product is then an integer
+ * multiple of 2^-18 below 2^36 units and a 128-term sum stays below 2^43 units,
+ * so dot products are accumulated exactly in int64 and rounded once to float32
+ * (round to nearest even) at the end.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_DIM 128   /* index head dimension [P1 index_q / index_k] */
+#define ORACLE_HEADS 4   /* index heads [P1 index_q; P2 num_index_heads] */
+#define ORACLE_BLOCK 128 /* keys per B128 block [P1 description; P3 num_valid_pages] */
+#define ORACLE_TOPK 16   /* Top16 row width [P3 description] */
+
+typedef struct {
+    float score[ORACLE_TOPK];
+    int32_t id[ORACLE_TOPK];
+} oracle_row;
+
+/* ------------------------------------------------------------------------ */
+/* E4M3FN decode (OCP OFP8 E4M3), built once into a 256-entry table.          */
+/* ------------------------------------------------------------------------ */
+
+static int g_table_ready = 0;
+static int64_t g_units[256];   /* value in units of 2^-9 (finite codes)      */
+static double g_value[256];    /* value as a double (NaN for the NaN codes)  */
+static int g_is_nan[256];
+
+static void build_e4m3fn_table(void)
+{
+    for (int code = 0; code < 256; ++code) {
+        int sign = (code >> 7) & 1;
+        int exponent = (code >> 3) & 0xF;
+        int mantissa = code & 0x7;
+        int64_t magnitude_units;
+        if (exponent == 0xF && mantissa == 0x7) {
+            /* S.1111.111 is the only NaN encoding; there are no infinities. */
+            g_is_nan[code] = 1;
+            g_units[code] = 0;
+            g_value[code] = NAN;
+            continue;
+        }
+        if (exponent == 0) {
+            /* subnormal: (mantissa / 8) * 2^(1 - 7) = mantissa * 2^-9 */
+            magnitude_units = mantissa;
+        } else {
+            /* normal: (1 + mantissa / 8) * 2^(exponent - 7)
+             *       = (8 + mantissa) * 2^(exponent - 10)
+             *       = (8 + mantissa) * 2^(exponent - 1) units of 2^-9 */
+            magnitude_units = (int64_t)(8 + mantissa) << (exponent - 1);
+        }
+        g_is_nan[code] = 0;
+        g_units[code] = sign ? -magnitude_units : magnitude_units;
+        g_value[code] = ldexp((double)magnitude_units, -9);
+        if (sign)
+            g_value[code] = -g_value[code];  /* keeps -0.0 for code 0x80 */
+    }
+    g_table_ready = 1;
+}
+
+static void ensure_table(void)
+{
+    if (!g_table_ready)
+        build_e4m3fn_table();
+}
+
+/* Fills values[256] with the decoded e4m3fn value of every byte code. */
+void oracle_e4m3fn_table(double* values)
+{
+    ensure_table();
+    for (int c = 0; c < 256; ++c)
+        values[c] = g_value[c];
+}
+
+/* ------------------------------------------------------------------------ */
+/* One dot product, exact. [P1 index_q, index_k: fp8 e4m3fn rows of 128]     */
+/* ------------------------------------------------------------------------ */
+
+/* Returns sum_i q[i]*k[i] in units of 2^-18 (exact); *abs_units receives
+ * sum_i |q[i]*k[i]| in the same units. Sets *has_nan if either row holds a
+ * NaN code. */
+static int64_t dot_units(const uint8_t* q, const uint8_t* k, int64_t* abs_units, int* has_nan)
+{
+    int64_t acc = 0, acc_abs = 0;
+    int nan = 0;
+    for (int i = 0; i < ORACLE_DIM; ++i) {
+        int64_t prod = g_units[q[i]] * g_units[k[i]];
+        acc += prod;
+        acc_abs += prod < 0 ? -prod : prod;
+        nan |= g_is_nan[q[i]] | g_is_nan[k[i]];
+    }
+    if (abs_units)
+        *abs_units = acc_abs;
+    if (has_nan)
+        *has_nan = nan;
+    return acc;
+}
+
+/* units of 2^-18 -> float32, rounded once (the double is exact: |x| < 2^53). */
+static float units_to_float(int64_t units)
+{
+    return (float)ldexp((double)units, -18);
+}
+
+/* Batched single dot products: out_f32[i] = fp32(q_i . k_i) rounded once,
+ * out_exact[i] = the exact value as a double (exact, see file header). */
+void oracle_dots(const uint8_t* q, const uint8_t* k, int64_t n, float* out_f32, double* out_exact)
+{
+    ensure_table();
+    for (int64_t i = 0; i < n; ++i) {
+        int nan = 0;
+        int64_t u = dot_units(q + i * ORACLE_DIM, k + i * ORACLE_DIM, NULL, &nan);
+        out_f32[i] = nan ? NAN : units_to_float(u);
+        out_exact[i] = nan ? NAN : ldexp((double)u, -18);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Score plane.                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Number of written columns of a request: its ceil(seq_len / 128) B128 blocks
+ * rounded up to a multiple of four [P1 description]. With every page's full
+ * rows on one device, a column is one global B128 block at both page sizes;
+ * at page_size 256 each page holds two blocks and
+ * roundup4(ceil(s/128)) == roundup4(2*ceil(s/256)) for every s, so counting
+ * two blocks per page of the request gives the same padded count. */
+int64_t oracle_written_columns(int64_t seq_len)
+{
+    if (seq_len <= 0)
+        return 0;
+    int64_t blocks = (seq_len + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+    return (blocks + 3) / 4 * 4;
+}
+
+/* Score of one plane element [P1 description, index_q, index_k, block_table]:
+ * q_row is the token's 128-byte head row, pos its position
+ * (seq_len - decode_query_len + j). Column c covers keys [128c, 128c + 128);
+ * key p lives at index_k[block_table_row[p / page_size], p % page_size, :].
+ * Visible keys: p < seq_len and p <= pos.
+ * *score = fp32(max visible dot) or -inf if no key is visible;
+ * *amax  = max over visible keys of sum_i |q_i k_i| (0 if none).
+ * Returns 0, or -1 if a needed block_table entry is outside [0, num_pages). */
+int oracle_score_element(const uint8_t* q_row, const uint8_t* index_k, int64_t num_pages,
+                         int32_t page_size, const int32_t* block_table_row, int64_t seq_len,
+                         int64_t pos, int64_t c, float* score, double* amax)
+{
+    ensure_table();
+    int have = 0, bad = 0;
+    int64_t best = 0, best_abs = 0;
+    for (int64_t p = c * ORACLE_BLOCK; p < (c + 1) * ORACLE_BLOCK; ++p) {
+        if (p >= seq_len || p > pos)
+            continue;
+        int64_t page = block_table_row[p / page_size];
+        if (page < 0 || page >= num_pages) {
+            bad = 1;
+            continue;
+        }
+        const uint8_t* key = index_k + ((page * page_size) + (p % page_size)) * ORACLE_DIM;
+        int64_t abs_units = 0;
+        int64_t u = dot_units(q_row, key, &abs_units, NULL);
+        if (!have || u > best)
+            best = u;
+        if (!have || abs_units > best_abs)
+            best_abs = abs_units;
+        have = 1;
+    }
+    *score = have ? units_to_float(best) : -INFINITY;
+    if (amax)
+        *amax = have ? ldexp((double)best_abs, -18) : 0.0;
+    return bad ? -1 : 0;
+}
+
+/* The whole plane [P1]: for request b, token j, head h, column
+ * c < min(written_columns(seq_len[b]), cols):
+ *   score_out[(b*dql + j), h, c] = oracle_score_element(...)
+ * Other columns are left as they are. amax_out (nullable) has the plane's
+ * shape and receives the per-element amax for written columns.
+ * Returns the number of elements that met an out-of-range block_table entry. */
+int64_t oracle_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                            int32_t decode_query_len, float* score_out, int32_t cols,
+                            double* amax_out)
+{
+    ensure_table();
+    int64_t bad = 0;
+    int64_t rows = (int64_t)batch * decode_query_len * ORACLE_HEADS;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t t = row / ORACLE_HEADS;
+        int64_t b = t / decode_query_len;
+        int64_t j = t % decode_query_len;
+        int64_t seq_len = seq_lens[b];
+        int64_t pos = seq_len - decode_query_len + j;
+        int64_t written = oracle_written_columns(seq_len);
+        if (written > cols)
+            written = cols;
+        const uint8_t* q_row = index_q + row * ORACLE_DIM;
+        for (int64_t c = 0; c < written; ++c) {
+            float s;
+            double a;
+            if (oracle_score_element(q_row, index_k, num_pages, page_size,
+                                     block_table + b * block_table_stride, seq_len, pos, c,
+                                     &s, &a) != 0)
+                ++bad;
+            score_out[row * cols + c] = s;
+            if (amax_out)
+                amax_out[row * cols + c] = a;
+        }
+    }
+    return bad;
+}
+
+/* Sampled elements: for each i, element (row[i], col[i]) of the plane
+ * (row = (b*dql + j)*4 + h). Same definition as oracle_score_decode. */
+int64_t oracle_score_sampled(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                             const int32_t* block_table, int64_t block_table_stride,
+                             const int32_t* seq_lens, int32_t page_size, int32_t decode_query_len,
+                             const int64_t* sample_rows, const int64_t* sample_cols,
+                             int64_t n_samples, float* score_out, double* amax_out)
+{
+    ensure_table();
+    int64_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : bad)
+    for (int64_t i = 0; i < n_samples; ++i) {
+        int64_t row = sample_rows[i];
+        int64_t t = row / ORACLE_HEADS;
+        int64_t b = t / decode_query_len;
+        int64_t j = t % decode_query_len;
+        int64_t seq_len = seq_lens[b];
+        int64_t pos = seq_len - decode_query_len + j;
+        float s;
+        double a;
+        if (oracle_score_element(index_q + row * ORACLE_DIM, index_k, num_pages, page_size,
+                                 block_table + b * block_table_stride, seq_len, pos,
+                                 sample_cols[i], &s, &a) != 0)
+            ++bad;
+        score_out[i] = s;
+        if (amax_out)
+            amax_out[i] = a;
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top16 select and merge [P3 description; P2 init_blocks/local_blocks].     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float score;
+    int32_t id;
+} entry;
+
+/* Ranking: higher score first; equal scores (-0 == +0 as floats) -> lower id. */
+static int rank_cmp(const void* pa, const void* pb)
+{
+    const entry* a = (const entry*)pa;
+    const entry* b = (const entry*)pb;
+    if (a->score > b->score)
+        return -1;
+    if (a->score < b->score)
+        return 1;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+static int id_cmp(const void* pa, const void* pb)
+{
+    const entry* a = (const entry*)pa;
+    const entry* b = (const entry*)pb;
+    return (a->id > b->id) - (a->id < b->id);
+}
+
+/* Forced begin/end blocks of a row with n valid blocks: [0, init) and
+ * [n - local, n), both inside [0, n). */
+static int is_forced(int64_t id, int64_t n, int32_t init_blocks, int32_t local_blocks)
+{
+    if (id < 0 || id >= n)
+        return 0;
+    return id < init_blocks || id >= n - local_blocks;
+}
+
+/* Keeps the forced entries and the best (16 - n_forced_total) of the others
+ * by (score desc, id asc); writes them by ascending id, then pads with
+ * (-inf, -1). `cand` is sorted in place. */
+static void emit_row(entry* forced, int n_forced, int budget, entry* cand, int64_t n_cand,
+                     oracle_row* out)
+{
+    entry chosen[ORACLE_TOPK];
+    int m = 0;
+    for (int i = 0; i < n_forced; ++i)
+        chosen[m++] = forced[i];
+    qsort(cand, (size_t)n_cand, sizeof(entry), rank_cmp);
+    int64_t take = budget < n_cand ? budget : n_cand;
+    for (int64_t i = 0; i < take; ++i)
+        chosen[m++] = cand[i];
+    qsort(chosen, (size_t)m, sizeof(entry), id_cmp);
+    for (int i = 0; i < ORACLE_TOPK; ++i) {
+        out->score[i] = i < m ? chosen[i].score : -INFINITY;
+        out->id[i] = i < m ? chosen[i].id : -1;
+    }
+}
+
+/* Top16 select of every (token, head, range) row [P3 description]:
+ * scores [T, 4, cols]; range r covers columns [r*w, min((r+1)*w, cols)),
+ * w = ceil(cols / num_ranges). Valid ids are [0, n), n = num_valid_pages[t]
+ * clamped to [0, cols]. Forced ids of the range are kept, the rest ranked.
+ * out: [T, 4, num_ranges] rows. Returns the number of tokens whose
+ * num_valid_pages was outside [0, cols], or -1 for invalid arguments. */
+int64_t oracle_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
+                            const int32_t* num_valid_pages, int32_t init_blocks,
+                            int32_t local_blocks, int32_t num_ranges, oracle_row* out)
+{
+    if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > ORACLE_TOPK ||
+        num_ranges < 1 || cols < 1)
+        return -1;
+    int64_t width = ((int64_t)cols + num_ranges - 1) / num_ranges;
+    int64_t bad = 0;
+    entry* cand = (entry*)malloc(sizeof(entry) * (size_t)(width > 0 ? width : 1));
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t n = num_valid_pages[t];
+        if (n < 0 || n > cols) {
+            ++bad;
+            n = n < 0 ? 0 : cols;
+        }
+        for (int h = 0; h < ORACLE_HEADS; ++h) {
+            const float* srow = scores + (t * ORACLE_HEADS + h) * (int64_t)cols;
+            for (int32_t r = 0; r < num_ranges; ++r) {
+                int64_t lo = r * width;
+                int64_t hi = lo + width < cols ? lo + width : cols;
+                int64_t valid_hi = hi < n ? hi : n;
+                entry forced[ORACLE_TOPK];
+                int n_forced = 0;
+                int64_t n_cand = 0;
+                for (int64_t id = lo; id < valid_hi; ++id) {
+                    entry e = {srow[id], (int32_t)id};
+                    if (is_forced(id, n, init_blocks, local_blocks))
+                        forced[n_forced++] = e;
+                    else
+                        cand[n_cand++] = e;
+                }
+                emit_row(forced, n_forced, ORACLE_TOPK - n_forced, cand, n_cand,
+                         out + (t * ORACLE_HEADS + h) * num_ranges + r);
+            }
+        }
+    }
+    free(cand);
+    return bad;
+}
+
+/* Merge of R partial Top16 rows per (token, head) [P2 decode: owner merge]:
+ * the union of the rows' entries (id >= 0; an id met twice keeps its higher
+ * score), forced ids of [0, n) recomputed, the rest ranked as in select with
+ * budget 16 - |forced of [0, n)|. partial: [T, 4, R]; out: [T, 4].
+ * Returns the number of (token, head) rows in which a forced id was missing
+ * from the union, or -1 for invalid arguments. */
+int64_t oracle_top16_merge(const oracle_row* partial, int32_t num_tokens, int32_t num_ranges,
+                           const int32_t* num_valid_pages, int32_t init_blocks,
+                           int32_t local_blocks, oracle_row* out)
+{
+    if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > ORACLE_TOPK ||
+        num_ranges < 1)
+        return -1;
+    int64_t cap = (int64_t)num_ranges * ORACLE_TOPK;
+    entry* all = (entry*)malloc(sizeof(entry) * (size_t)cap);
+    entry* cand = (entry*)malloc(sizeof(entry) * (size_t)cap);
+    int64_t missing_rows = 0;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t n = num_valid_pages[t] < 0 ? 0 : num_valid_pages[t];
+        for (int h = 0; h < ORACLE_HEADS; ++h) {
+            const oracle_row* rows = partial + (t * ORACLE_HEADS + h) * num_ranges;
+            int64_t n_all = 0;
+            for (int32_t r = 0; r < num_ranges; ++r) {
+                for (int s = 0; s < ORACLE_TOPK; ++s) {
+                    if (rows[r].id[s] < 0)
+                        continue;
+                    int64_t k;
+                    for (k = 0; k < n_all; ++k)
+                        if (all[k].id == rows[r].id[s])
+                            break;
+                    if (k < n_all) {
+                        if (rows[r].score[s] > all[k].score)
+                            all[k].score = rows[r].score[s];
+                    } else {
+                        all[n_all].id = rows[r].id[s];
+                        all[n_all].score = rows[r].score[s];
+                        ++n_all;
+                    }
+                }
+            }
+            int64_t expected_forced = 0;
+            for (int64_t id = 0; id < n; ++id)
+                expected_forced += is_forced(id, n, init_blocks, local_blocks);
+            entry forced[ORACLE_TOPK];
+            int n_forced = 0;
+            int64_t n_cand = 0;
+            for (int64_t k = 0; k < n_all; ++k) {
+                if (is_forced(all[k].id, n, init_blocks, local_blocks))
+                    forced[n_forced++] = all[k];
+                else
+                    cand[n_cand++] = all[k];
+            }
+            if (n_forced != expected_forced)
+                ++missing_rows;
+            emit_row(forced, n_forced, ORACLE_TOPK - (int)expected_forced, cand, n_cand,
+                     out + t * ORACLE_HEADS + h);
+        }
+    }
+    free(all);
+    free(cand);
+    return missing_rows;
+}

@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with:
+
+* a library routine (torch's CPU float8_e4m3fn -> float cast; numpy float64
+  matrix products, which are exact here: every partial sum of e4m3fn products
+  is a multiple of 2^-18 below 2^43);
+* a closed form (one-hot rows, monotone keys with a known block maximum);
+* brute force written differently from the oracle (whole-request score
+  matrices with explicit masks; O(n^2) rank counting for the Top16);
+* an invariant (written-column range, merge of split lists == whole-row
+  select);
+* the stored column-count table in tests/golden.
+
+The tests run them on the real oracle; the mutation test runs them on oracle
+builds with planted mistakes and expects at least one to fail.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CANARY_BITS = np.uint32(0x7FC0DEAD)
+NEG_INF = np.float32(-np.inf)
+
+
+# ----------------------------------------------------------------------------
+# independent helpers (library routines, not the oracle)
+# ----------------------------------------------------------------------------
+
+def torch_decode(codes) -> np.ndarray:
+    """float64 values of uint8 e4m3fn codes, decoded by torch's own cast."""
+    t = torch.as_tensor(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def finite_codes() -> np.ndarray:
+    c = np.arange(256, dtype=np.uint8)
+    return c[(c & 0x7F) != 0x7F]
+
+
+def canary_plane(T: int, cols: int) -> np.ndarray:
+    return np.full((T, 4, cols), CANARY_BITS, dtype=np.uint32).view(np.float32)
+
+
+def brute_force_plane(index_q, index_k, block_table, seq_lens, page_size, dql, cols):
+    """Score plane by whole-request matrices: keys gathered in position order,
+    S = Q @ K^T in float64 (exact), explicit causal mask, block max, one
+    rounding to float32. Unwritten entries are NaN, amax alongside."""
+    q = np.asarray(index_q, dtype=np.uint8)
+    k = np.asarray(index_k, dtype=np.uint8)
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    B = sl.shape[0]
+    out = np.full((B * dql, 4, cols), np.nan, dtype=np.float32)
+    amax = np.zeros((B * dql, 4, cols), dtype=np.float64)
+    for b in range(B):
+        s = int(sl[b])
+        if s <= 0:
+            continue
+        p = np.arange(s)
+        keys = k[bt[b, p // page_size], p % page_size]          # [s, 128] codes
+        kd = torch_decode(keys)                                  # [s, 128]
+        qd = torch_decode(q[b * dql:(b + 1) * dql]).reshape(dql * 4, 128)
+        S = qd @ kd.T                                            # [dql*4, s]
+        A = np.abs(qd) @ np.abs(kd).T
+        nblk = -(-s // 128)
+        ncols = min(-(-nblk // 4) * 4, cols)
+        for r in range(dql * 4):
+            j = r // 4
+            pos = s - dql + j
+            vis = p <= pos
+            for c in range(ncols):
+                sel = vis & (p >= 128 * c) & (p < 128 * c + 128)
+                if sel.any():
+                    out[b * dql + j, r % 4, c] = np.float32(S[r, sel].max())
+                    amax[b * dql + j, r % 4, c] = A[r, sel].max()
+                else:
+                    out[b * dql + j, r % 4, c] = NEG_INF
+    return out, amax
+
+
+def brute_select_row(srow, n, lo, hi, init, local):
+    """Top16 row by rank counting: a candidate is taken iff fewer than
+    (16 - |forced|) other candidates beat it (higher score, or equal score and
+    lower id). Returns (ids ascending, scores)."""
+    valid = list(range(lo, min(hi, n)))
+    forced = [i for i in valid if i < init or i >= n - local]
+    cand = [i for i in valid if i not in forced]
+    budget = 16 - len(forced)
+    taken = []
+    for x in cand:
+        beat = 0
+        for y in cand:
+            if y == x:
+                continue
+            if srow[y] > srow[x] or (srow[y] == srow[x] and y < x):
+                beat += 1
+        if beat < budget:
+            taken.append(x)
+    ids = sorted(forced + taken)
+    return ids, [srow[i] for i in ids]
+
+
+def _assert_row(ids_row, sc_row, exp_ids, srow):
+    m = len(exp_ids)
+    assert m <= 16
+    got_ids = [int(x) for x in ids_row]
+    assert got_ids[:m] == exp_ids, (got_ids, exp_ids)
+    assert all(x == -1 for x in got_ids[m:]), got_ids
+    for i, idx in enumerate(exp_ids):
+        assert np.float32(sc_row[i]).view(np.uint32) == np.float32(srow[idx]).view(np.uint32)
+    assert all(np.isneginf(sc_row[m:]))
+
+
+# ----------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------
+
+def pin_e4m3_table(orc):
+    """Decode table == torch's cast for all 256 codes; spot closed forms."""
+    t = orc.e4m3fn_table()
+    ref = torch_decode(np.arange(256, dtype=np.uint8))
+    nan_codes = sorted(np.where(np.isnan(t))[0].tolist())
+    assert nan_codes == [0x7F, 0xFF], nan_codes
+    fin = ~np.isnan(ref)
+    assert np.array_equal(t[fin], ref[fin])
+    assert np.array_equal(np.signbit(t[fin]), np.signbit(ref[fin]))
+    # closed forms of the OCP E4M3 definition
+    assert t[0x38] == 1.0 and t[0x40] == 2.0 and t[0x30] == 0.5
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert t[0x00] == 0.0 and not np.signbit(t[0x00])
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+
+
+def pin_dots_vs_float64(orc, seed=7):
+    """Exact dots == float64 numpy products of torch-decoded rows."""
+    rng = np.random.default_rng(seed)
+    fc = finite_codes()
+    parts = [
+        rng.choice(fc, size=(1500, 128)),
+        torch.randn(500, 128, generator=torch.Generator().manual_seed(seed)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy(),
+        rng.integers(0, 8, size=(50, 128)),            # subnormals only
+    ]
+    q = np.concatenate([p.astype(np.uint8) for p in parts])
+    k = np.concatenate([rng.permutation(p.astype(np.uint8)) for p in parts])
+    # extremes: 448*448*128 and -448*448*128
+    q = np.concatenate([q, np.full((2, 128), 0x7E, np.uint8)])
+    k = np.concatenate([k, np.stack([np.full(128, 0x7E, np.uint8), np.full(128, 0xFE, np.uint8)])])
+    f32, exact = orc.dots(q, k)
+    ref = (torch_decode(q) * torch_decode(k)).sum(axis=1)
+    assert np.array_equal(exact, ref)
+    assert np.array_equal(f32, ref.astype(np.float32))
+    assert exact[-2] == 448.0 * 448.0 * 128 and exact[-1] == -448.0 * 448.0 * 128
+
+
+def pin_code_pairs(orc):
+    """One-hot rows: q . k == dec(a) * dec(b) for every pair of finite codes."""
+    fc = finite_codes()
+    a, b = np.meshgrid(fc, fc, indexing="ij")
+    a, b = a.ravel(), b.ravel()
+    n = a.size
+    dim = (a.astype(np.int64) * 7 + b) % 128
+    q = np.zeros((n, 128), dtype=np.uint8)
+    k = np.zeros((n, 128), dtype=np.uint8)
+    q[np.arange(n), dim] = a
+    k[np.arange(n), dim] = b
+    f32, exact = orc.dots(q, k)
+    prod = torch_decode(a) * torch_decode(b)
+    assert np.array_equal(exact, prod)
+    assert np.array_equal(f32, prod.astype(np.float32))
+    # NaN codes propagate
+    q1 = np.zeros((2, 128), np.uint8)
+    k1 = np.zeros((2, 128), np.uint8)
+    q1[0, 3] = 0x7F
+    k1[1, 5] = 0xFF
+    f, _ = orc.dots(q1, k1)
+    assert np.isnan(f).all()
+
+
+def _tiny_workloads():
+    yield workloads.generate(batch=3, seq=("list", [300, 1000, 129]), page_size=128, dql=1,
+                             seed=11, pool=("exact", None))
+    yield workloads.generate(batch=4, seq=("list", [700, 256, 513, 1]), page_size=256, dql=2,
+                             seed=12, outlier_frac=0.05)
+    yield workloads.generate(batch=6, seq=("list", [1, 7, 8, 9, 383, 640]), page_size=128,
+                             dql=8, seed=13, scale=0.5)
+    yield workloads.generate(batch=3, seq=("list", [0, 3, 1030]), page_size=256, dql=5, seed=14,
+                             cols=12)
+
+
+def pin_plane_brute_force(orc):
+    """Oracle plane == whole-request brute force, bit for bit, incl. amax."""
+    for w in _tiny_workloads():
+        args = (w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(), w.seq_lens.numpy())
+        plane, amax, bad = orc.score_decode(*args, page_size=w.page_size,
+                                            decode_query_len=w.dql, cols=w.cols, want_amax=True)
+        ref, ref_amax = brute_force_plane(*args, w.page_size, w.dql, w.cols)
+        assert bad == 0
+        written = ~np.isnan(ref)
+        assert np.array_equal(np.isnan(plane), np.isnan(ref)), w.name
+        assert np.array_equal(plane[written], ref[written]), w.name
+        assert np.array_equal(amax[written], ref_amax[written]), w.name
+        # sampled interface agrees with the plane
+        T = w.num_tokens
+        rows, cols = np.nonzero(written.reshape(T * 4, w.cols))
+        s, a, bad2 = orc.score_sampled(*args, rows, cols, page_size=w.page_size,
+                                       decode_query_len=w.dql)
+        assert bad2 == 0
+        assert np.array_equal(s, ref.reshape(T * 4, w.cols)[rows, cols])
+        assert np.array_equal(a, ref_amax.reshape(T * 4, w.cols)[rows, cols])
+
+
+def pin_plane_closed_form(orc):
+    """q = 1.0 at dim 0; key p carries code min(p % 128, 126) at dim 0, so the
+    block maximum is the value of the last visible key's code (codes 0x00..0x7E
+    increase in value): tests the inclusive causal bound exactly."""
+    dql = 8
+    seqs = [1, 2, 127, 128, 129, 200, 256, 300]
+    B = len(seqs)
+    ps = 128
+    npages = [-(-s // ps) for s in seqs]
+    total = sum(npages)
+    k = np.zeros((total + 1, ps, 128), dtype=np.uint8)
+    k[:, :, 0] = np.minimum(np.arange(ps), 126).astype(np.uint8)[None, :]
+    bt = np.full((B, 4), total, dtype=np.int32)
+    perm = np.random.default_rng(3).permutation(total)
+    off = 0
+    for b, n in enumerate(npages):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = np.zeros((B * dql, 4, 128), dtype=np.uint8)
+    q[:, :, 0] = 0x38  # 1.0
+    cols = 4
+    plane, _, bad = orc.score_decode(q, k, bt, np.array(seqs, np.int32), page_size=ps,
+                                     decode_query_len=dql, cols=cols)
+    assert bad == 0
+    val = torch_decode(np.arange(256, dtype=np.uint8))
+    for b, s in enumerate(seqs):
+        nblk = -(-s // 128)
+        for j in range(dql):
+            pos = s - dql + j
+            for c in range(cols):
+                got = plane[b * dql + j, :, c]
+                if c >= nblk:
+                    want = -np.inf
+                elif pos < 128 * c:
+                    want = -np.inf
+                else:
+                    last = min(pos, s - 1, 128 * c + 127)
+                    want = val[min(last % 128, 126)]
+                assert np.all(got == np.float32(want)), (s, j, c, got, want)
+
+
+def pin_written_range(orc):
+    """Canary columns past roundup4(blocks) stay bit-identical; columns in
+    [blocks, roundup4(blocks)) hold -inf; the rest are written."""
+    for w in _tiny_workloads():
+        T = w.num_tokens
+        cols = w.cols + 8
+        base = canary_plane(T, cols)
+        plane, _, _ = orc.score_decode(w.index_q.numpy(), w.index_k.numpy(),
+                                       w.block_table.numpy(), w.seq_lens.numpy(),
+                                       page_size=w.page_size, decode_query_len=w.dql, cols=cols,
+                                       plane=base)
+        bits = plane.view(np.uint32)
+        for b in range(w.batch):
+            s = int(w.seq_lens[b])
+            nblk = -(-s // 128) if s > 0 else 0
+            wcols = -(-nblk // 4) * 4
+            rows = slice(b * w.dql, (b + 1) * w.dql)
+            assert np.all(bits[rows, :, wcols:] == CANARY_BITS), (w.name, b)
+            assert np.all(np.isneginf(plane[rows, :, nblk:wcols])), (w.name, b)
+            assert not np.any(bits[rows, :, :nblk] == CANARY_BITS), (w.name, b)
+
+
+def pin_column_counts_golden(orc):
+    """Written-column counts of the stored table (derived by hand from the
+    column rule of the msa_icp_decode_index_score_sharded page)."""
+    path = os.path.join(HERE, "golden", "column_counts.txt")
+    n = 0
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            seq_len, page_size, want = (int(x) for x in line.split())
+            assert orc.written_columns(seq_len) == want, (seq_len, page_size, want)
+            n += 1
+    assert n >= 10
+
+
+def _random_plane(rng, T, cols, ties):
+    if ties:
+        pool = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.5, 2.0], dtype=np.float32)
+        return rng.choice(pool, size=(T, 4, cols)).astype(np.float32)
+    return rng.standard_normal((T, 4, cols)).astype(np.float32)
+
+
+def pin_select_brute_force(orc, seed=5):
+    """Oracle select == rank-counting brute force (ids and raw scores)."""
+    rng = np.random.default_rng(seed)
+    cases = [(1, 2, 1), (0, 0, 1), (16, 0, 1), (0, 16, 2), (8, 8, 3), (4, 4, 5), (2, 2, 4),
+             (1, 4, 1)]
+    for ci, (init, local, R) in enumerate(cases):
+        for ties in (False, True):
+            T, cols = 3, int(rng.integers(1, 90))
+            s = _random_plane(rng, T, cols, ties)
+            nvp = rng.integers(0, cols + 1, size=T).astype(np.int32)
+            nvp[0] = cols
+            if T > 1:
+                nvp[1] = min(cols, int(rng.integers(0, 20)))
+            sc, ids, bad = orc.top16_select(s, nvp, init_blocks=init, local_blocks=local,
+                                            num_ranges=R)
+            assert bad == 0
+            w = -(-cols // R)
+            for t in range(T):
+                for h in range(4):
+                    for r in range(R):
+                        lo, hi = r * w, min(r * w + w, cols)
+                        exp_ids, _ = brute_select_row(s[t, h], int(nvp[t]), lo, hi, init, local)
+                        _assert_row(ids[t, h, r], sc[t, h, r], exp_ids, s[t, h])
+
+
+def pin_select_invariants(orc, seed=6):
+    """ids ascending, unique, valid; forced present; count = min(16, |valid|)."""
+    rng = np.random.default_rng(seed)
+    for init, local in [(1, 2), (4, 4), (2, 2), (1, 4), (0, 0), (16, 0)]:
+        T, cols = 8, 700
+        s = _random_plane(rng, T, cols, ties=bool(rng.integers(0, 2)))
+        nvp = rng.integers(0, cols + 1, size=T).astype(np.int32)
+        sc, ids, _ = orc.top16_select(s, nvp, init_blocks=init, local_blocks=local)
+        for t in range(T):
+            n = int(nvp[t])
+            forced = set(range(min(init, n))) | set(range(max(0, n - local), n))
+            for h in range(4):
+                row = [int(x) for x in ids[t, h, 0] if x >= 0]
+                assert row == sorted(set(row))
+                assert all(0 <= x < n for x in row)
+                assert forced <= set(row)
+                assert len(row) == min(16, n)
+
+
+def pin_merge_split_equivalence(orc, seed=8):
+    """merge(select over R ranges) == select over the whole row, bit for bit;
+    merge of one full row is the identity."""
+    rng = np.random.default_rng(seed)
+    for init, local in [(1, 2), (4, 4), (0, 0), (2, 14)]:
+        for ties in (False, True):
+            T, cols = 4, 256
+            s = _random_plane(rng, T, cols, ties)
+            nvp = rng.integers(0, cols + 1, size=T).astype(np.int32)
+            nvp[0] = cols
+            nvp[1] = 5
+            whole_s, whole_i, _ = orc.top16_select(s, nvp, init_blocks=init, local_blocks=local)
+            for R in (1, 2, 3, 8, cols // 4):
+                ps, pi, _ = orc.top16_select(s, nvp, init_blocks=init, local_blocks=local,
+                                             num_ranges=R)
+                ms, mi, missing = orc.top16_merge(ps, pi, nvp, init_blocks=init,
+                                                  local_blocks=local)
+                assert missing == 0
+                assert np.array_equal(mi, whole_i[:, :, 0]), (init, local, R)
+                assert np.array_equal(ms.view(np.uint32), whole_s[:, :, 0].view(np.uint32))
+
+
+def pin_merge_missing_forced(orc):
+    """A merge input that lacks a forced id is reported."""
+    T, cols = 1, 64
+    s = np.arange(T * 4 * cols, dtype=np.float32).reshape(T, 4, cols)
+    nvp = np.array([cols], np.int32)
+    ps, pi, _ = orc.top16_select(s, nvp, init_blocks=2, local_blocks=2, num_ranges=2)
+    pi = pi.copy()
+    ps = ps.copy()
+    pi[0, 0, 0, 0] = -1  # drop forced id 0 from head 0
+    _, _, missing = orc.top16_merge(ps, pi, nvp, init_blocks=2, local_blocks=2)
+    assert missing == 1
+
+
+ALL_PINS = [
+    pin_e4m3_table, pin_dots_vs_float64, pin_code_pairs, pin_plane_brute_force,
+    pin_plane_closed_form, pin_written_range, pin_column_counts_golden, pin_select_brute_force,
+    pin_select_invariants, pin_merge_split_equivalence, pin_merge_missing_forced,
+]

@@ -1,0 +1,61 @@
+"""Plants plausible mistakes in copies of the oracle's C source and checks that
+the pins catch every one (so a passing pin set means something). CPU only;
+the planted builds live in a temporary directory and are never used
+elsewhere."""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+
+import oracle_pins as P
+
+# (name, exact text in msa_oracle.c, replacement)
+MUTATIONS = [
+    ("mask_off_by_one", "if (p >= seq_len || p > pos)", "if (p >= seq_len || p >= pos)"),
+    ("normal_exponent", "(int64_t)(8 + mantissa) << (exponent - 1)",
+     "(int64_t)(8 + mantissa) << exponent"),
+    ("subnormal_as_normal", "magnitude_units = mantissa;", "magnitude_units = 8 + mantissa;"),
+    ("dropped_sign", "        acc += prod;\n", "        acc += prod < 0 ? -prod : prod;\n"),
+    ("max_becomes_min", "if (!have || u > best)", "if (!have || u < best)"),
+    ("page_row_index", "((page * page_size) + (p % page_size))",
+     "((page * page_size) + (p % ORACLE_BLOCK))"),
+    ("unpadded_columns", "return (blocks + 3) / 4 * 4;", "return blocks;"),
+    ("rounding_scale", "(float)ldexp((double)units, -18)", "(float)ldexp((double)units, -17)"),
+    ("tie_break_reversed",
+     "    if (a->score < b->score)\n        return 1;\n    return (a->id > b->id) - (a->id < b->id);",
+     "    if (a->score < b->score)\n        return 1;\n    return (a->id < b->id) - (a->id > b->id);"),
+    ("forced_end_off_by_one", "return id < init_blocks || id >= n - local_blocks;",
+     "return id < init_blocks || id > n - local_blocks;"),
+    ("range_width_floor", "int64_t width = ((int64_t)cols + num_ranges - 1) / num_ranges;",
+     "int64_t width = (int64_t)cols / num_ranges;"),
+    ("merge_budget", "ORACLE_TOPK - (int)expected_forced, cand",
+     "ORACLE_TOPK - (int)expected_forced - 1, cand"),
+    ("amax_signed", "acc_abs += prod < 0 ? -prod : prod;", "acc_abs += prod;"),
+    ("ascending_by_score", "qsort(chosen, (size_t)m, sizeof(entry), id_cmp);",
+     "qsort(chosen, (size_t)m, sizeof(entry), rank_cmp);"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle_build.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique/absent"
+    src = tmp_path / f"mut_{name}.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle_build.build(src=str(src), out=str(tmp_path / f"libmut_{name}.so"))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake {name}"
