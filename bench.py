@@ -1,0 +1,216 @@
+"""Benchmark of the decode-time block indexer on one MI355X.
+
+One step = the whole chain on one batch of the long-context workload
+(4 requests x 1,048,576 keys, page_size 256, decode_query_len 8,
+plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
+
+    msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
+
+Inputs are seeded and synthetic (workloads.py) and resident in HBM before
+timing. Before every step a 1 GiB fill evicts the 256 MB Infinity Cache; it
+sits outside the step's event pair. The step time is measured with HIP
+events on the stream the kernels run on. Each kernel has its own event pair
+for the roofline figure. The contract's wall clock brackets all K steps,
+fills included, with a synchronize on both sides.
+
+Prints one JSON line. `value` is scored keys/s, i.e. the sum of seq_len over
+the mean step time. `roofline` rates the scorer, the dominant kernel, against
+HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
+`cpu_baseline` times the oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+FLUSH_BYTES = 1 << 30           # > 256 MB Infinity Cache
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_score_decode_long_b4_s1m.json")
+KERNEL_SOURCES = [os.path.join(HERE, "sparse_attention_block_msa_amd", "csrc", f)
+                  for f in ("score_decode.hip", "msa_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes: int):
+    """HBM bytes per scorer launch from the committed counter summary, or
+    None when it is missing or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
+            "total_bytes": t["fetch_bytes"] + t["write_bytes"],
+            "vs_algorithmic": round((t["fetch_bytes"] + t["write_bytes"]) / launch_bytes, 4),
+            "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
+
+
+def cpu_baseline(w, dev_rows_unused=None):
+    """The oracle on the same workload, on this host's cores."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    plane, _, _ = orc.score_decode(w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(),
+                                   w.seq_lens.numpy(), page_size=w.page_size,
+                                   decode_query_len=w.dql, cols=w.cols)
+    t1 = time.perf_counter()
+    ps, pi, _ = orc.top16_select(plane, w.num_valid_pages.numpy(), init_blocks=w.init_blocks,
+                                 local_blocks=w.local_blocks, num_ranges=w.num_ranges)
+    if w.num_ranges > 1:
+        orc.top16_merge(ps, pi, w.num_valid_pages.numpy(), init_blocks=w.init_blocks,
+                        local_blocks=w.local_blocks)
+    t2 = time.perf_counter()
+    keys = w.total_keys
+    return {"value": keys / (t2 - t0), "unit": "keys/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"the full workload once: {keys} keys scored ({t1 - t0:.1f} s), then "
+                      f"Top16 select over {w.num_ranges} ranges and merge ({t2 - t1:.2f} s)",
+            "seconds": round(t2 - t0, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, help="workload number (1..5)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting fill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "there is no multi-GPU path to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_block_msa_amd as msa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    w = workloads.config(args.config)
+    q, k = w.index_q.to(dev), w.index_k.to(dev)
+    bt, sl, nvp = w.block_table.to(dev), w.seq_lens.to(dev), w.num_valid_pages.to(dev)
+    T, R = w.num_tokens, w.num_ranges
+    plane = torch.empty((T, 4, w.cols), dtype=torch.float32, device=dev)
+    part = msa.new_rows(T, 4, R, device=dev)
+    final = msa.new_rows(T, 4, device=dev)
+    errors = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    msa.msa_warmup()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
+                             decode_query_len=w.dql, errors=errors, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        msa.msa_top16_select(plane, nvp, part, init_blocks=w.init_blocks,
+                             local_blocks=w.local_blocks, num_ranges=R, errors=errors,
+                             stream=stream)
+        if ev:
+            ev[2].record(stream)
+        if R > 1:
+            msa.msa_top16_merge(part, nvp, final, init_blocks=w.init_blocks,
+                                local_blocks=w.local_blocks, errors=errors, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.zero_()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if int(errors.item()) != 0:
+        raise RuntimeError(f"device error counter = {int(errors.item())}")
+
+    step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+    score_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
+    select_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
+    merge_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
+    mean = lambda xs: sum(xs) / len(xs)
+    ms_step = mean(step_ms)
+    keys = w.total_keys
+    launch_bytes = workloads.index_k_bytes(w)
+    value = keys / (ms_step * 1e-3)
+    e2e_gbps = launch_bytes / (ms_step * 1e-3) / 1e9
+    score_mean = mean(score_ms)
+    achieved = launch_bytes / (score_mean * 1e-3) / 1e9
+
+    out = {
+        "metric": "index-K scored keys/s and achieved HBM GB/s (% of peak), score+Top16, 1 GPU",
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-products-f32-accumulate",
+        "data": "synthetic (seeded N(0,1) -> float8_e4m3fn, random page permutation)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": int(w.seq_lens.max()),
+                   "page_size": w.page_size, "decode_query_len": w.dql, "cols": w.cols,
+                   "ranges": R, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
+                   "index_k_bytes": launch_bytes, "parallelism": "single-gpu",
+                   "cache_flush_between_steps": not args.no_flush},
+        "e2e": {"hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
+                "step_ms_p10": step_ms[len(step_ms) // 10],
+                "step_ms_p50": step_ms[len(step_ms) // 2],
+                "step_ms_p90": step_ms[(len(step_ms) * 9) // 10],
+                "kernels_ms": {"score_decode": score_mean, "top16_select": mean(select_ms),
+                               "top16_merge": mean(merge_ms)},
+                "wall_s_all_steps_incl_flush": wall},
+        "roofline": {"kernel": "score_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": launch_bytes,
+                     "launch_ms": score_mean,
+                     "traffic": load_traffic(launch_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * msa_indexer.h -- C ABI of the decode-time sparse-attention block indexer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs one decode step of a sparse-attention block indexer on one
+ * GPU. There are three stream-ordered steps:
+ *
+ *   1. msa_score_decode: the score plane. Each decode token's 4 fp8 index
+ *      heads are scored against the paged fp8 index-K cache, with one column
+ *      per 128-token (B128) block.
+ *   2. msa_top16_select: per (token, head) row, or per column range of the
+ *      row, the forced begin/end blocks plus the best remaining blocks, as 16
+ *      raw scores and 16 ascending block ids.
+ *   3. msa_top16_merge: merges the per-range Top16 lists of a row into one.
+ *
+ * The operations follow the FlashInfer msa_ops API pages:
+ *   "flashinfer.msa_ops.msa_icp_decode_index_score_sharded"  (step 1)
+ *   "flashinfer.msa_ops.msa_icp_topk_select_publish"         (step 2, row format)
+ *   "flashinfer.msa_ops.prepare_msa_icp_indexer"             (the decode chain
+ *       score -> select -> merge; forced init/local blocks)
+ * Here one GPU holds every page's full rows. There is no rank, world size,
+ * peer publish or receive row.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device buffers are device memory that the caller
+ *    allocates and owns. The library never allocates, frees or synchronises.
+ *    It enqueues its kernels on `stream` and returns before they run.
+ *    Inputs are only read.
+ *  - Return value: MSA_OK (0) on success. MSA_ERR_INVALID_ARG (-1) if a
+ *    host-checkable precondition fails; nothing is launched in that case and
+ *    msa_last_error() describes the failed check. MSA_ERR_LAUNCH (-2) if the
+ *    HIP runtime refuses a launch.
+ *  - `errors` (nullable, device int32[>= 1]) counts violations of conditions
+ *    that only the device can see, by atomic increments. Examples are a
+ *    block_table entry outside [0, num_pages), or num_valid_pages outside
+ *    [0, cols]. The kernel then clamps or skips the offending input and
+ *    writes a defined result. It never traps. The counter is not reset.
+ *  - Inputs must not hold e4m3fn NaN codes (0x7F, 0xFF). Results are then
+ *    unspecified.
+ */
+#ifndef MSA_INDEXER_H
+#define MSA_INDEXER_H
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1)
+#define MSA_ERR_LAUNCH (-2)
+
+#define MSA_NUM_HEADS 4          /* index heads (prepare_msa_icp_indexer: num_index_heads) */
+#define MSA_HEAD_DIM 128         /* index head dim (index_q / index_k last dimension)      */
+#define MSA_BLOCK_TOKENS 128     /* tokens per B128 block = one score-plane column          */
+#define MSA_TOPK 16              /* entries per Top16 row                                  */
+#define MSA_MAX_SCORE_COLS 8192  /* score_out: 0 < cols <= 8192, cols % 4 == 0             */
+#define MSA_MAX_SELECT_COLS 12287 /* select scores: 0 < K < 12288                          */
+#define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
+
+/*
+ * One Top16 row (128 bytes). score[i] is the raw score-plane value of block
+ * id[i]. Ids ascend. Unused slots hold (score -inf, id -1) and follow the
+ * used ones. Source: "msa_icp_topk_select_publish", description. The page
+ * names a row of 16 raw scores and 16 ascending global ids. Its ready flag and
+ * generation tags belong to the cross-GPU publish, which this library does
+ * not have.
+ */
+typedef struct msa_top16_row {
+    float score[MSA_TOPK];
+    int32_t id[MSA_TOPK];
+} msa_top16_row;
+
+/*
+ * Step 1: the score plane.
+ * Source: "msa_icp_decode_index_score_sharded" (description; parameters
+ * index_q, index_k, block_table, seq_lens, score_out, page_size,
+ * decode_query_len).
+ *
+ * index_q      device, e4m3fn bytes [batch * decode_query_len, 4, 128], contiguous,
+ *              16-byte aligned. Token j of request b is row b*decode_query_len + j.
+ *              Its position is seq_lens[b] - decode_query_len + j.
+ * index_k      device, e4m3fn bytes [num_pages, page_size, 128], contiguous,
+ *              16-byte aligned. Key p of request b is row p % page_size of page
+ *              block_table[b, p / page_size].
+ * block_table  device int32, read as [batch, block_table_stride] rows with unit last
+ *              stride. Request b uses entries [0, ceil(seq_len/page_size)). An entry it
+ *              needs at or past the row stride, or outside [0, num_pages), is counted
+ *              in `errors`, and that block scores -inf.
+ * seq_lens     device int32 [batch]. A request with seq_len <= 0 writes nothing.
+ * page_size    128 or 256.
+ * decode_query_len  1 <= len and 4*len <= 32.
+ * score_out    device float32 [batch*decode_query_len, 4, cols], contiguous,
+ *              16-byte aligned, 0 < cols <= 8192, cols % 4 == 0.
+ *
+ * Writes score_out[t, h, c] for every token t of request b and every column
+ * c < W_b = min(roundup4(ceil(seq_len_b / 128)), cols). A W_b that cols cuts
+ * short is counted in `errors`. Columns c >= W_b are not touched. The value
+ * is the maximum, over keys p of block c (128c <= p < 128c + 128) with
+ * p < seq_len and p <= the token's position, of the dot product of the
+ * token's head row with key p's row (fp8 products, fp32 accumulation). It is
+ * -inf if no key of the block qualifies, which includes the padding columns
+ * [ceil(seq_len/128), W_b).
+ */
+int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                     const int32_t* block_table, int64_t block_table_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                     int32_t decode_query_len, float* score_out, int32_t cols, int32_t* errors,
+                     hipStream_t stream);
+
+/*
+ * Step 2: Top16 select per (token, head, column range).
+ * Source: "msa_icp_topk_select_publish" (description: 16 raw scores and 16
+ * ascending global ids; every row written, padding rows included; scores;
+ * num_valid_pages: global B128 block counts) and "prepare_msa_icp_indexer"
+ * (init_blocks, local_blocks: forced begin / end blocks, sum at most 16).
+ *
+ * scores           device float32 [num_tokens, 4, cols], contiguous, 0 < cols < 12288.
+ * num_valid_pages  device int32 [num_tokens]: valid block ids of token t are [0, n),
+ *                  n = num_valid_pages[t]. A value outside [0, cols] is counted in
+ *                  `errors` and clamped.
+ * init_blocks, local_blocks  >= 0, sum <= 16.
+ * num_ranges       R, 1 <= R <= min(cols, 768). Range r is the columns
+ *                  [r*w, min((r+1)*w, cols)) with w = ceil(cols / R).
+ * out              device [num_tokens, 4, R] rows. Every row is written on every call.
+ *
+ * Row (t, h, r) keeps the forced ids of its range, [0, init) and [n - local, n)
+ * within [0, n). It then takes the best 16 - |forced| of the range's other
+ * valid ids, ranked by score descending and then lower id (-0 == +0). All
+ * kept entries are listed by ascending id.
+ */
+int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
+                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                     int32_t num_ranges, msa_top16_row* out, int32_t* errors, hipStream_t stream);
+
+/*
+ * Step 3: merge of the R per-range rows of each (token, head).
+ * Source: "prepare_msa_icp_indexer" (decode: score plane -> Top16 select ->
+ * merge). On one GPU the merge reduces the split-column lists of a row.
+ *
+ * partial          device [num_tokens, 4, R] rows from msa_top16_select over disjoint
+ *                  column ranges in ascending order, so that valid ids ascend along the
+ *                  concatenated rows. A descending consecutive pair is counted in `errors`.
+ * num_valid_pages  device int32 [num_tokens], as given to msa_top16_select.
+ * init_blocks, local_blocks  as given to msa_top16_select.
+ * num_ranges       R, 1 <= R <= 768.
+ * out              device [num_tokens, 4] rows. Every row is written on every call.
+ *
+ * Applies the select rule to the union of the R rows. Forced ids are
+ * recomputed over [0, n). A forced id missing from the union is counted in
+ * `errors`. The result equals msa_top16_select with R = 1 on the same scores.
+ */
+int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
+                    const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                    msa_top16_row* out, int32_t* errors, hipStream_t stream);
+
+/*
+ * Score-plane width for requests of up to max_seq_len tokens:
+ * roundup4(ceil(max_seq_len / 128)).
+ * Source: "msa_icp_decode_index_score_sharded", score_out (which refers to
+ * msa_icp_decode_score_columns()). Returns MSA_ERR_INVALID_ARG if
+ * max_seq_len < 1 or the width would exceed 8192. Host only, no device call.
+ */
+int32_t msa_score_columns(int64_t max_seq_len);
+
+/*
+ * Loads every kernel of the library into the current device's context, so
+ * that no later launch waits on module loading, for example inside a timed
+ * region or a graph capture.
+ * Source: "prepare_msa_icp_indexer", the paragraph on warmup().
+ * Returns MSA_OK or MSA_ERR_LAUNCH.
+ */
+int msa_warmup(void);
+
+/*
+ * Text of the last failed check or launch of the calling thread. The string
+ * is empty if there was none. It stays valid until the thread's next call
+ * into the library.
+ */
+const char* msa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_INDEXER_H */

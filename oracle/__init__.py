@@ -55,6 +55,8 @@ class Oracle:
         lib.oracle_top16_select.restype = i64
         lib.oracle_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P]
         lib.oracle_top16_merge.restype = i64
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -76,6 +78,10 @@ class Oracle:
         e = np.empty(n, dtype=np.float64)
         self.lib.oracle_dots(_ptr(q), _ptr(k), n, _ptr(f), _ptr(e))
         return f, e
+
+    def num_threads(self) -> int:
+        """OpenMP threads the plane functions use."""
+        return int(self.lib.oracle_num_threads())
 
     def written_columns(self, seq_len: int) -> int:
         return int(self.lib.oracle_written_columns(int(seq_len)))

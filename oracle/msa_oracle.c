@@ -41,6 +41,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_DIM 128   /* index head dimension [P1 index_q / index_k] */
 #define ORACLE_HEADS 4   /* index heads [P1 index_q; P2 num_index_heads] */
@@ -148,6 +151,16 @@ void oracle_dots(const uint8_t* q, const uint8_t* k, int64_t n, float* out_f32, 
         out_f32[i] = nan ? NAN : units_to_float(u);
         out_exact[i] = nan ? NAN : ldexp((double)u, -18);
     }
+}
+
+/* Threads the plane functions may use (OpenMP), for reporting. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------------ */

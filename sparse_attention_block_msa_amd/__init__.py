@@ -1,0 +1,209 @@
+"""Python binding of ``libmsa_indexer.so``, the MI355X (gfx950) decode-time
+sparse-attention block indexer.
+
+The functions carry the C-ABI names declared in ``include/msa_indexer.h``
+and only marshal arguments. They check dtype, shape, device and contiguity,
+pass raw device pointers and the current HIP stream, and turn error codes
+into exceptions. Every step of the computation runs in the library's HIP
+kernels. PyTorch provides the device memory and the streams.
+
+The operations follow the FlashInfer msa_ops API pages
+"msa_icp_decode_index_score_sharded" (score plane),
+"msa_icp_topk_select_publish" (Top16 rows) and "prepare_msa_icp_indexer"
+(the decode chain score -> select -> merge and the forced init/local blocks).
+fp8 tensors may be passed as ``torch.float8_e4m3fn`` or as their raw
+``torch.uint8`` codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsa_indexer.so")
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARG = -1
+MSA_ERR_LAUNCH = -2
+NUM_HEADS = 4
+HEAD_DIM = 128
+BLOCK_TOKENS = 128
+TOPK = 16
+ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
+
+EXPORTS = ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_score_columns",
+           "msa_warmup", "msa_last_error")
+
+
+class MsaError(RuntimeError):
+    """A failed call into the library (the message is msa_last_error())."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the library once. Raises if it has not been built: there is no
+    fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; "
+            "g.build()' or python sparse_attention_block_msa_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.msa_score_decode.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, P]
+    lib.msa_score_decode.restype = ctypes.c_int
+    lib.msa_top16_select.argtypes = [P, i32, i32, P, i32, i32, i32, P, P, P]
+    lib.msa_top16_select.restype = ctypes.c_int
+    lib.msa_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
+    lib.msa_top16_merge.restype = ctypes.c_int
+    lib.msa_score_columns.argtypes = [i64]
+    lib.msa_score_columns.restype = i32
+    lib.msa_warmup.argtypes = []
+    lib.msa_warmup.restype = ctypes.c_int
+    lib.msa_last_error.argtypes = []
+    lib.msa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != MSA_OK:
+        msg = load().msa_last_error()
+        raise MsaError(rc, msg.decode() if msg else "")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name}: expected float8_e4m3fn or uint8 codes, got {t.dtype}")
+    return t
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    dev = ts[0].device
+    for t in ts:
+        _need(t.is_cuda, "all tensors must be on a GPU device")
+        _need(t.device == dev, "all tensors must be on the same device")
+
+
+def _errors_ptr(errors):
+    if errors is None:
+        return None
+    _need(errors.dtype == torch.int32 and errors.numel() >= 1 and errors.is_cuda,
+          "errors: expected a device int32 tensor with >= 1 element")
+    return errors.data_ptr()
+
+
+def new_rows(*shape, device="cuda") -> torch.Tensor:
+    """An int32 tensor [*shape, 32] holding Top16 rows."""
+    return torch.empty((*shape, ROW_WORDS), dtype=torch.int32, device=device)
+
+
+def row_scores(rows: torch.Tensor) -> torch.Tensor:
+    """float32 view [..., 16] of the scores of Top16 rows."""
+    return rows[..., :TOPK].view(torch.float32)
+
+
+def row_ids(rows: torch.Tensor) -> torch.Tensor:
+    """int32 view [..., 16] of the block ids of Top16 rows."""
+    return rows[..., TOPK:]
+
+
+def msa_score_columns(max_seq_len: int) -> int:
+    """Plane width roundup4(ceil(max_seq_len / 128)) (host only)."""
+    cols = load().msa_score_columns(int(max_seq_len))
+    _check(min(cols, 0))
+    return int(cols)
+
+
+def msa_warmup() -> None:
+    """Loads every kernel into the current device's context."""
+    _check(load().msa_warmup())
+
+
+def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, score_out: torch.Tensor, *, page_size: int,
+                     decode_query_len: int, errors: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """Writes the score plane score_out [T, 4, cols] (columns past each
+    request's roundup4(ceil(seq_len/128)) untouched). See msa_indexer.h."""
+    q = _u8(index_q, "index_q")
+    k = _u8(index_k, "index_k")
+    _dev(q, k, block_table, seq_lens, score_out)
+    B = seq_lens.numel()
+    _need(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens: int32 [B]")
+    _need(q.shape == (B * decode_query_len, NUM_HEADS, HEAD_DIM) and q.is_contiguous(),
+          f"index_q: expected contiguous [{B * decode_query_len}, 4, 128], got {tuple(q.shape)}")
+    _need(k.dim() == 3 and k.shape[1] == page_size and k.shape[2] == HEAD_DIM and k.is_contiguous(),
+          f"index_k: expected contiguous [pages, {page_size}, 128], got {tuple(k.shape)}")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
+          block_table.shape[0] == B and block_table.is_contiguous(),
+          "block_table: contiguous int32 [B, width]")
+    _need(score_out.dtype == torch.float32 and score_out.dim() == 3 and
+          score_out.shape[:2] == (B * decode_query_len, NUM_HEADS) and score_out.is_contiguous(),
+          "score_out: contiguous float32 [T, 4, cols]")
+    lib = load()
+    _check(lib.msa_score_decode(
+        q.data_ptr(), k.data_ptr(), k.shape[0], block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), B, page_size, decode_query_len, score_out.data_ptr(),
+        score_out.shape[2], _errors_ptr(errors), _stream_handle(stream)))
+
+
+def msa_top16_select(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,
+                     init_blocks: int, local_blocks: int, num_ranges: int = 1,
+                     errors: torch.Tensor | None = None, stream=None) -> None:
+    """Top16 rows [T, 4, R] of scores [T, 4, cols] over R column ranges.
+    `out` is an int32 tensor [T, 4, R, 32] (see new_rows)."""
+    _dev(scores, num_valid_pages, out)
+    _need(scores.dtype == torch.float32 and scores.dim() == 3 and scores.shape[1] == NUM_HEADS and
+          scores.is_contiguous(), "scores: contiguous float32 [T, 4, cols]")
+    T, _, cols = scores.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, {num_ranges}, 32]")
+    lib = load()
+    _check(lib.msa_top16_select(scores.data_ptr(), T, cols, num_valid_pages.data_ptr(),
+                                init_blocks, local_blocks, num_ranges, out.data_ptr(),
+                                _errors_ptr(errors), _stream_handle(stream)))
+
+
+def msa_top16_merge(partial: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,
+                    init_blocks: int, local_blocks: int, errors: torch.Tensor | None = None,
+                    stream=None) -> None:
+    """Merges partial rows [T, 4, R, 32] into rows [T, 4, 32]."""
+    _dev(partial, num_valid_pages, out)
+    _need(partial.dtype == torch.int32 and partial.dim() == 4 and partial.shape[1] == NUM_HEADS
+          and partial.shape[3] == ROW_WORDS and partial.is_contiguous(),
+          "partial: contiguous int32 [T, 4, R, 32]")
+    T, _, R, _ = partial.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, 32]")
+    lib = load()
+    _check(lib.msa_top16_merge(partial.data_ptr(), T, R, num_valid_pages.data_ptr(), init_blocks,
+                               local_blocks, out.data_ptr(), _errors_ptr(errors),
+                               _stream_handle(stream)))

@@ -1,0 +1,190 @@
+// C-ABI entry points: host-side argument checks, then one kernel launch each
+// on the caller's stream. Nothing here allocates or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "msa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int launch_result(hipError_t e, const char* what)
+{
+    if (e != hipSuccess)
+        return fail(MSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return MSA_OK;
+}
+
+bool aligned(const void* ptr, uintptr_t a)
+{
+    return ((uintptr_t)ptr % a) == 0;
+}
+
+#define MSA_CHECK(cond, ...)                                   \
+    do {                                                       \
+        if (!(cond))                                           \
+            return fail(MSA_ERR_INVALID_ARG, __VA_ARGS__);     \
+    } while (0)
+
+int check_forced(const char* fn, int32_t init_blocks, int32_t local_blocks)
+{
+    MSA_CHECK(init_blocks >= 0 && local_blocks >= 0,
+              "%s: init_blocks (%d) and local_blocks (%d) must be >= 0", fn, init_blocks,
+              local_blocks);
+    MSA_CHECK(init_blocks + local_blocks <= MSA_TOPK,
+              "%s: init_blocks + local_blocks = %d exceeds %d", fn, init_blocks + local_blocks,
+              MSA_TOPK);
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void)
+{
+    return g_last_error;
+}
+
+int32_t msa_score_columns(int64_t max_seq_len)
+{
+    g_last_error[0] = '\0';
+    MSA_CHECK(max_seq_len >= 1, "msa_score_columns: max_seq_len (%lld) must be >= 1",
+              (long long)max_seq_len);
+    const int64_t blocks = (max_seq_len + MSA_BLOCK_TOKENS - 1) / MSA_BLOCK_TOKENS;
+    const int64_t cols = (blocks + 3) / 4 * 4;
+    MSA_CHECK(cols <= MSA_MAX_SCORE_COLS, "msa_score_columns: %lld columns exceed %d",
+              (long long)cols, MSA_MAX_SCORE_COLS);
+    return (int32_t)cols;
+}
+
+int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                     const int32_t* block_table, int64_t block_table_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                     int32_t decode_query_len, float* score_out, int32_t cols, int32_t* errors,
+                     hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_score_decode";
+    MSA_CHECK(index_q && index_k && block_table && seq_lens && score_out,
+              "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(index_q, 16) && aligned(index_k, 16) && aligned(score_out, 16),
+              "%s: index_q, index_k and score_out must be 16-byte aligned", fn);
+    MSA_CHECK(aligned(block_table, 4) && aligned(seq_lens, 4) && aligned(errors, 4),
+              "%s: int32 arrays must be 4-byte aligned", fn);
+    MSA_CHECK(page_size == 128 || page_size == 256, "%s: page_size (%d) must be 128 or 256", fn,
+              page_size);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn,
+              batch);
+    MSA_CHECK(num_pages >= 1, "%s: num_pages (%lld) must be >= 1", fn, (long long)num_pages);
+    MSA_CHECK(block_table_stride >= 1, "%s: block_table_stride (%lld) must be >= 1", fn,
+              (long long)block_table_stride);
+
+    msa::ScoreParams p;
+    p.q = index_q;
+    p.k = index_k;
+    p.num_pages = num_pages;
+    p.bt = block_table;
+    p.bt_stride = block_table_stride;
+    p.seq_lens = seq_lens;
+    p.out = score_out;
+    p.errors = errors;
+    p.batch = batch;
+    p.page_size = page_size;
+    p.dql = decode_query_len;
+    p.cols = cols;
+    p.chunks_per_req = (cols + msa::kScoreChunk - 1) / msa::kScoreChunk;
+    return launch_result(msa::launch_score_decode(p, stream), fn);
+}
+
+int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
+                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                     int32_t num_ranges, msa_top16_row* out, int32_t* errors, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_top16_select";
+    MSA_CHECK(scores && num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(scores, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
+                  aligned(errors, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4*ranges < 2^31", fn, num_tokens);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SELECT_COLS,
+              "%s: cols (%d) must satisfy 0 < cols <= %d", fn, cols, MSA_MAX_SELECT_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+
+    msa::SelectParams p;
+    p.scores = scores;
+    p.nvp = num_valid_pages;
+    p.out = out;
+    p.errors = errors;
+    p.num_tokens = num_tokens;
+    p.cols = cols;
+    p.init_blocks = init_blocks;
+    p.local_blocks = local_blocks;
+    p.num_ranges = num_ranges;
+    p.width = (cols + num_ranges - 1) / num_ranges;
+    return launch_result(msa::launch_top16_select(p, stream), fn);
+}
+
+int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
+                    const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                    msa_top16_row* out, int32_t* errors, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_top16_merge";
+    MSA_CHECK(partial && num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(partial, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
+                  aligned(errors, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4 < 2^31", fn, num_tokens);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, %d]", fn, num_ranges, MSA_MAX_RANGES);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+
+    msa::MergeParams p;
+    p.partial = partial;
+    p.nvp = num_valid_pages;
+    p.out = out;
+    p.errors = errors;
+    p.num_tokens = num_tokens;
+    p.num_ranges = num_ranges;
+    p.init_blocks = init_blocks;
+    p.local_blocks = local_blocks;
+    return launch_result(msa::launch_top16_merge(p, stream), fn);
+}
+
+int msa_warmup(void)
+{
+    g_last_error[0] = '\0';
+    hipError_t e = msa::warmup_score_kernels();
+    if (e == hipSuccess)
+        e = msa::warmup_top16_kernels();
+    return launch_result(e, "msa_warmup");
+}
+
+}  // extern "C"

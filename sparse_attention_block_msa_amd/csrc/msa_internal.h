@@ -1,0 +1,70 @@
+// Internal declarations shared by the library's translation units: launch
+// parameter blocks and the launchers each kernel file provides. Host-side
+// validation lives in msa_abi.hip; the launchers assume valid arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa_indexer.h"
+
+namespace msa {
+
+constexpr int kHeads = MSA_NUM_HEADS;
+constexpr int kDim = MSA_HEAD_DIM;
+constexpr int kBlockTokens = MSA_BLOCK_TOKENS;
+constexpr int kTop = MSA_TOPK;
+
+// Plane columns (B128 blocks) one scorer wave produces; a multiple of 4 so
+// that every wave writes whole float4 groups of columns.
+constexpr int kScoreChunk = 16;
+
+struct ScoreParams {
+    const uint8_t* q;        // [batch*dql, 4, 128] e4m3fn
+    const uint8_t* k;        // [num_pages, page_size, 128] e4m3fn
+    int64_t num_pages;
+    const int32_t* bt;       // [batch, bt_stride]
+    int64_t bt_stride;
+    const int32_t* seq_lens; // [batch]
+    float* out;              // [batch*dql, 4, cols]
+    int32_t* errors;         // nullable
+    int32_t batch;
+    int32_t page_size;       // 128 or 256
+    int32_t dql;             // 1..8
+    int32_t cols;            // multiple of 4, <= 8192
+    int32_t chunks_per_req;  // ceil(cols / kScoreChunk)
+};
+
+struct SelectParams {
+    const float* scores;     // [T, 4, cols]
+    const int32_t* nvp;      // [T]
+    msa_top16_row* out;      // [T, 4, R]
+    int32_t* errors;         // nullable
+    int32_t num_tokens;
+    int32_t cols;
+    int32_t init_blocks;
+    int32_t local_blocks;
+    int32_t num_ranges;
+    int32_t width;           // ceil(cols / R)
+};
+
+struct MergeParams {
+    const msa_top16_row* partial;  // [T, 4, R]
+    const int32_t* nvp;            // [T]
+    msa_top16_row* out;            // [T, 4]
+    int32_t* errors;               // nullable
+    int32_t num_tokens;
+    int32_t num_ranges;
+    int32_t init_blocks;
+    int32_t local_blocks;
+};
+
+hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream);
+
+// Loads the kernels of each file into the current device's context.
+hipError_t warmup_score_kernels();
+hipError_t warmup_top16_kernels();
+
+}  // namespace msa

@@ -1,0 +1,354 @@
+// Top16 select and merge kernels for gfx950.
+//
+// Operation ("flashinfer.msa_ops.msa_icp_topk_select_publish", description;
+// "flashinfer.msa_ops.prepare_msa_icp_indexer", init_blocks / local_blocks
+// and the decode chain's merge): a row keeps its forced begin/end blocks
+// ([0, init) and [n - local, n) within the valid ids [0, n)) and the best
+// 16 - |forced| of its other valid blocks, ranked by score descending and
+// then lower id, and lists them by ascending id; unused slots hold
+// (-inf, -1). The merge applies the same rule to the union of a row's
+// per-range lists.
+//
+// Design:
+//  * A wave (64 lanes) owns a contiguous span of a row's elements; element i
+//    of lane l is element span_lo + 64*i + l, so loads are coalesced and
+//    "element order" == "id order".
+//  * Ranking key: the fp32 score mapped to an order-preserving uint32 (with -0
+//    mapped to +0, so -0 and +0 tie); non-candidates get key 0, below every
+//    real score. The K-th largest key is found by a 32-step bitwise descent in
+//    which each step counts keys >= a trial value with one ballot + popcount
+//    per register (no cross-lane reduction needed). Ties at that key are
+//    broken by element order using the same ballots and mbcnt.
+//  * Kept elements are compacted to their ascending-id slot with mbcnt.
+//  * Spans longer than 2048 elements are split over 4 waves of one
+//    workgroup; each wave selects its part, and wave 0 merges the four
+//    partial rows from LDS with the same routine. Splitting is exact: a
+//    block that belongs to the row's best K is also among the best of its
+//    own part (fewer blocks beat it there than in the whole row).
+#include <math.h>
+
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ int is_forced(int id, int n, int init_blocks, int local_blocks)
+{
+    return id >= 0 && id < n && (id < init_blocks || id >= n - local_blocks);
+}
+
+// Wave-level select. Element i of this lane has key u[i] (0 = not a
+// candidate) and is forced if bit i of fbits is set. Keeps all forced
+// elements and the best min(budget, #candidates) candidates, and calls
+// emit(i, slot) for each kept element, slots ascending in element order.
+// Returns the number of kept elements (uniform).
+template <int V, class Emit>
+__device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbits, int budget,
+                                           Emit&& emit)
+{
+    int n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        n_cand += __popcll(__ballot(u[i] != 0u));
+    const int K = min(budget, n_cand);
+
+    uint32_t thr = 0xFFFFFFFFu;
+    int need = 0;
+    if (K > 0) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                cnt += __popcll(__ballot(u[i] >= trial));
+            if (cnt >= K)
+                prefix = trial;
+        }
+        thr = prefix;  // the K-th largest key
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            gt += __popcll(__ballot(u[i] > thr));
+        need = K - gt;  // how many keys equal to thr are kept (lowest ids first)
+    }
+
+    int base = 0, tie_base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool tie = K > 0 && u[i] == thr;
+        const uint64_t tie_mask = __ballot(tie);
+        const bool take = ((fbits >> i) & 1ull) ||
+                          (K > 0 && (u[i] > thr || (tie && tie_base + lanes_below(tie_mask) < need)));
+        const uint64_t take_mask = __ballot(take);
+        if (take)
+            emit(i, base + lanes_below(take_mask));
+        base += __popcll(take_mask);
+        tie_base += __popcll(tie_mask);
+    }
+    return base;
+}
+
+__device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
+{
+    if (lane >= kept && lane < kTop) {
+        row->score[lane] = -INFINITY;
+        row->id[lane] = -1;
+    }
+}
+
+// Second level of a split row: the NW partial rows in LDS are merged by wave
+// 0 into `out`. Forced ids are recomputed from (n, init, local). The
+// candidate budget is `budget`, or 16 - (forced entries found) if budget < 0.
+// Returns the number of forced entries found (uniform in wave 0).
+template <int NW>
+__device__ __forceinline__ int merge_lds_rows(const msa_top16_row* part, int n, int init_blocks,
+                                              int local_blocks, int budget, msa_top16_row* out,
+                                              int lane)
+{
+    static_assert(NW * kTop <= 64, "partial rows must fit one wave");
+    uint32_t u[1] = {0u};
+    uint64_t fbits = 0;
+    float s = -INFINITY;
+    int id = -1;
+    if (lane < NW * kTop) {
+        s = part[lane / kTop].score[lane % kTop];
+        id = part[lane / kTop].id[lane % kTop];
+    }
+    const bool forced = is_forced(id, n, init_blocks, local_blocks);
+    if (forced)
+        fbits = 1;
+    else if (id >= 0)
+        u[0] = order_key(s);
+    const int n_forced = __popcll(__ballot(forced));
+    if (budget < 0)
+        budget = kTop - n_forced;
+    const int kept = wave_select<1>(u, fbits, budget, [&](int, int slot) {
+        out->score[slot] = s;
+        out->id[slot] = id;
+    });
+    pad_row(out, kept, lane);
+    return n_forced;
+}
+
+// |[0, min(init, n)) U [max(0, n - local), n)|
+__device__ __forceinline__ int forced_count(int n, int init_blocks, int local_blocks)
+{
+    if (n <= 0)
+        return 0;
+    const int a = min(init_blocks, n);
+    const int s = max(0, n - local_blocks);
+    return a + (n - s) - max(0, a - s);
+}
+
+template <int V, int NW>
+__global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
+{
+    __shared__ msa_top16_row part[NW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t job = blockIdx.x;  // ((t * 4) + h) * R + r
+    const int r = (int)(job % p.num_ranges);
+    const int64_t th = job / p.num_ranges;
+    const int t = (int)(th / kHeads);
+
+    int n = p.nvp[t];
+    if (n < 0 || n > p.cols) {
+        if (r == 0 && (th % kHeads) == 0 && threadIdx.x == 0 && p.errors)
+            atomicAdd(p.errors, 1);
+        n = n < 0 ? 0 : p.cols;
+    }
+    const int lo = r * p.width;
+    const int hi = min(lo + p.width, p.cols);
+    const int vhi = min(hi, n);
+    const int span_lo = lo + wave * (V * 64);
+    const float* srow = p.scores + th * p.cols;
+
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    int n_forced = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int id = span_lo + i * 64 + lane;
+        u[i] = 0u;
+        bool forced = false;
+        if (id < vhi) {
+            forced = is_forced(id, n, p.init_blocks, p.local_blocks);
+            if (!forced)
+                u[i] = order_key(srow[id]);
+        }
+        fbits |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+
+    msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
+    const int kept = wave_select<V>(u, fbits, kTop - n_forced, [&](int i, int slot) {
+        const int id = span_lo + i * 64 + lane;
+        dst->score[slot] = srow[id];
+        dst->id[slot] = id;
+    });
+    pad_row(dst, kept, lane);
+
+    if (NW > 1) {
+        __syncthreads();
+        if (wave == 0)  // every forced id of the range is in exactly one partial row
+            merge_lds_rows<NW>(part, n, p.init_blocks, p.local_blocks, -1, p.out + job, lane);
+    }
+}
+
+template <int V, int NW>
+__global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
+{
+    __shared__ msa_top16_row part[NW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t th = blockIdx.x;  // t * 4 + h
+    const int t = (int)(th / kHeads);
+    const int n = max(0, p.nvp[t]);
+    const int total = p.num_ranges * kTop;  // entries in the concatenated rows
+    const msa_top16_row* rows = p.partial + th * p.num_ranges;
+    const int span_lo = wave * (V * 64);
+
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    int n_forced = 0;
+    bool disorder = false;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = span_lo + i * 64 + lane;
+        u[i] = 0u;
+        bool forced = false;
+        if (e < total) {
+            const int id = rows[e / kTop].id[e % kTop];
+            if (id >= 0) {
+                forced = is_forced(id, n, p.init_blocks, p.local_blocks);
+                if (!forced)
+                    u[i] = order_key(rows[e / kTop].score[e % kTop]);
+                if (e > 0) {
+                    const int prev = rows[(e - 1) / kTop].id[(e - 1) % kTop];
+                    disorder |= prev >= id;
+                }
+            }
+        }
+        fbits |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+    const uint64_t disorder_mask = __ballot(disorder);
+    if (disorder_mask && lane == 0 && p.errors)
+        atomicAdd(p.errors, 1);
+
+    const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
+    msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
+    const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
+    const int kept = wave_select<V>(u, fbits, budget, [&](int i, int slot) {
+        const int e = span_lo + i * 64 + lane;
+        dst->score[slot] = rows[e / kTop].score[e % kTop];
+        dst->id[slot] = rows[e / kTop].id[e % kTop];
+    });
+    pad_row(dst, kept, lane);
+
+    int found_forced = n_forced;
+    if (NW > 1) {
+        __syncthreads();
+        if (wave == 0)
+            found_forced = merge_lds_rows<NW>(part, n, p.init_blocks, p.local_blocks,
+                                              kTop - expected_forced, p.out + th, lane);
+    }
+    if ((NW == 1 || wave == 0) && found_forced < expected_forced && lane == 0 && p.errors)
+        atomicAdd(p.errors, 1);
+}
+
+// Launch shape: spans up to 2048 elements use one wave with V = the next
+// power of two >= span/64; longer spans use 4 waves with V = 16, 32 or 48.
+struct Shape {
+    int v;
+    int nw;
+};
+
+Shape pick_shape(int64_t span)
+{
+    const int64_t per_lane = (span + 63) / 64;
+    if (per_lane <= 32) {
+        int v = 1;
+        while (v < per_lane)
+            v *= 2;
+        return {v, 1};
+    }
+    const int64_t per_lane4 = (span + 255) / 256;
+    return {per_lane4 <= 16 ? 16 : per_lane4 <= 32 ? 32 : 48, 4};
+}
+
+template <int V, int NW>
+hipError_t launch_select_shape(const SelectParams& p, hipStream_t stream)
+{
+    const int64_t jobs = (int64_t)p.num_tokens * kHeads * p.num_ranges;
+    void* args[] = {const_cast<SelectParams*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_select_kernel<V, NW>),
+                           dim3((unsigned)jobs), dim3(NW * 64), args, 0, stream);
+}
+
+template <int V, int NW>
+hipError_t launch_merge_shape(const MergeParams& p, hipStream_t stream)
+{
+    const int64_t jobs = (int64_t)p.num_tokens * kHeads;
+    void* args[] = {const_cast<MergeParams*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_merge_kernel<V, NW>),
+                           dim3((unsigned)jobs), dim3(NW * 64), args, 0, stream);
+}
+
+#define MSA_FOR_EACH_SHAPE(X) \
+    X(1, 1) X(2, 1) X(4, 1) X(8, 1) X(16, 1) X(32, 1) X(16, 4) X(32, 4) X(48, 4)
+
+}  // namespace
+
+hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream)
+{
+    const Shape s = pick_shape(p.width);
+#define X(V, NW)                                      \
+    if (s.v == V && s.nw == NW)                       \
+        return launch_select_shape<V, NW>(p, stream);
+    MSA_FOR_EACH_SHAPE(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream)
+{
+    const Shape s = pick_shape((int64_t)p.num_ranges * kTop);
+#define X(V, NW)                                     \
+    if (s.v == V && s.nw == NW)                      \
+        return launch_merge_shape<V, NW>(p, stream);
+    MSA_FOR_EACH_SHAPE(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t warmup_top16_kernels()
+{
+    hipFuncAttributes attr;
+    hipError_t e = hipSuccess;
+#define X(V, NW)                                                                                  \
+    if (e == hipSuccess)                                                                          \
+        e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_select_kernel<V, NW>)); \
+    if (e == hipSuccess)                                                                          \
+        e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_merge_kernel<V, NW>));
+    MSA_FOR_EACH_SHAPE(X)
+#undef X
+    return e;
+}
+
+}  // namespace msa

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched): the
+library loads, exports every function include/msa_indexer.h declares, and
+rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_block_msa_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_indexer.h")
+FAKE = 4096  # a 16-byte-aligned non-null pointer value; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(msa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msa.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_score_columns",
+              "msa_warmup", "msa_last_error"):
+        assert n in names
+    assert set(names) == set(msa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_row_type_is_128_bytes():
+    text = open(HEADER).read()
+    assert "float score[MSA_TOPK];" in text and "int32_t id[MSA_TOPK];" in text
+    assert msa.ROW_WORDS * 4 == 128
+
+
+def test_score_columns_matches_golden_table(lib):
+    path = os.path.join(ROOT, "tests", "golden", "column_counts.txt")
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        s, _, want = (int(x) for x in line.split())
+        got = lib.msa_score_columns(s)
+        if s < 1 or want > 8192:
+            assert got == msa.MSA_ERR_INVALID_ARG, (s, got)
+        else:
+            assert got == want, (s, got, want)
+    assert msa.msa_score_columns(1048576) == 8192
+    with pytest.raises(msa.MsaError):
+        msa.msa_score_columns(0)
+
+
+def _score(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seq=FAKE, batch=2,
+             page_size=128, dql=1, out=FAKE, cols=32, errors=None, stream=None)
+    a.update(kw)
+    return lib.msa_score_decode(a["q"], a["k"], a["num_pages"], a["bt"], a["bt_stride"],
+                                a["seq"], a["batch"], a["page_size"], a["dql"], a["out"],
+                                a["cols"], a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=None), "null"),
+    (dict(k=None), "null"),
+    (dict(out=None), "null"),
+    (dict(q=FAKE + 4), "aligned"),
+    (dict(out=FAKE + 8), "aligned"),
+    (dict(page_size=64), "page_size"),
+    (dict(page_size=512), "page_size"),
+    (dict(dql=0), "decode_query_len"),
+    (dict(dql=9), "decode_query_len"),
+    (dict(cols=0), "cols"),
+    (dict(cols=30), "cols"),
+    (dict(cols=8196), "cols"),
+    (dict(batch=0), "batch"),
+    (dict(num_pages=0), "num_pages"),
+    (dict(bt_stride=0), "block_table_stride"),
+])
+def test_score_decode_rejects(lib, kw, needle):
+    assert _score(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _select(lib, **kw):
+    a = dict(scores=FAKE, T=4, cols=100, nvp=FAKE, init=1, local=2, R=1, out=FAKE, errors=None,
+             stream=None)
+    a.update(kw)
+    return lib.msa_top16_select(a["scores"], a["T"], a["cols"], a["nvp"], a["init"], a["local"],
+                                a["R"], a["out"], a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(scores=None), "null"),
+    (dict(out=None), "null"),
+    (dict(T=0), "num_tokens"),
+    (dict(cols=0), "cols"),
+    (dict(cols=12288), "cols"),
+    (dict(init=-1), "init_blocks"),
+    (dict(init=9, local=8), "exceeds"),
+    (dict(R=0), "num_ranges"),
+    (dict(R=101), "num_ranges"),
+    (dict(cols=12287, R=769), "num_ranges"),
+    (dict(scores=FAKE + 2), "aligned"),
+])
+def test_select_rejects(lib, kw, needle):
+    assert _select(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _merge(lib, **kw):
+    a = dict(partial=FAKE, T=4, R=8, nvp=FAKE, init=1, local=2, out=FAKE, errors=None,
+             stream=None)
+    a.update(kw)
+    return lib.msa_top16_merge(a["partial"], a["T"], a["R"], a["nvp"], a["init"], a["local"],
+                               a["out"], a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(partial=None), "null"),
+    (dict(T=0), "num_tokens"),
+    (dict(R=0), "num_ranges"),
+    (dict(R=769), "num_ranges"),
+    (dict(local=17, init=0), "exceeds"),
+    (dict(errors=FAKE + 1), "aligned"),
+])
+def test_merge_rejects(lib, kw, needle):
+    assert _merge(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros((1, 4, 128), dtype=torch.uint8)
+    k = torch.zeros((2, 128, 128), dtype=torch.uint8)
+    bt = torch.zeros((1, 2), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    out = torch.zeros((1, 4, 4), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        msa.msa_score_decode(q, k, bt, sl, out, page_size=128, decode_query_len=1)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The binding and the HIP sources never name the oracle."""
+    pkg = os.path.join(ROOT, "sparse_attention_block_msa_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
