@@ -7,8 +7,10 @@ plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
     msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
 
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
-timing. Before every step a 1 GiB fill evicts the 256 MB Infinity Cache; it
-sits outside the step's event pair. The step time is measured with HIP
+timing. Before every step a read pass over a 1 GiB buffer evicts index-K
+from the 256 MB Infinity Cache; it sits outside the step's event pair. (A
+read, not a fill: a 1 GiB fill would leave the caches full of dirty lines
+whose write-back the next kernel would pay for.) The step time is measured with HIP
 events on the stream the kernels run on. Each kernel has its own event pair
 for the roofline figure. The contract's wall clock brackets all K steps,
 fills included, with a synchronize on both sides.
@@ -31,7 +33,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-FLUSH_BYTES = 1 << 30           # > 256 MB Infinity Cache
+FLUSH_BYTES = 1 << 30           # read before each step; > 256 MB Infinity Cache
+COPY_BYTES = 512 << 20          # calibration copy: reads and writes this many bytes
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_score_decode_long_b4_s1m.json")
 KERNEL_SOURCES = [os.path.join(HERE, "sparse_attention_block_msa_amd", "csrc", f)
                   for f in ("score_decode.hip", "msa_internal.h")]
@@ -93,8 +96,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5, help="workload number (1..5)")
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting fill")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting read pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, copy a 512 MiB buffer once (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -118,7 +124,7 @@ def main():
     part = msa.new_rows(T, 4, R, device=dev)
     final = msa.new_rows(T, 4, device=dev)
     errors = torch.zeros(1, dtype=torch.int32, device=dev)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     msa.msa_warmup()
     stream = torch.cuda.current_stream()
 
@@ -143,7 +149,7 @@ def main():
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         if not args.no_flush:
-            flush.zero_()
+            flush.sum()
         step()
     torch.cuda.synchronize()
 
@@ -153,12 +159,18 @@ def main():
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
-            flush.zero_()
+            flush.sum()
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     if int(errors.item()) != 0:
         raise RuntimeError(f"device error counter = {int(errors.item())}")
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
     score_ms = [ev[0].elapsed_time(ev[1]) for ev in events]

@@ -9,14 +9,20 @@
 // block count rounded up to a multiple of four and no further.
 //
 // Design (one wave = 64 lanes per workgroup):
-//  * A wave owns kScoreChunk consecutive columns of one request. Its Q tile
+//  * A wave owns a chunk of consecutive columns of one request. Its Q tile
 //    (4*dql <= 32 rows of 128 fp8 bytes) is converted once to bf16 and stays
 //    in registers for the whole chunk as the B operand of the MFMA.
 //  * A B128 block is 128 keys x 128 bytes = 16 KiB, contiguous inside one
-//    page. It is processed as 8 tiles of 16 keys. Keys stream from HBM
-//    straight into registers with 16-byte loads; after a tile has been
-//    converted, its raw registers are reloaded with that tile of the next
-//    block, so about one block (16 KiB) per wave is always in flight.
+//    page. It is staged through a per-wave 4 KiB LDS tile in four pieces of
+//    32 keys with global_load_lds_dwordx4: each DMA instruction moves 1 KiB
+//    of whole 128-byte rows (a fully contiguous, non-temporal read), and the
+//    per-lane source addresses are chosen so the tile lands XOR-swizzled,
+//    letting the MFMA-layout ds_read_b128s hit every LDS bank once. Loads
+//    never occupy VGPRs, so the kernel runs 5 waves per SIMD and the
+//    occupancy hides HBM latency. (Loading the MFMA layout straight into
+//    registers needs half-row 64-byte accesses per instruction; measured on
+//    MI355X, that pattern streams at about 5.2 TB/s against 6.5 TB/s for
+//    whole-row DMA.)
 //  * Contraction: every e4m3fn value is exactly a bf16 value, so each key
 //    tile is converted with v_cvt_scalef32_pk_bf16_fp8 (scale 1.0, two values
 //    per instruction) and contracted with v_mfma_f32_16x16x32_bf16, four
@@ -46,6 +52,25 @@
 namespace msa {
 namespace {
 
+// Launch shape: one 64-lane wave per workgroup, a block staged in kParts
+// pieces, and registers capped for 5 (<= 16 query rows) or 4 (32 rows)
+// waves per SIMD (LDS use: 4 KiB per wave).
+#ifndef MSA_SCORE_LOAD_AUX
+#define MSA_SCORE_LOAD_AUX 2  // cache-policy bits of the index-K DMA: nt (non-temporal)
+#endif
+#ifndef MSA_SCORE_PARTS
+#define MSA_SCORE_PARTS 4
+#endif
+#ifndef MSA_SCORE_WAVES_PER_EU_16
+#define MSA_SCORE_WAVES_PER_EU_16 5  // up to 16 query rows (decode_query_len <= 4)
+#endif
+#ifndef MSA_SCORE_WAVES_PER_EU_32
+#define MSA_SCORE_WAVES_PER_EU_32 4  // 17..32 query rows (more registers for the Q tile)
+#endif
+#ifndef MSA_SCORE_CHUNK
+#define MSA_SCORE_CHUNK 16
+#endif
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -56,6 +81,44 @@ __device__ __forceinline__ v8i load_row_slice(const uint8_t* row, int g)
 {
     const v4i lo = *reinterpret_cast<const v4i*>(row + 16 * g);
     const v4i hi = *reinterpret_cast<const v4i*>(row + 64 + 16 * g);
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* global_ptr;
+
+// One piece of a B128 block (kPieceRows consecutive key rows, 128 bytes each)
+// is staged in a per-wave LDS tile. Row `row`, 16-byte chunk c of the piece
+// sits at LDS chunk position (row, c ^ swz(row)): the 16 lanes that read
+// chunk g of 16 consecutive rows then touch 16 distinct (row parity,
+// position) pairs, i.e. all 64 banks once.
+__device__ __forceinline__ int swz(int row)
+{
+    return (row >> 1) & 7;
+}
+
+// Copies kPieceRows rows (contiguous in HBM) into the LDS tile with the
+// swizzle above. Each instruction moves 1 KiB = 8 whole rows: lane l fetches
+// row 8t + l/8, chunk (l%8) ^ swz(row), and the DMA engine writes it to LDS
+// byte 16*l of the instruction's 1 KiB slot. The loads are non-temporal:
+// every key is read exactly once per call.
+template <int kPieceRows>
+__device__ __forceinline__ void stage_piece(const uint8_t* piece, uint8_t* tile, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < kPieceRows / 8; ++t) {
+        const int row = 8 * t + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        __builtin_amdgcn_global_load_lds((global_ptr)(piece + row * kDim + chunk * 16),
+                                         (lds_ptr)(tile + t * 1024), 16, 0, MSA_SCORE_LOAD_AUX);
+    }
+}
+
+// The lane's 32-byte slice of tile row `row` (chunks g and 4 + g).
+__device__ __forceinline__ v8i read_row_slice(const uint8_t* tile, int row, int g)
+{
+    const v4i lo = *reinterpret_cast<const v4i*>(tile + row * kDim + 16 * (g ^ swz(row)));
+    const v4i hi = *reinterpret_cast<const v4i*>(tile + row * kDim + 16 * ((4 + g) ^ swz(row)));
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
@@ -87,38 +150,48 @@ __device__ __forceinline__ float max4(v4f a)
     return fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
 }
 
-// Scores one B128 block held in ka (8 key tiles, raw fp8) against the NT
-// query tiles, reloading ka with the next block's tiles as they are consumed.
-// On return mx[n] holds, in every lane, the block max of query row
-// 16n + lane%16. kMask: keys whose in-block index exceeds lim[n] are excluded.
-template <int NT, bool kMask>
-__device__ __forceinline__ void score_block(v8i (&ka)[8], const Bf16Slice (&qb)[NT],
-                                            const uint8_t* next_block, int r16, int g,
+// Scores one B128 block against the NT query tiles. The block is staged
+// through the wave's LDS tile in kParts pieces of 8 / kParts key tiles (16
+// keys each): DMA, wait, then convert and contract each tile. Other waves on
+// the SIMD keep HBM busy meanwhile. On return mx[n] holds, in every lane,
+// the block max of query row 16n + lane%16. kMask: keys whose in-block index
+// exceeds lim[n] are excluded.
+template <int NT, int kParts, bool kMask>
+__device__ __forceinline__ void score_block(const uint8_t* block, uint8_t* tile,
+                                            const Bf16Slice (&qb)[NT], int lane, int r16, int g,
                                             const int (&lim)[NT], float (&mx)[NT])
 {
+    constexpr int kTiles = 8 / kParts;
+    constexpr int kPieceRows = kTiles * 16;
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < NT; ++n)
         mx[n] = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        const Bf16Slice kt = to_bf16(ka[mt]);
-        ka[mt] = load_row_slice(next_block + (mt * 16 + r16) * kDim, g);
+    for (int part = 0; part < kParts; ++part) {
+        stage_piece<kPieceRows>(block + part * kPieceRows * kDim, tile, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // the piece's DMA has landed in LDS
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            v4f a = zero;
+        for (int t = 0; t < kTiles; ++t) {
+            const int mt = part * kTiles + t;
+            const Bf16Slice kt = to_bf16(read_row_slice(tile, t * 16 + r16, g));
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt.op[s], qb[n].op[s], a, 0, 0, 0);
-            if (kMask) {
-                const int k0 = mt * 16 + g * 4;
-                a.x = (k0 + 0 <= lim[n]) ? a.x : -INFINITY;
-                a.y = (k0 + 1 <= lim[n]) ? a.y : -INFINITY;
-                a.z = (k0 + 2 <= lim[n]) ? a.z : -INFINITY;
-                a.w = (k0 + 3 <= lim[n]) ? a.w : -INFINITY;
+            for (int n = 0; n < NT; ++n) {
+                v4f a = zero;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt.op[s], qb[n].op[s], a, 0, 0, 0);
+                if (kMask) {
+                    const int k0 = mt * 16 + g * 4;
+                    a.x = (k0 + 0 <= lim[n]) ? a.x : -INFINITY;
+                    a.y = (k0 + 1 <= lim[n]) ? a.y : -INFINITY;
+                    a.z = (k0 + 2 <= lim[n]) ? a.z : -INFINITY;
+                    a.w = (k0 + 3 <= lim[n]) ? a.w : -INFINITY;
+                }
+                mx[n] = fmaxf(mx[n], max4(a));
             }
-            mx[n] = fmaxf(mx[n], max4(a));
         }
+        __syncthreads();  // the tile's reads are done before the next DMA reuses it
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -127,9 +200,11 @@ __device__ __forceinline__ void score_block(v8i (&ka)[8], const Bf16Slice (&qb)[
     }
 }
 
-template <int NT>
-__global__ __launch_bounds__(64) void score_decode_kernel(ScoreParams p)
+template <int NT, int kParts, int kWavesPerEU>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void score_decode_kernel(ScoreParams p)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -146,19 +221,19 @@ __global__ __launch_bounds__(64) void score_decode_kernel(ScoreParams p)
             atomicAdd(p.errors, 1);
         wcols = p.cols;
     }
-    const int c_begin = chunk * kScoreChunk;
+    const int c_begin = chunk * p.chunk;
     if (c_begin >= wcols)
         return;
     // c_begin is a multiple of 4 below roundup4(nblk), hence below nblk: the
     // chunk holds at least one block with keys.
-    const int c_end = min(c_begin + kScoreChunk, wcols);
+    const int c_end = min(c_begin + p.chunk, wcols);
     const int c_last = min(c_end, nblk) - 1;
 
     const int rows = p.dql * kHeads;
     const int64_t row_base = (int64_t)b * rows;
     const int ps_shift = p.page_size == 256 ? 1 : 0;  // log2(B128 blocks per page)
 
-    // Block-table entries of this chunk, one per lane (at most 16).
+    // Block-table entries of this chunk, one per lane (at most kMaxScoreChunk).
     const int pg_begin = c_begin >> ps_shift;
     const int pg_count = (c_last >> ps_shift) - pg_begin + 1;
     int my_page = 0;
@@ -198,35 +273,31 @@ __global__ __launch_bounds__(64) void score_decode_kernel(ScoreParams p)
         qb[n] = to_bf16(raw);
     }
 
-    v8i ka[8];
-    {
-        const uint8_t* first = block_ptr(c_begin);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            ka[mt] = load_row_slice(first + (mt * 16 + r16) * kDim, g);
-    }
-
     const int first_masked = seq - p.dql;  // blocks reaching past this key need the mask
     for (int c4 = c_begin; c4 < c_end; c4 += 4) {
         float vals[NT][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = c4 + u;
-            const uint8_t* next = block_ptr(min(c + 1, c_last));
             float mx[NT];
             int lim[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n)
                 lim[n] = pos[n] - c * kBlockTokens;
-            if (c * kBlockTokens + (kBlockTokens - 1) > first_masked)
-                score_block<NT, true>(ka, qb, next, r16, g, lim, mx);
-            else
-                score_block<NT, false>(ka, qb, next, r16, g, lim, mx);
             const bool has_keys =
-                c <= c_last && !((bad_mask >> ((c >> ps_shift) - pg_begin)) & 1ull);
+                c <= c_last && !((bad_mask >> ((min(c, c_last) >> ps_shift) - pg_begin)) & 1ull);
+            if (!has_keys) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    mx[n] = -INFINITY;
+            } else if (c * kBlockTokens + (kBlockTokens - 1) > first_masked) {
+                score_block<NT, kParts, true>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
+            } else {
+                score_block<NT, kParts, false>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
+            }
 #pragma unroll
             for (int n = 0; n < NT; ++n)
-                vals[n][u] = has_keys ? mx[n] : -INFINITY;
+                vals[n][u] = mx[n];
         }
         // Lanes of group g == n store query row 16n + lane%16.
 #pragma unroll
@@ -242,23 +313,39 @@ __global__ __launch_bounds__(64) void score_decode_kernel(ScoreParams p)
 
 }  // namespace
 
+constexpr int kParts = MSA_SCORE_PARTS;
+static_assert(MSA_SCORE_CHUNK % 4 == 0 && MSA_SCORE_CHUNK <= kMaxScoreChunk, "bad chunk");
+
+template <int NT>
+const void* score_kernel_fn()
+{
+    constexpr int kWavesPerEU = NT == 1 ? MSA_SCORE_WAVES_PER_EU_16 : MSA_SCORE_WAVES_PER_EU_32;
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kWavesPerEU>);
+}
+
+int score_chunk_for(int batch, int cols)
+{
+    (void)batch;
+    (void)cols;
+    return MSA_SCORE_CHUNK;
+}
+
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)p.batch * p.chunks_per_req));
     const dim3 block(64);
     void* args[] = {const_cast<ScoreParams*>(&p)};
-    const void* fn = p.dql * kHeads <= 16 ? reinterpret_cast<const void*>(&score_decode_kernel<1>)
-                                          : reinterpret_cast<const void*>(&score_decode_kernel<2>);
+    const void* fn = p.dql * kHeads <= 16 ? score_kernel_fn<1>() : score_kernel_fn<2>();
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 hipError_t warmup_score_kernels()
 {
     hipFuncAttributes attr;
-    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&score_decode_kernel<1>));
+    hipError_t e = hipFuncGetAttributes(&attr, score_kernel_fn<1>());
     if (e != hipSuccess)
         return e;
-    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&score_decode_kernel<2>));
+    return hipFuncGetAttributes(&attr, score_kernel_fn<2>());
 }
 
 }  // namespace msa

@@ -178,28 +178,29 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
     const int span_lo = lo + wave * (V * 64);
     const float* srow = p.scores + th * p.cols;
 
+    // All V loads are issued unconditionally (index clamped into the row) so
+    // that they overlap; invalid elements are masked afterwards.
+    float sv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        sv[i] = srow[min(span_lo + i * 64 + lane, p.cols - 1)];
     uint32_t u[V];
     uint64_t fbits = 0;
     int n_forced = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int id = span_lo + i * 64 + lane;
-        u[i] = 0u;
-        bool forced = false;
-        if (id < vhi) {
-            forced = is_forced(id, n, p.init_blocks, p.local_blocks);
-            if (!forced)
-                u[i] = order_key(srow[id]);
-        }
+        const bool valid = id < vhi;
+        const bool forced = valid && is_forced(id, n, p.init_blocks, p.local_blocks);
+        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
         fbits |= (uint64_t)forced << i;
         n_forced += __popcll(__ballot(forced));
     }
 
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
     const int kept = wave_select<V>(u, fbits, kTop - n_forced, [&](int i, int slot) {
-        const int id = span_lo + i * 64 + lane;
-        dst->score[slot] = srow[id];
-        dst->id[slot] = id;
+        dst->score[slot] = sv[i];
+        dst->id[slot] = span_lo + i * 64 + lane;
     });
     pad_row(dst, kept, lane);
 
@@ -223,6 +224,19 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
     const msa_top16_row* rows = p.partial + th * p.num_ranges;
     const int span_lo = wave * (V * 64);
 
+    // Loads are unconditional (entry index clamped into the rows) so that
+    // they overlap; entries past the end are masked afterwards.
+    float sv[V];
+    int iv[V];
+    int pv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = min(span_lo + i * 64 + lane, total - 1);
+        const int ep = max(e - 1, 0);
+        sv[i] = rows[e / kTop].score[e % kTop];
+        iv[i] = rows[e / kTop].id[e % kTop];
+        pv[i] = rows[ep / kTop].id[ep % kTop];
+    }
     uint32_t u[V];
     uint64_t fbits = 0;
     int n_forced = 0;
@@ -230,20 +244,10 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int e = span_lo + i * 64 + lane;
-        u[i] = 0u;
-        bool forced = false;
-        if (e < total) {
-            const int id = rows[e / kTop].id[e % kTop];
-            if (id >= 0) {
-                forced = is_forced(id, n, p.init_blocks, p.local_blocks);
-                if (!forced)
-                    u[i] = order_key(rows[e / kTop].score[e % kTop]);
-                if (e > 0) {
-                    const int prev = rows[(e - 1) / kTop].id[(e - 1) % kTop];
-                    disorder |= prev >= id;
-                }
-            }
-        }
+        const bool valid = e < total && iv[i] >= 0;
+        const bool forced = valid && is_forced(iv[i], n, p.init_blocks, p.local_blocks);
+        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
+        disorder |= valid && e > 0 && pv[i] >= iv[i];
         fbits |= (uint64_t)forced << i;
         n_forced += __popcll(__ballot(forced));
     }
@@ -255,9 +259,8 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
     msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
     const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
     const int kept = wave_select<V>(u, fbits, budget, [&](int i, int slot) {
-        const int e = span_lo + i * 64 + lane;
-        dst->score[slot] = rows[e / kTop].score[e % kTop];
-        dst->id[slot] = rows[e / kTop].id[e % kTop];
+        dst->score[slot] = sv[i];
+        dst->id[slot] = iv[i];
     });
     pad_row(dst, kept, lane);
 
