@@ -103,6 +103,93 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
     return base;
 }
 
+// Compaction buffer of one wave: up to 64 entries (key, raw score, id).
+struct Candidate {
+    uint32_t key;
+    float score;
+    int id;  // bit 30: forced
+};
+constexpr int kForcedFlag = 1 << 30;
+
+// Wave-level select, same contract as wave_select, for V > 1 values per lane.
+// Elements are (u[i], sv[i], id_of(i)). Every key of the best K is >= theta,
+// the K-th largest of the 64 per-lane maxima (at least K keys are >= it), so
+// when the keys >= theta plus the forced elements number at most 64 they are
+// compacted in element order into `buf` (one per lane) and ranked there with
+// one value per lane; otherwise the full V-value search runs.
+template <int V, class IdOf, class Emit>
+__device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], const float (&sv)[V],
+                                                    uint64_t fbits, int budget, int lane,
+                                                    Candidate* buf, IdOf&& id_of, Emit&& emit)
+{
+    int n_cand = 0, n_forced = 0;
+    uint32_t lane_max = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        n_cand += __popcll(__ballot(u[i] != 0u));
+        n_forced += __popcll(__ballot((fbits >> i) & 1ull));
+        lane_max = max(lane_max, u[i]);
+    }
+    const int K = min(budget, n_cand);
+    uint32_t theta = 1u;
+    if (K > 0) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            if (__popcll(__ballot(lane_max >= trial)) >= K)
+                prefix = trial;
+        }
+        theta = max(prefix, 1u);
+    }
+    int n_sel = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        n_sel += __popcll(__ballot(u[i] >= theta));
+    if (K > 0 && n_sel + n_forced > 64)
+        return wave_select<V>(u, fbits, budget, [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
+
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool forced = (fbits >> i) & 1ull;
+        const bool sel = forced || (K > 0 && u[i] >= theta);
+        const uint64_t mask = __ballot(sel);
+        if (sel) {
+            Candidate c;
+            c.key = forced ? 0u : u[i];
+            c.score = sv[i];
+            c.id = id_of(i) | (forced ? kForcedFlag : 0);
+            buf[base + lanes_below(mask)] = c;
+        }
+        base += __popcll(mask);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    Candidate mine = {0u, -INFINITY, -1};
+    if (lane < base)
+        mine = buf[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t u1[1] = {mine.key};
+    const uint64_t f1 = (lane < base && (mine.id & kForcedFlag)) ? 1ull : 0ull;
+    return wave_select<1>(u1, f1, budget,
+                          [&](int, int slot) { emit(mine.score, mine.id & ~kForcedFlag, slot); });
+}
+
+// Picks the search for V values per lane: direct for small V, filtered above.
+template <int V, class IdOf, class Emit>
+__device__ __forceinline__ int select_row(const uint32_t (&u)[V], const float (&sv)[V],
+                                          uint64_t fbits, int budget, int lane, Candidate* buf,
+                                          IdOf&& id_of, Emit&& emit)
+{
+    if (V <= 2)
+        return wave_select<V>(u, fbits, budget,
+                              [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
+    return wave_select_filtered<V>(u, sv, fbits, budget, lane, buf, id_of, emit);
+}
+
 __device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
 {
     if (lane >= kept && lane < kTop) {
@@ -159,6 +246,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
 {
     __shared__ msa_top16_row part[NW];
+    __shared__ Candidate cand[NW][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t job = blockIdx.x;  // ((t * 4) + h) * R + r
@@ -198,10 +286,12 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
     }
 
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
-    const int kept = wave_select<V>(u, fbits, kTop - n_forced, [&](int i, int slot) {
-        dst->score[slot] = sv[i];
-        dst->id[slot] = span_lo + i * 64 + lane;
-    });
+    const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, lane, cand[wave],
+                                   [&](int i) { return span_lo + i * 64 + lane; },
+                                   [&](float score, int id, int slot) {
+                                       dst->score[slot] = score;
+                                       dst->id[slot] = id;
+                                   });
     pad_row(dst, kept, lane);
 
     if (NW > 1) {
@@ -215,6 +305,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
 {
     __shared__ msa_top16_row part[NW];
+    __shared__ Candidate cand[NW][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
@@ -258,10 +349,12 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
     const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
     msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
     const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
-    const int kept = wave_select<V>(u, fbits, budget, [&](int i, int slot) {
-        dst->score[slot] = sv[i];
-        dst->id[slot] = iv[i];
-    });
+    const int kept = select_row<V>(u, sv, fbits, budget, lane, cand[wave],
+                                   [&](int i) { return iv[i]; },
+                                   [&](float score, int id, int slot) {
+                                       dst->score[slot] = score;
+                                       dst->id[slot] = id;
+                                   });
     pad_row(dst, kept, lane);
 
     int found_forced = n_forced;

@@ -1,0 +1,245 @@
+"""GPU edge cases through the C ABI, checked against the CPU oracle.
+
+Select / merge (bit-exact): ties, signed zeros and -inf (the ranking
+treats -0 == +0, lower id wins), all-equal rows (more than 64 candidates at
+the threshold), empty and short rows, forced blocks covering everything,
+num_valid_pages outside [0, cols] (error counter, clamped), rows wide enough
+for the four-wave path, and up to the maximum number of ranges.
+
+Scorer: empty and one-token requests, sequences shorter than the decode
+length, exact multiples of 128, page_size 256 with odd block counts, every
+decode_query_len, a plane exactly as wide as the written columns, a plane
+too narrow (error counter, clamped), and out-of-range block_table entries
+(error counter, block scored -inf).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_block_msa_amd as msa
+import workloads
+from oracle_pins import CANARY_BITS
+from parity import assert_rows_equal, compare_plane, written_mask
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+TIE_POOL = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.5, 2.0], dtype=np.float32)
+
+
+def plane_of(rng, T, cols, kind):
+    if kind == "normal":
+        return rng.standard_normal((T, 4, cols)).astype(np.float32)
+    if kind == "ties":
+        return rng.choice(TIE_POOL, size=(T, 4, cols)).astype(np.float32)
+    if kind == "equal":
+        return np.full((T, 4, cols), 0.25, dtype=np.float32)
+    if kind == "zeros":
+        return rng.choice(np.array([0.0, -0.0], np.float32), size=(T, 4, cols))
+    if kind == "neginf":
+        p = np.full((T, 4, cols), -np.inf, dtype=np.float32)
+        p[:, :, ::7] = 1.0
+        return p
+    raise ValueError(kind)
+
+
+def gpu_select(plane, nvp, init, local, R):
+    T = plane.shape[0]
+    scores = torch.from_numpy(np.ascontiguousarray(plane)).to(DEV)
+    nvp_t = torch.from_numpy(np.ascontiguousarray(nvp, dtype=np.int32)).to(DEV)
+    out = msa.new_rows(T, 4, R, device=DEV)
+    out.fill_(0x7BADBEEF)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_top16_select(scores, nvp_t, out, init_blocks=init, local_blocks=local, num_ranges=R,
+                         errors=err)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    return msa.row_scores(o).numpy(), msa.row_ids(o).numpy(), int(err.item()), out, nvp_t
+
+
+def gpu_merge(rows, nvp_t, init, local):
+    T = rows.shape[0]
+    out = msa.new_rows(T, 4, device=DEV)
+    out.fill_(0x7BADBEEF)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_top16_merge(rows, nvp_t, out, init_blocks=init, local_blocks=local, errors=err)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    return msa.row_scores(o).numpy(), msa.row_ids(o).numpy(), int(err.item())
+
+
+SELECT_CASES = [
+    # (cols, R, init, local, kind)
+    (1, 1, 1, 2, "normal"),
+    (3, 1, 0, 0, "ties"),
+    (4, 2, 1, 2, "ties"),
+    (63, 1, 16, 0, "normal"),
+    (64, 1, 0, 16, "ties"),
+    (65, 3, 8, 8, "ties"),
+    (200, 1, 1, 2, "equal"),
+    (200, 4, 2, 2, "zeros"),
+    (256, 1, 1, 2, "neginf"),
+    (1000, 1, 1, 4, "ties"),
+    (1024, 1, 4, 4, "equal"),
+    (2048, 1, 2, 2, "normal"),
+    (2048, 2, 2, 2, "ties"),
+    (2049, 1, 1, 2, "normal"),
+    (4096, 1, 4, 4, "ties"),
+    (8192, 1, 4, 4, "normal"),
+    (8192, 8, 4, 4, "equal"),
+    (12287, 1, 1, 2, "ties"),
+    (12287, 5, 0, 0, "normal"),
+]
+
+
+@pytest.mark.parametrize("cols,R,init,local,kind", SELECT_CASES)
+def test_select_and_merge_edge(cols, R, init, local, kind):
+    rng = np.random.default_rng(cols * 7 + R)
+    T = 5
+    plane = plane_of(rng, T, cols, kind)
+    nvp = np.array([cols, 0, min(cols, 5), int(rng.integers(0, cols + 1)), max(0, cols - 1)],
+                   dtype=np.int32)
+    gs, gi, err, rows, nvp_t = gpu_select(plane, nvp, init, local, R)
+    os_, oi, obad = oracle.top16_select(plane, nvp, init_blocks=init, local_blocks=local,
+                                        num_ranges=R)
+    assert err == 0 and obad == 0
+    assert_rows_equal(gs, gi, os_, oi, f"select cols={cols} R={R} {kind}")
+    ms, mi, merr = gpu_merge(rows, nvp_t, init, local)
+    ws, wi, _ = oracle.top16_select(plane, nvp, init_blocks=init, local_blocks=local,
+                                    num_ranges=1)
+    assert merr == 0
+    assert_rows_equal(ms, mi, ws[:, :, 0], wi[:, :, 0], f"merge cols={cols} R={R} {kind}")
+
+
+@pytest.mark.parametrize("R", [16, 100, 768])
+def test_merge_many_ranges(R):
+    """Merge of up to 768 partial rows (12288 entries: the four-wave path)."""
+    rng = np.random.default_rng(R)
+    cols = max(R * 16, 1024)
+    cols = min(cols, 12287)
+    T = 3
+    plane = plane_of(rng, T, cols, "ties" if R == 100 else "normal")
+    nvp = np.array([cols, cols // 2, 7], dtype=np.int32)
+    init, local = 2, 3
+    gs, gi, err, rows, nvp_t = gpu_select(plane, nvp, init, local, R)
+    os_, oi, _ = oracle.top16_select(plane, nvp, init_blocks=init, local_blocks=local,
+                                     num_ranges=R)
+    assert err == 0
+    assert_rows_equal(gs, gi, os_, oi, f"select R={R}")
+    ms, mi, merr = gpu_merge(rows, nvp_t, init, local)
+    rs, ri, missing = oracle.top16_merge(os_, oi, nvp, init_blocks=init, local_blocks=local)
+    assert merr == 0 and missing == 0
+    assert_rows_equal(ms, mi, rs, ri, f"merge R={R}")
+
+
+def test_select_num_valid_pages_out_of_range():
+    """nvp < 0 or > cols: counted once per token and clamped, like the oracle."""
+    rng = np.random.default_rng(3)
+    T, cols = 4, 300
+    plane = plane_of(rng, T, cols, "normal")
+    nvp = np.array([-5, cols + 10, 20, cols], dtype=np.int32)
+    gs, gi, err, _, _ = gpu_select(plane, nvp, 1, 2, 2)
+    os_, oi, obad = oracle.top16_select(plane, nvp, init_blocks=1, local_blocks=2, num_ranges=2)
+    assert obad == 2 and err == 2
+    assert_rows_equal(gs, gi, os_, oi, "clamped nvp")
+
+
+def test_merge_reports_missing_forced_block():
+    rng = np.random.default_rng(4)
+    T, cols = 2, 128
+    plane = plane_of(rng, T, cols, "normal")
+    nvp = np.array([cols, cols], dtype=np.int32)
+    os_, oi, _ = oracle.top16_select(plane, nvp, init_blocks=2, local_blocks=2, num_ranges=2)
+    oi = oi.copy()
+    oi[0, 1, 0, 0] = -1  # drop forced block 0 of (token 0, head 1)
+    s = torch.from_numpy(np.ascontiguousarray(os_)).view(torch.int32)
+    i = torch.from_numpy(np.ascontiguousarray(oi))
+    rows = torch.cat([s, i], dim=-1).contiguous().to(DEV)
+    nvp_t = torch.from_numpy(nvp).to(DEV)
+    ms, mi, merr = gpu_merge(rows, nvp_t, 2, 2)
+    rs, ri, missing = oracle.top16_merge(os_, oi, nvp, init_blocks=2, local_blocks=2)
+    assert missing == 1 and merr >= 1
+    assert_rows_equal(ms, mi, rs, ri, "merge with a missing forced block")
+
+
+# ---------------------------------------------------------------------------
+# scorer edge cases
+# ---------------------------------------------------------------------------
+
+def run_scorer(w, cols, *, block_table=None, extra=0):
+    T = w.num_tokens
+    out = torch.full((T, 4, cols + extra), int(CANARY_BITS), dtype=torch.int32,
+                     device=DEV).view(torch.float32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bt = w.block_table if block_table is None else block_table
+    msa.msa_score_decode(w.index_q.to(DEV), w.index_k.to(DEV), bt.to(DEV), w.seq_lens.to(DEV),
+                         out, page_size=w.page_size, decode_query_len=w.dql, errors=err)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(err.item())
+
+
+def check_plane(w, got, cols_total, block_table=None):
+    bt = (w.block_table if block_table is None else block_table).numpy()
+    ref, amax, _ = oracle.score_decode(w.index_q.numpy(), w.index_k.numpy(), bt,
+                                       w.seq_lens.numpy(), page_size=w.page_size,
+                                       decode_query_len=w.dql, cols=cols_total, want_amax=True)
+    written = written_mask(w.seq_lens.numpy(), w.dql, cols_total)
+    n_bad, ratio = compare_plane(got, ref, amax, written)
+    assert n_bad == 0, f"{n_bad} elements out of tolerance (ratio {ratio})"
+    assert np.all(got.view(np.uint32)[~written] == CANARY_BITS), "unwritten column touched"
+
+
+@pytest.mark.parametrize("dql", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("page_size", [128, 256])
+def test_scorer_ragged_small(dql, page_size):
+    seqs = [0, 1, dql - 1 if dql > 1 else 2, 127, 128, 129, 383, 512, 777, 2048 + 5]
+    w = workloads.generate(batch=len(seqs), seq=("list", seqs), page_size=page_size, dql=dql,
+                           seed=100 + dql * 3 + page_size, scale=1.0)
+    got, err = run_scorer(w, w.cols, extra=8)
+    assert err == 0
+    check_plane(w, got, w.cols + 8)
+
+
+def test_scorer_plane_exactly_as_wide_as_written():
+    w = workloads.generate(batch=2, seq=("list", [4096, 4096 - 128 * 3]), page_size=128, dql=2,
+                           seed=7)
+    assert w.cols == 32
+    got, err = run_scorer(w, w.cols)
+    assert err == 0
+    check_plane(w, got, w.cols)
+
+
+def test_scorer_plane_too_narrow_is_counted_and_clamped():
+    w = workloads.generate(batch=2, seq=("list", [3000, 200]), page_size=256, dql=1, seed=8)
+    cols = 8  # request 0 needs 24 columns
+    got, err = run_scorer(w, cols)
+    assert err == 1
+    check_plane(w, got, cols)
+
+
+def test_scorer_bad_block_table_entries():
+    """Entries outside [0, num_pages) are counted; their blocks score -inf and
+    nothing outside index_k is read."""
+    w = workloads.generate(batch=2, seq=("list", [1000, 600]), page_size=128, dql=2, seed=9)
+    bt = w.block_table.clone()
+    num_pages = w.index_k.shape[0]
+    bt[0, 2] = num_pages          # one past the end
+    bt[1, 0] = -3                 # negative
+    got, err = run_scorer(w, w.cols, block_table=bt)
+    assert err == 2
+    # expected: the oracle's plane with those two blocks forced to -inf
+    ref_bt = w.block_table.clone()
+    ref, amax, _ = oracle.score_decode(w.index_q.numpy(), w.index_k.numpy(), ref_bt.numpy(),
+                                       w.seq_lens.numpy(), page_size=128, decode_query_len=2,
+                                       cols=w.cols, want_amax=True)
+    ref[0:2, :, 2] = -np.inf
+    ref[2:4, :, 0] = -np.inf
+    written = written_mask(w.seq_lens.numpy(), 2, w.cols)
+    n_bad, ratio = compare_plane(got, ref, amax, written)
+    assert n_bad == 0, (n_bad, ratio)
