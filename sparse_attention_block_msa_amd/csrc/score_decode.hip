@@ -18,7 +18,7 @@
 //    of whole 128-byte rows (a fully contiguous, non-temporal read), and the
 //    per-lane source addresses are chosen so the tile lands XOR-swizzled,
 //    letting the MFMA-layout ds_read_b128s hit every LDS bank once. Loads
-//    never occupy VGPRs, so the kernel runs 5 waves per SIMD and the
+//    never occupy VGPRs, so the kernel runs 4-6 waves per SIMD and the
 //    occupancy hides HBM latency. (Loading the MFMA layout straight into
 //    registers needs half-row 64-byte accesses per instruction; measured on
 //    MI355X, that pattern streams at about 5.2 TB/s against 6.5 TB/s for
@@ -53,7 +53,7 @@ namespace msa {
 namespace {
 
 // Launch shape: one 64-lane wave per workgroup, a block staged in kParts
-// pieces, and registers capped for 5 (<= 16 query rows) or 4 (32 rows)
+// pieces, and registers capped for 6 (<= 16 query rows) or 4 (32 rows)
 // waves per SIMD (LDS use: 4 KiB per wave).
 #ifndef MSA_SCORE_LOAD_AUX
 #define MSA_SCORE_LOAD_AUX 2  // cache-policy bits of the index-K DMA: nt (non-temporal)
@@ -62,7 +62,7 @@ namespace {
 #define MSA_SCORE_PARTS 4
 #endif
 #ifndef MSA_SCORE_WAVES_PER_EU_16
-#define MSA_SCORE_WAVES_PER_EU_16 5  // up to 16 query rows (decode_query_len <= 4)
+#define MSA_SCORE_WAVES_PER_EU_16 6  // up to 16 query rows (decode_query_len <= 4)
 #endif
 #ifndef MSA_SCORE_WAVES_PER_EU_32
 #define MSA_SCORE_WAVES_PER_EU_32 4  // 17..32 query rows (more registers for the Q tile)
