@@ -37,7 +37,9 @@
 //    row l%16, so the block max is a per-lane max over 8 tiles x 4 values
 //    followed by a max across the four 16-lane groups. The causal mask is
 //    applied only in blocks that reach past the first token's position.
-//  * Every 4 blocks the wave stores one float4 per query row.
+//  * The chunk's block maxima collect in a small per-wave LDS array and are
+//    stored to the plane (64 contiguous bytes per query row) only when the
+//    chunk is done, so no DMA wait ever waits on a plane store.
 //
 // Byte order inside a lane's operands: the 32 bytes a lane supplies per row
 // are bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the 128-byte row
@@ -70,6 +72,9 @@ namespace {
 #ifndef MSA_SCORE_CHUNK
 #define MSA_SCORE_CHUNK 16
 #endif
+
+constexpr int kChunk = MSA_SCORE_CHUNK;
+static_assert(kChunk % 4 == 0 && kChunk <= kMaxScoreChunk, "bad chunk");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)
 void score_decode_kernel(ScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
+    __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of the chunk
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -221,12 +227,12 @@ void score_decode_kernel(ScoreParams p)
             atomicAdd(p.errors, 1);
         wcols = p.cols;
     }
-    const int c_begin = chunk * p.chunk;
+    const int c_begin = chunk * kChunk;
     if (c_begin >= wcols)
         return;
     // c_begin is a multiple of 4 below roundup4(nblk), hence below nblk: the
     // chunk holds at least one block with keys.
-    const int c_end = min(c_begin + p.chunk, wcols);
+    const int c_end = min(c_begin + kChunk, wcols);
     const int c_last = min(c_end, nblk) - 1;
 
     const int rows = p.dql * kHeads;
@@ -274,47 +280,48 @@ void score_decode_kernel(ScoreParams p)
     }
 
     const int first_masked = seq - p.dql;  // blocks reaching past this key need the mask
-    for (int c4 = c_begin; c4 < c_end; c4 += 4) {
-        float vals[NT][4];
+    for (int c = c_begin; c < c_end; ++c) {
+        float mx[NT];
+        int lim[NT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = c4 + u;
-            float mx[NT];
-            int lim[NT];
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-                lim[n] = pos[n] - c * kBlockTokens;
-            const bool has_keys =
-                c <= c_last && !((bad_mask >> ((min(c, c_last) >> ps_shift) - pg_begin)) & 1ull);
-            if (!has_keys) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    mx[n] = -INFINITY;
-            } else if (c * kBlockTokens + (kBlockTokens - 1) > first_masked) {
-                score_block<NT, kParts, true>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
-            } else {
-                score_block<NT, kParts, false>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
-            }
+        for (int n = 0; n < NT; ++n)
+            lim[n] = pos[n] - c * kBlockTokens;
+        const bool has_keys =
+            c <= c_last && !((bad_mask >> ((min(c, c_last) >> ps_shift) - pg_begin)) & 1ull);
+        if (!has_keys) {
 #pragma unroll
             for (int n = 0; n < NT; ++n)
-                vals[n][u] = mx[n];
+                mx[n] = -INFINITY;
+        } else if (c * kBlockTokens + (kBlockTokens - 1) > first_masked) {
+            score_block<NT, kParts, true>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
+        } else {
+            score_block<NT, kParts, false>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
         }
-        // Lanes of group g == n store query row 16n + lane%16.
+        // lanes of group g == n keep query row 16n + lane%16
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int rho = n * 16 + r16;
-            if (g == n && rho < rows) {
-                const v4f v = {vals[n][0], vals[n][1], vals[n][2], vals[n][3]};
-                *reinterpret_cast<v4f*>(p.out + (row_base + rho) * p.cols + c4) = v;
-            }
-        }
+        for (int n = 0; n < NT; ++n)
+            if (g == n)
+                res[n * 16 + r16][c - c_begin] = mx[n];
+    }
+
+    // All plane stores are issued at the very end: on this ISA stores share
+    // the vector-memory counter with the DMA, so a store issued mid-chunk
+    // would make every later DMA wait also wait for it.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int quads = (c_end - c_begin) / 4;  // float4 groups per row
+    for (int i = lane; i < rows * quads; i += 64) {
+        const int rho = i / quads;
+        const int q4 = i - rho * quads;
+        const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
+        *reinterpret_cast<v4f*>(p.out + (row_base + rho) * p.cols + c_begin + q4 * 4) = v;
     }
 }
 
 }  // namespace
 
 constexpr int kParts = MSA_SCORE_PARTS;
-static_assert(MSA_SCORE_CHUNK % 4 == 0 && MSA_SCORE_CHUNK <= kMaxScoreChunk, "bad chunk");
 
 template <int NT>
 const void* score_kernel_fn()
