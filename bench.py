@@ -6,6 +6,10 @@ plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
 
     msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
 
+The same step with select and merge in one launch
+(msa_top16_select_merge, per-range rows also written) is timed beside it
+and reported under e2e.fused_select_merge.
+
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
 timing. Before every step a read pass over a 1 GiB buffer evicts index-K
 from the 256 MB Infinity Cache; it sits outside the step's event pair. (A
@@ -169,6 +173,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    # Timed region 1b: the same K steps with select and merge in one launch
+    # (msa_top16_select_merge, also writing the per-range rows), reported
+    # beside the headline.
+    def step_fused():
+        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
+                             decode_query_len=w.dql, errors=errors, stream=stream)
+        msa.msa_top16_select_merge(plane, nvp, final, init_blocks=w.init_blocks,
+                                   local_blocks=w.local_blocks, num_ranges=R, partial=part,
+                                   errors=errors, stream=stream)
+
+    fused_ms = None
+    if R <= 16 and -(-w.cols // R) <= 2048:
+        for _ in range(args.warmup):
+            step_fused()
+        fused_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                        for _ in range(args.steps)]
+        for i in range(args.steps):
+            if not args.no_flush:
+                flush.sum()
+            fused_events[i][0].record(stream)
+            step_fused()
+            fused_events[i][1].record(stream)
+        torch.cuda.synchronize()
+        fused_ms = sum(ev[0].elapsed_time(ev[1]) for ev in fused_events) / args.steps
+
     # Timed region 2: the same K steps with an event between every kernel,
     # for per-kernel durations (the events themselves lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -225,6 +254,10 @@ def main():
                 "kernels_ms": {"score_decode": score_mean, "top16_select": mean(select_ms),
                                "top16_merge": mean(merge_ms)},
                 "step_ms_with_kernel_events": mean([ev[0].elapsed_time(ev[3]) for ev in events]),
+                "fused_select_merge": None if fused_ms is None else {
+                    "ms_per_step": fused_ms, "keys_per_s": keys / (fused_ms * 1e-3),
+                    "hbm_gbps": launch_bytes / (fused_ms * 1e-3) / 1e9,
+                    "frac_of_peak": launch_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                 "wall_s_all_steps_incl_flush": wall},
         "roofline": {"kernel": "score_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -3,14 +3,16 @@
  * for AMD Instinct MI355X (gfx950).
  *
  * The library runs one decode step of a sparse-attention block indexer on one
- * GPU. There are three stream-ordered steps:
+ * GPU. There are three stream-ordered steps (steps 2 and 3 can also run as
+ * one launch, msa_top16_select_merge):
  *
  *   1. msa_score_decode: the score plane. Each decode token's 4 fp8 index
  *      heads are scored against the paged fp8 index-K cache, with one column
  *      per 128-token (B128) block.
  *   2. msa_top16_select: per (token, head) row, or per column range of the
- *      row, the forced begin/end blocks plus the best remaining blocks, as 16
- *      raw scores and 16 ascending block ids.
+ *      row, the forced blocks at both ends plus the best remaining blocks;
+ *      each kept block contributes its unscaled score and its id, and the
+ *      ids increase along the row.
  *   3. msa_top16_merge: merges the per-range Top16 lists of a row into one.
  *
  * The operations follow the FlashInfer msa_ops API pages:
@@ -61,12 +63,12 @@ extern "C" {
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
 
 /*
- * One Top16 row (128 bytes). score[i] is the raw score-plane value of block
- * id[i]. Ids ascend. Unused slots hold (score -inf, id -1) and follow the
- * used ones. Source: "msa_icp_topk_select_publish", description. The page
- * names a row of 16 raw scores and 16 ascending global ids. Its ready flag and
- * generation tags belong to the cross-GPU publish, which this library does
- * not have.
+ * One Top16 row (128 bytes). score[i] is the score-plane value of block
+ * id[i], unscaled. Ids ascend. Unused slots hold (score -inf, id -1) and
+ * follow the used ones. Source: "msa_icp_topk_select_publish", description
+ * (the row carries sixteen scores and sixteen increasing block ids). The
+ * page's row also has a ready flag or generation tags; those belong to the
+ * cross-GPU publish, which this library does not have.
  */
 typedef struct msa_top16_row {
     float score[MSA_TOPK];
@@ -112,10 +114,11 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
 
 /*
  * Step 2: Top16 select per (token, head, column range).
- * Source: "msa_icp_topk_select_publish" (description: 16 raw scores and 16
- * ascending global ids; every row written, padding rows included; scores;
- * num_valid_pages: global B128 block counts) and "prepare_msa_icp_indexer"
- * (init_blocks, local_blocks: forced begin / end blocks, sum at most 16).
+ * Source: "msa_icp_topk_select_publish" (description: the row format, and
+ * that each call writes all rows including padding rows; scores;
+ * num_valid_pages, which counts global B128 blocks) and
+ * "prepare_msa_icp_indexer" (init_blocks, local_blocks: the blocks forced
+ * in at the start and at the end of a row; at most 16 together).
  *
  * scores           device float32 [num_tokens, 4, cols], contiguous, 0 < cols < 12288.
  * num_valid_pages  device int32 [num_tokens]: valid block ids of token t are [0, n),
@@ -155,6 +158,30 @@ int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
 int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
                     msa_top16_row* out, int32_t* errors, hipStream_t stream);
+
+/*
+ * Steps 2 and 3 in one launch: Top16 select over R column ranges, then the
+ * merge of each (token, head) row's R range rows.
+ * Source: "prepare_msa_icp_indexer" (decode: score plane -> Top16 select ->
+ * merge); the select and merge rules are those of msa_top16_select and
+ * msa_top16_merge above.
+ *
+ * Arguments are as for msa_top16_select, and additionally:
+ * num_ranges  R, 1 <= R <= min(cols, 16), with ceil(cols / R) <= 2048. Larger
+ *             splits use the two separate calls.
+ * partial     device [num_tokens, 4, R] rows, or NULL. When given it receives
+ *             exactly what msa_top16_select writes.
+ * out         device [num_tokens, 4] rows. It receives exactly what
+ *             msa_top16_merge of those R rows writes.
+ *
+ * One workgroup per (token, head). Wave r selects range r and keeps its row in
+ * LDS, then one wave merges the R rows, so no partial rows go through memory
+ * between the two steps.
+ */
+int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols,
+                           const int32_t* num_valid_pages, int32_t init_blocks,
+                           int32_t local_blocks, int32_t num_ranges, msa_top16_row* partial,
+                           msa_top16_row* out, int32_t* errors, hipStream_t stream);
 
 /*
  * Score-plane width for requests of up to max_seq_len tokens:

@@ -14,10 +14,10 @@
  *   [P2] "flashinfer.msa_ops.prepare_msa_icp_indexer": decode chain
  *        (score plane -> Top16 select -> owner merge); init_blocks/local_blocks
  *        (forced begin/end blocks, sum at most 16).
- *   [P3] "flashinfer.msa_ops.msa_icp_topk_select_publish": description (row =
- *        16 raw scores + 16 ascending global ids, every row written including
- *        padding rows); scores (K limit); num_valid_pages (global B128 block
- *        counts).
+ *   [P3] "flashinfer.msa_ops.msa_icp_topk_select_publish": description (the
+ *        row format: sixteen unscaled scores with increasing block ids; all
+ *        rows are written on each call, padding rows too); scores (K limit);
+ *        num_valid_pages (a count of global B128 blocks).
  *   OCP 8-bit Floating Point Specification (OFP8), E4M3 format: bias 7, no
  *        infinities, S.1111.111 is NaN, exponent field 0 is subnormal.
  *

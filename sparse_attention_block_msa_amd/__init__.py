@@ -33,8 +33,8 @@ BLOCK_TOKENS = 128
 TOPK = 16
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
-EXPORTS = ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_score_columns",
-           "msa_warmup", "msa_last_error")
+EXPORTS = ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_top16_select_merge",
+           "msa_score_columns", "msa_warmup", "msa_last_error")
 
 
 class MsaError(RuntimeError):
@@ -66,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_top16_select.restype = ctypes.c_int
     lib.msa_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
     lib.msa_top16_merge.restype = ctypes.c_int
+    lib.msa_top16_select_merge.argtypes = [P, i32, i32, P, i32, i32, i32, P, P, P, P]
+    lib.msa_top16_select_merge.restype = ctypes.c_int
     lib.msa_score_columns.argtypes = [i64]
     lib.msa_score_columns.restype = i32
     lib.msa_warmup.argtypes = []
@@ -207,3 +209,30 @@ def msa_top16_merge(partial: torch.Tensor, num_valid_pages: torch.Tensor, out: t
     _check(lib.msa_top16_merge(partial.data_ptr(), T, R, num_valid_pages.data_ptr(), init_blocks,
                                local_blocks, out.data_ptr(), _errors_ptr(errors),
                                _stream_handle(stream)))
+
+
+def msa_top16_select_merge(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor,
+                           *, init_blocks: int, local_blocks: int, num_ranges: int,
+                           partial: torch.Tensor | None = None,
+                           errors: torch.Tensor | None = None, stream=None) -> None:
+    """Select over num_ranges column ranges and merge, in one launch: `out`
+    [T, 4, 32] receives the merged rows and `partial` [T, 4, R, 32] (optional)
+    the per-range rows."""
+    _dev(scores, num_valid_pages, out)
+    _need(scores.dtype == torch.float32 and scores.dim() == 3 and scores.shape[1] == NUM_HEADS and
+          scores.is_contiguous(), "scores: contiguous float32 [T, 4, cols]")
+    T, _, cols = scores.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, 32]")
+    if partial is not None:
+        _dev(scores, partial)
+        _need(partial.dtype == torch.int32 and
+              partial.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and partial.is_contiguous(),
+              f"partial: contiguous int32 [{T}, 4, {num_ranges}, 32]")
+    lib = load()
+    _check(lib.msa_top16_select_merge(
+        scores.data_ptr(), T, cols, num_valid_pages.data_ptr(), init_blocks, local_blocks,
+        num_ranges, partial.data_ptr() if partial is not None else None, out.data_ptr(),
+        _errors_ptr(errors), _stream_handle(stream)))

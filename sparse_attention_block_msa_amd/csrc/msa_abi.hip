@@ -179,6 +179,47 @@ int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t nu
     return launch_result(msa::launch_top16_merge(p, stream), fn);
 }
 
+int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols,
+                           const int32_t* num_valid_pages, int32_t init_blocks,
+                           int32_t local_blocks, int32_t num_ranges, msa_top16_row* partial,
+                           msa_top16_row* out, int32_t* errors, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_top16_select_merge";
+    MSA_CHECK(scores && num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(scores, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
+                  aligned(partial, 4) && aligned(errors, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4 < 2^31", fn, num_tokens);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SELECT_COLS,
+              "%s: cols (%d) must satisfy 0 < cols <= %d", fn, cols, MSA_MAX_SELECT_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= msa::kMaxFusedRanges,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              msa::kMaxFusedRanges);
+    const int32_t width = (cols + num_ranges - 1) / num_ranges;
+    MSA_CHECK(width <= msa::kMaxFusedWidth,
+              "%s: ceil(cols / num_ranges) = %d exceeds %d; use msa_top16_select + "
+              "msa_top16_merge", fn, width, msa::kMaxFusedWidth);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+
+    msa::SelectMergeParams p;
+    p.scores = scores;
+    p.nvp = num_valid_pages;
+    p.partial = partial;
+    p.out = out;
+    p.errors = errors;
+    p.num_tokens = num_tokens;
+    p.cols = cols;
+    p.init_blocks = init_blocks;
+    p.local_blocks = local_blocks;
+    p.num_ranges = num_ranges;
+    p.width = width;
+    return launch_result(msa::launch_top16_select_merge(p, stream), fn);
+}
+
 int msa_warmup(void)
 {
     g_last_error[0] = '\0';

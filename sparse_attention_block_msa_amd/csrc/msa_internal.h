@@ -64,7 +64,27 @@ struct MergeParams {
     int32_t local_blocks;
 };
 
+// Fused select + merge: at most this many ranges (one wave each) and at
+// most 2048 columns per range.
+constexpr int kMaxFusedRanges = 16;
+constexpr int kMaxFusedWidth = 2048;
+
+struct SelectMergeParams {
+    const float* scores;     // [T, 4, cols]
+    const int32_t* nvp;      // [T]
+    msa_top16_row* partial;  // [T, 4, R] or null
+    msa_top16_row* out;      // [T, 4]
+    int32_t* errors;         // nullable
+    int32_t num_tokens;
+    int32_t cols;
+    int32_t init_blocks;
+    int32_t local_blocks;
+    int32_t num_ranges;
+    int32_t width;           // ceil(cols / R)
+};
+
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream);
 hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream);
 

@@ -368,6 +368,91 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 }
 
+// Select over R ranges and merge, one (token, head) row per workgroup: wave
+// r selects range r exactly as top16_select_kernel does with one wave per
+// range, writes its row to `partial` (when given) and to LDS, and wave 0 then
+// merges the R rows exactly as top16_merge_kernel does (every forced id of
+// the row is in one of them, so the budget is 16 - |forced of [0, n)|).
+template <int V, int VM>
+__global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergeParams p)
+{
+    __shared__ msa_top16_row part[kMaxFusedRanges];
+    __shared__ Candidate cand[kMaxFusedRanges][64];
+    const int lane = threadIdx.x & 63;
+    const int r = threadIdx.x >> 6;
+    const int64_t th = blockIdx.x;  // t * 4 + h
+    const int t = (int)(th / kHeads);
+
+    int n = p.nvp[t];
+    if (n < 0 || n > p.cols) {
+        if ((th % kHeads) == 0 && threadIdx.x == 0 && p.errors)
+            atomicAdd(p.errors, 1);
+        n = n < 0 ? 0 : p.cols;
+    }
+    const int lo = r * p.width;
+    const int vhi = min(min(lo + p.width, p.cols), n);
+    const float* srow = p.scores + th * p.cols;
+
+    float sv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        sv[i] = srow[min(lo + i * 64 + lane, p.cols - 1)];
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    int n_forced = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int id = lo + i * 64 + lane;
+        const bool valid = id < vhi;
+        const bool forced = valid && is_forced(id, n, p.init_blocks, p.local_blocks);
+        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
+        fbits |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+    msa_top16_row* mine = &part[r];
+    const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, lane, cand[r],
+                                   [&](int i) { return lo + i * 64 + lane; },
+                                   [&](float score, int id, int slot) {
+                                       mine->score[slot] = score;
+                                       mine->id[slot] = id;
+                                   });
+    pad_row(mine, kept, lane);
+    __syncthreads();
+    if (p.partial && lane < 2 * kTop)
+        reinterpret_cast<int*>(p.partial + th * p.num_ranges + r)[lane] =
+            reinterpret_cast<const int*>(mine)[lane];
+    if (r != 0)
+        return;
+
+    // wave 0: merge the R rows from LDS
+    const int total = p.num_ranges * kTop;
+    float mv[VM];
+    int iv[VM];
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const int e = min(i * 64 + lane, total - 1);
+        mv[i] = part[e / kTop].score[e % kTop];
+        iv[i] = part[e / kTop].id[e % kTop];
+    }
+    uint32_t um[VM];
+    uint64_t fm = 0;
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const bool valid = i * 64 + lane < total && iv[i] >= 0;
+        const bool forced = valid && is_forced(iv[i], n, p.init_blocks, p.local_blocks);
+        um[i] = valid && !forced ? order_key(mv[i]) : 0u;
+        fm |= (uint64_t)forced << i;
+    }
+    msa_top16_row* dst = p.out + th;
+    const int kept_m = select_row<VM>(um, mv, fm, kTop - forced_count(n, p.init_blocks, p.local_blocks),
+                                      lane, cand[0], [&](int i) { return iv[i]; },
+                                      [&](float score, int id, int slot) {
+                                          dst->score[slot] = score;
+                                          dst->id[slot] = id;
+                                      });
+    pad_row(dst, kept_m, lane);
+}
+
 // Launch shape: spans up to 2048 elements use one wave with V = the next
 // power of two >= span/64; longer spans use 4 waves with V = 16, 32 or 48.
 struct Shape {
@@ -433,6 +518,34 @@ hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream)
     return hipErrorInvalidValue;
 }
 
+template <int V, int VM>
+hipError_t launch_fused_shape(const SelectMergeParams& p, hipStream_t stream)
+{
+    void* args[] = {const_cast<SelectMergeParams*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_select_merge_kernel<V, VM>),
+                           dim3((unsigned)((int64_t)p.num_tokens * kHeads)),
+                           dim3(p.num_ranges * 64), args, 0, stream);
+}
+
+#define MSA_FOR_EACH_FUSED_SHAPE(X) \
+    X(1, 1) X(2, 1) X(4, 1) X(8, 1) X(16, 1) X(32, 1) \
+    X(1, 2) X(2, 2) X(4, 2) X(8, 2) X(16, 2) X(32, 2) \
+    X(1, 4) X(2, 4) X(4, 4) X(8, 4) X(16, 4) X(32, 4)
+
+hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream)
+{
+    const Shape s = pick_shape(p.width);
+    const int vm = p.num_ranges <= 4 ? 1 : p.num_ranges <= 8 ? 2 : 4;
+    if (s.nw != 1)
+        return hipErrorInvalidValue;
+#define X(V, VM)                                   \
+    if (s.v == V && vm == VM)                      \
+        return launch_fused_shape<V, VM>(p, stream);
+    MSA_FOR_EACH_FUSED_SHAPE(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
 hipError_t warmup_top16_kernels()
 {
     hipFuncAttributes attr;
@@ -443,6 +556,12 @@ hipError_t warmup_top16_kernels()
     if (e == hipSuccess)                                                                          \
         e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_merge_kernel<V, NW>));
     MSA_FOR_EACH_SHAPE(X)
+#undef X
+#define X(V, VM)                                                                               \
+    if (e == hipSuccess)                                                                       \
+        e = hipFuncGetAttributes(&attr,                                                        \
+                                 reinterpret_cast<const void*>(&top16_select_merge_kernel<V, VM>));
+    MSA_FOR_EACH_FUSED_SHAPE(X)
 #undef X
     return e;
 }

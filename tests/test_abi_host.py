@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_score_columns",
-              "msa_warmup", "msa_last_error"):
+    for n in ("msa_score_decode", "msa_top16_select", "msa_top16_merge",
+              "msa_top16_select_merge", "msa_score_columns", "msa_warmup", "msa_last_error"):
         assert n in names
     assert set(names) == set(msa.EXPORTS)
 
@@ -159,3 +159,28 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def _fused(lib, **kw):
+    a = dict(scores=FAKE, T=4, cols=8192, nvp=FAKE, init=4, local=4, R=8, partial=None,
+             out=FAKE, errors=None, stream=None)
+    a.update(kw)
+    return lib.msa_top16_select_merge(a["scores"], a["T"], a["cols"], a["nvp"], a["init"],
+                                      a["local"], a["R"], a["partial"], a["out"], a["errors"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(scores=None), "null"),
+    (dict(out=None), "null"),
+    (dict(T=0), "num_tokens"),
+    (dict(cols=12288), "cols"),
+    (dict(R=17), "num_ranges"),
+    (dict(R=0), "num_ranges"),
+    (dict(cols=8192, R=2), "exceeds 2048"),
+    (dict(init=10, local=7), "exceeds"),
+    (dict(partial=FAKE + 2), "aligned"),
+])
+def test_select_merge_rejects(lib, kw, needle):
+    assert _fused(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()

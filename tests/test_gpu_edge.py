@@ -243,3 +243,55 @@ def test_scorer_bad_block_table_entries():
     written = written_mask(w.seq_lens.numpy(), 2, w.cols)
     n_bad, ratio = compare_plane(got, ref, amax, written)
     assert n_bad == 0, (n_bad, ratio)
+
+
+FUSED_CASES = [
+    # (cols, R, init, local, kind)
+    (1, 1, 1, 2, "normal"),
+    (64, 3, 8, 8, "ties"),
+    (300, 4, 1, 4, "equal"),
+    (1024, 1, 1, 4, "ties"),
+    (2048, 1, 2, 2, "normal"),
+    (2050, 2, 0, 0, "zeros"),
+    (8192, 8, 4, 4, "normal"),
+    (8192, 8, 4, 4, "ties"),
+    (8192, 16, 2, 14, "neginf"),
+    (12287, 16, 1, 2, "normal"),
+]
+
+
+@pytest.mark.parametrize("cols,R,init,local,kind", FUSED_CASES)
+@pytest.mark.parametrize("with_partial", [True, False])
+def test_select_merge_fused(cols, R, init, local, kind, with_partial):
+    """One-launch select + merge == msa_top16_select then msa_top16_merge ==
+    the oracle, bit for bit (merged rows and, when requested, range rows)."""
+    rng = np.random.default_rng(cols * 13 + R)
+    T = 5
+    plane = plane_of(rng, T, cols, kind)
+    nvp = np.array([cols, 0, min(cols, 5), int(rng.integers(0, cols + 1)), cols + 3],
+                   dtype=np.int32)
+    scores = torch.from_numpy(np.ascontiguousarray(plane)).to(DEV)
+    nvp_t = torch.from_numpy(nvp).to(DEV)
+    out = msa.new_rows(T, 4, device=DEV)
+    out.fill_(0x7BADBEEF)
+    part = msa.new_rows(T, 4, R, device=DEV) if with_partial else None
+    if part is not None:
+        part.fill_(0x7BADBEEF)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_top16_select_merge(scores, nvp_t, out, init_blocks=init, local_blocks=local,
+                               num_ranges=R, partial=part, errors=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1  # the token with num_valid_pages > cols
+    os_, oi, obad = oracle.top16_select(plane, nvp, init_blocks=init, local_blocks=local,
+                                        num_ranges=R)
+    assert obad == 1
+    clamped = np.minimum(np.maximum(nvp, 0), cols)
+    rs, ri, missing = oracle.top16_merge(os_, oi, clamped, init_blocks=init, local_blocks=local)
+    assert missing == 0
+    o = out.cpu()
+    assert_rows_equal(msa.row_scores(o).numpy(), msa.row_ids(o).numpy(), rs, ri,
+                      f"fused merge cols={cols} R={R} {kind}")
+    if part is not None:
+        pc = part.cpu()
+        assert_rows_equal(msa.row_scores(pc).numpy(), msa.row_ids(pc).numpy(), os_, oi,
+                          f"fused ranges cols={cols} R={R} {kind}")
