@@ -109,8 +109,6 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
     p.page_size = page_size;
     p.dql = decode_query_len;
     p.cols = cols;
-    p.chunk = msa::score_chunk_for(batch, cols);
-    p.chunks_per_req = (cols + p.chunk - 1) / p.chunk;
     return launch_result(msa::launch_score_decode(p, stream), fn);
 }
 

@@ -15,13 +15,6 @@ constexpr int kDim = MSA_HEAD_DIM;
 constexpr int kBlockTokens = MSA_BLOCK_TOKENS;
 constexpr int kTop = MSA_TOPK;
 
-// Plane columns (B128 blocks) one scorer wave produces: a multiple of 4 (so
-// every wave writes whole float4 groups of columns) of at most
-// kMaxScoreChunk (the chunk's block-table entries are held one per lane).
-// The host picks the chunk so that the grid has enough waves to fill the
-// GPU (score_chunk_for).
-constexpr int kMaxScoreChunk = 32;
-int score_chunk_for(int batch, int cols);
 
 struct ScoreParams {
     const uint8_t* q;        // [batch*dql, 4, 128] e4m3fn
@@ -36,8 +29,6 @@ struct ScoreParams {
     int32_t page_size;       // 128 or 256
     int32_t dql;             // 1..8
     int32_t cols;            // multiple of 4, <= 8192
-    int32_t chunk;           // columns per wave (multiple of 4, <= kMaxScoreChunk)
-    int32_t chunks_per_req;  // ceil(cols / chunk)
 };
 
 struct SelectParams {

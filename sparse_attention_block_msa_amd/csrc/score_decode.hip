@@ -9,17 +9,17 @@
 // block count rounded up to a multiple of four and no further.
 //
 // Design (one wave = 64 lanes per workgroup):
-//  * A wave owns a chunk of consecutive columns of one request. Its Q tile
-//    (4*dql <= 32 rows of 128 fp8 bytes) is converted once to bf16 and stays
-//    in registers for the whole chunk as the B operand of the MFMA.
+//  * A fixed grid of waves splits all requests' plane columns into equal
+//    contiguous ranges (see score_decode_kernel). A wave converts the Q tile
+//    of the request it is in (4*dql <= 32 rows of 128 fp8 bytes) to bf16
+//    once and keeps it in registers as the B operand of the MFMA.
 //  * A B128 block is 128 keys x 128 bytes = 16 KiB, contiguous inside one
 //    page. It is staged through a per-wave 4 KiB LDS tile in four pieces of
 //    32 keys with global_load_lds_dwordx4: each DMA instruction moves 1 KiB
 //    of whole 128-byte rows (a fully contiguous, non-temporal read), and the
 //    per-lane source addresses are chosen so the tile lands XOR-swizzled,
 //    letting the MFMA-layout ds_read_b128s hit every LDS bank once. Loads
-//    never occupy VGPRs, so the kernel runs 4-6 waves per SIMD and the
-//    occupancy hides HBM latency. (Loading the MFMA layout straight into
+//    never occupy VGPRs. (Loading the MFMA layout straight into
 //    registers needs half-row 64-byte accesses per instruction; measured on
 //    MI355X, that pattern streams at about 5.2 TB/s against 6.5 TB/s for
 //    whole-row DMA.)
@@ -55,26 +55,29 @@ namespace msa {
 namespace {
 
 // Launch shape: one 64-lane wave per workgroup, a block staged in kParts
-// pieces, and registers capped for 6 (<= 16 query rows) or 4 (32 rows)
-// waves per SIMD (LDS use: 4 KiB per wave).
+// pieces (LDS use: 4 KiB tile + 2 KiB results per wave), a grid of 3
+// (<= 16 query rows) or 2 (32 rows) waves per SIMD, measured best on the
+// five workloads.
 #ifndef MSA_SCORE_LOAD_AUX
 #define MSA_SCORE_LOAD_AUX 2  // cache-policy bits of the index-K DMA: nt (non-temporal)
 #endif
 #ifndef MSA_SCORE_PARTS
 #define MSA_SCORE_PARTS 4
 #endif
-#ifndef MSA_SCORE_WAVES_PER_EU_16
-#define MSA_SCORE_WAVES_PER_EU_16 6  // up to 16 query rows (decode_query_len <= 4)
-#endif
-#ifndef MSA_SCORE_WAVES_PER_EU_32
-#define MSA_SCORE_WAVES_PER_EU_32 4  // 17..32 query rows (more registers for the Q tile)
-#endif
+
 #ifndef MSA_SCORE_CHUNK
-#define MSA_SCORE_CHUNK 16
+#define MSA_SCORE_CHUNK 16  // columns per window (LDS result buffer)
+#endif
+#ifndef MSA_SCORE_WAVES_PER_SIMD_16
+#define MSA_SCORE_WAVES_PER_SIMD_16 3  // grid: waves per SIMD for up to 16 query rows
+#endif
+#ifndef MSA_SCORE_WAVES_PER_SIMD_32
+#define MSA_SCORE_WAVES_PER_SIMD_32 2  // grid: waves per SIMD for 17..32 query rows
 #endif
 
 constexpr int kChunk = MSA_SCORE_CHUNK;
-static_assert(kChunk % 4 == 0 && kChunk <= kMaxScoreChunk, "bad chunk");
+// a window's block-table entries are held one per lane
+static_assert(kChunk % 4 == 0 && kChunk <= 64, "bad window width");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -205,58 +208,90 @@ __device__ __forceinline__ void score_block(const uint8_t* block, uint8_t* tile,
     }
 }
 
-template <int NT, int kParts, int kWavesPerEU>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void score_decode_kernel(ScoreParams p)
+// Written plane columns of a request: roundup4(ceil(seq / 128)) clamped to
+// the plane width (*clamped says whether the width cut it short).
+__device__ __forceinline__ int written_cols(int seq, int cols, bool& clamped)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
-    __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of the chunk
-    const int lane = threadIdx.x;
-    const int r16 = lane & 15;
-    const int g = lane >> 4;
-    const int b = blockIdx.x / p.chunks_per_req;
-    const int chunk = blockIdx.x - b * p.chunks_per_req;
-
-    const int seq = p.seq_lens[b];
+    clamped = false;
     if (seq <= 0)
-        return;
-    const int nblk = (int)(((int64_t)seq + kBlockTokens - 1) / kBlockTokens);
-    int wcols = (int)(((int64_t)nblk + 3) / 4 * 4);
-    if (wcols > p.cols) {
-        if (chunk == 0 && lane == 0 && p.errors)
-            atomicAdd(p.errors, 1);
-        wcols = p.cols;
+        return 0;
+    const int64_t nblk = ((int64_t)seq + kBlockTokens - 1) / kBlockTokens;
+    const int64_t w = (nblk + 3) / 4 * 4;
+    clamped = w > cols;
+    return clamped ? cols : (int)w;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off)
+            v += o;
     }
-    const int c_begin = chunk * kChunk;
-    if (c_begin >= wcols)
-        return;
-    // c_begin is a multiple of 4 below roundup4(nblk), hence below nblk: the
-    // chunk holds at least one block with keys.
-    const int c_end = min(c_begin + kChunk, wcols);
-    const int c_last = min(c_end, nblk) - 1;
+    return v;
+}
 
-    const int rows = p.dql * kHeads;
-    const int64_t row_base = (int64_t)b * rows;
-    const int ps_shift = p.page_size == 256 ? 1 : 0;  // log2(B128 blocks per page)
+// Block-table entries of a window, one per lane.
+struct WindowPages {
+    int page;           // this lane's page (0 for an entry that is out of range)
+    uint64_t bad_mask;  // lanes whose entry was out of range
+};
 
-    // Block-table entries of this chunk, one per lane (at most kMaxScoreChunk).
+// Issues the loads of the block-table entries of columns [c_begin, c_last]
+// of request b (at most kChunk pages), one per lane.
+__device__ __forceinline__ WindowPages load_window_pages(const ScoreParams& p, int b, int c_begin,
+                                                         int c_last, int lane)
+{
+    const int ps_shift = p.page_size == 256 ? 1 : 0;
     const int pg_begin = c_begin >> ps_shift;
     const int pg_count = (c_last >> ps_shift) - pg_begin + 1;
-    int my_page = 0;
-    bool my_bad = false;
+    WindowPages w;
+    w.page = 0;
+    bool bad = false;
     if (lane < pg_count) {
         const int64_t idx = (int64_t)pg_begin + lane;
         if (idx >= p.bt_stride) {
-            my_bad = true;
+            bad = true;
         } else {
             const int v = p.bt[(int64_t)b * p.bt_stride + idx];
             if (v < 0 || (int64_t)v >= p.num_pages)
-                my_bad = true;
+                bad = true;
             else
-                my_page = v;
+                w.page = v;
         }
     }
-    const uint64_t bad_mask = __ballot(my_bad);
+    w.bad_mask = __ballot(bad);
+    return w;
+}
+
+// Scores one window: columns [c_begin, c_end) of request b (at most kChunk,
+// multiples of 4, c_begin < nblk), whose block-table entries are in wp. The
+// block maxima collect in res and are stored once, after the window's last
+// block: on this ISA stores share the vector-memory counter with the DMA, so
+// a store issued mid-window would make every later DMA wait also wait for it.
+template <int NT, int kParts>
+__device__ __forceinline__ void score_window(const ScoreParams& p, int b, int seq, int nblk,
+                                             int c_begin, int c_end, const WindowPages& wp,
+                                             const Bf16Slice (&qb)[NT], const int (&pos)[NT],
+                                             uint8_t* tile, float (*res)[kChunk], int lane,
+                                             int r16, int g)
+{
+    const int rows = p.dql * kHeads;
+    const int64_t row_base = (int64_t)b * rows;
+    const int ps_shift = p.page_size == 256 ? 1 : 0;  // log2(B128 blocks per page)
+    const int c_last = min(c_end, nblk) - 1;           // >= c_begin
+    const int pg_begin = c_begin >> ps_shift;
+    const int my_page = wp.page;
+    const uint64_t bad_mask = wp.bad_mask;
     if (bad_mask != 0 && lane == 0 && p.errors)
         atomicAdd(p.errors, (int)__popcll(bad_mask));
 
@@ -265,19 +300,6 @@ void score_decode_kernel(ScoreParams p)
         const int half = c & ((1 << ps_shift) - 1);
         return p.k + ((int64_t)page * p.page_size + half * kBlockTokens) * kDim;
     };
-
-    // Query tiles and token positions of the rows this lane's columns map to.
-    Bf16Slice qb[NT];
-    int pos[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int rho = n * 16 + r16;
-        pos[n] = seq - p.dql + (rho >> 2);
-        v8i raw = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        if (rho < rows)
-            raw = load_row_slice(p.q + (row_base + rho) * kDim, g);
-        qb[n] = to_bf16(raw);
-    }
 
     const int first_masked = seq - p.dql;  // blocks reaching past this key need the mask
     for (int c = c_begin; c < c_end; ++c) {
@@ -304,9 +326,6 @@ void score_decode_kernel(ScoreParams p)
                 res[n * 16 + r16][c - c_begin] = mx[n];
     }
 
-    // All plane stores are issued at the very end: on this ISA stores share
-    // the vector-memory counter with the DMA, so a store issued mid-chunk
-    // would make every later DMA wait also wait for it.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -317,32 +336,172 @@ void score_decode_kernel(ScoreParams p)
         const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
         *reinterpret_cast<v4f*>(p.out + (row_base + rho) * p.cols + c_begin + q4 * 4) = v;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Work split: the plane columns every request writes (a multiple of 4 each)
+// are laid end to end and cut into gridDim.x equal, contiguous ranges of
+// 4-column groups, one per wave; a range may run across request boundaries.
+// Ragged batches therefore load every wave alike, and a wave pays its setup
+// (sequence lengths, Q tile) once rather than per request chunk.
+template <int NT, int kParts, int kWavesPerEU>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void score_decode_kernel(ScoreParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
+    __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
+    const int lane = threadIdx.x;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int rows = p.dql * kHeads;
+
+    // Groups of all requests, this wave's range [g_lo, g_hi), the request b
+    // holding g_lo and the groups before it (base). One pass over seq_lens
+    // when the batch fits one wave, two otherwise.
+    int64_t g_lo, g_hi;
+    int b = 0;
+    int64_t base = 0;
+    if (p.batch <= 64) {
+        bool clamped;
+        const int gb = lane < p.batch ? written_cols(p.seq_lens[lane], p.cols, clamped) / 4 : 0;
+        const int incl = wave_inclusive_scan(gb, lane);
+        const int64_t total = __shfl(incl, 63);
+        g_lo = total * (int64_t)blockIdx.x / gridDim.x;
+        g_hi = total * ((int64_t)blockIdx.x + 1) / gridDim.x;
+        if (g_lo >= g_hi)
+            return;
+        const int l = __ffsll((unsigned long long)__ballot(incl > g_lo)) - 1;
+        b = l;
+        base = __shfl(incl - gb, l);
+    } else {
+        int64_t total = 0;
+        for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            bool clamped;
+            const int bb = b0 + lane;
+            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / 4 : 0;
+            total += wave_sum(gb);
+        }
+        g_lo = total * (int64_t)blockIdx.x / gridDim.x;
+        g_hi = total * ((int64_t)blockIdx.x + 1) / gridDim.x;
+        if (g_lo >= g_hi)
+            return;
+        for (int b0 = 0; b0 < p.batch; b0 += 64) {
+            bool clamped;
+            const int bb = b0 + lane;
+            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / 4 : 0;
+            const int incl = wave_inclusive_scan(gb, lane);
+            const int chunk_total = __shfl(incl, 63);
+            if (base + chunk_total > g_lo) {
+                const int l = __ffsll((unsigned long long)__ballot(base + incl > g_lo)) - 1;
+                b = b0 + l;
+                base += __shfl(incl - gb, l);
+                break;
+            }
+            base += chunk_total;
+        }
+    }
+
+    int64_t gcur = g_lo;
+    while (gcur < g_hi) {
+        const int seq = p.seq_lens[b];
+        bool clamped;
+        const int wcols = written_cols(seq, p.cols, clamped);
+        if (wcols == 0) {  // requests with no columns own no groups
+            ++b;
+            continue;
+        }
+        if (clamped && gcur == base && lane == 0 && p.errors)
+            atomicAdd(p.errors, 1);
+        const int nblk = (int)(((int64_t)seq + kBlockTokens - 1) / kBlockTokens);
+        const int64_t row_base = (int64_t)b * rows;
+        const int64_t g_end_b = base + wcols / 4;
+        const int c_stop = (int)((min(g_hi, g_end_b) - base) * 4);
+        int c = (int)((gcur - base) * 4);
+
+        // Q tile loads and the first window's block-table loads go out
+        // together; the tile is converted once both have landed.
+        v8i qraw[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int rho = n * 16 + r16;
+            qraw[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            if (rho < rows)
+                qraw[n] = load_row_slice(p.q + (row_base + rho) * kDim, g);
+        }
+        int c_end = min(c + kChunk, c_stop);
+        WindowPages wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane);
+        Bf16Slice qb[NT];
+        int pos[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            pos[n] = seq - p.dql + ((n * 16 + r16) >> 2);
+            qb[n] = to_bf16(qraw[n]);
+        }
+        while (true) {
+            score_window<NT, kParts>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
+                                     g);
+            c = c_end;
+            if (c >= c_stop)
+                break;
+            c_end = min(c + kChunk, c_stop);
+            wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane);
+        }
+        gcur = min(g_hi, g_end_b);
+        base = g_end_b;
+        ++b;
+    }
 }
 
 }  // namespace
 
 constexpr int kParts = MSA_SCORE_PARTS;
 
+// Grid size: a whole number of waves per SIMD of the device (every wave
+// gets an equal share of the work, so an uneven count would leave some SIMDs
+// with one wave more than others and set the tail). Registers are capped for
+// that many waves per SIMD.
+template <int NT>
+constexpr int waves_per_simd()
+{
+    return NT == 1 ? MSA_SCORE_WAVES_PER_SIMD_16 : MSA_SCORE_WAVES_PER_SIMD_32;
+}
+
 template <int NT>
 const void* score_kernel_fn()
 {
-    constexpr int kWavesPerEU = NT == 1 ? MSA_SCORE_WAVES_PER_EU_16 : MSA_SCORE_WAVES_PER_EU_32;
-    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kWavesPerEU>);
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, waves_per_simd<NT>()>);
 }
 
-int score_chunk_for(int batch, int cols)
+// Compute units of the current device (host query, cached per device).
+int device_cus()
 {
-    (void)batch;
-    (void)cols;
-    return MSA_SCORE_CHUNK;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((int64_t)p.batch * p.chunks_per_req));
+    // One wave per workgroup; no more waves than 4-column groups can exist.
+    const bool small_q = p.dql * kHeads <= 16;
+    const int64_t waves =
+        (int64_t)device_cus() * 4 * (small_q ? waves_per_simd<1>() : waves_per_simd<2>());
+    const int64_t max_groups = (int64_t)p.batch * (p.cols / 4);
+    const dim3 grid((unsigned)(max_groups < waves ? max_groups : waves));
     const dim3 block(64);
     void* args[] = {const_cast<ScoreParams*>(&p)};
-    const void* fn = p.dql * kHeads <= 16 ? score_kernel_fn<1>() : score_kernel_fn<2>();
+    const void* fn = small_q ? score_kernel_fn<1>() : score_kernel_fn<2>();
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
