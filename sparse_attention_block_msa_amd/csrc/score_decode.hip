@@ -74,6 +74,12 @@ namespace {
 #ifndef MSA_SCORE_WAVES_PER_SIMD_32
 #define MSA_SCORE_WAVES_PER_SIMD_32 2  // grid: waves per SIMD for 17..32 query rows
 #endif
+#ifndef MSA_SCORE_REG_WAVES_16
+#define MSA_SCORE_REG_WAVES_16 MSA_SCORE_WAVES_PER_SIMD_16  // register cap: waves per SIMD
+#endif
+#ifndef MSA_SCORE_REG_WAVES_32
+#define MSA_SCORE_REG_WAVES_32 MSA_SCORE_WAVES_PER_SIMD_32
+#endif
 
 constexpr int kChunk = MSA_SCORE_CHUNK;
 // a window's block-table entries are held one per lane
@@ -471,7 +477,8 @@ constexpr int waves_per_simd()
 template <int NT>
 const void* score_kernel_fn()
 {
-    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, waves_per_simd<NT>()>);
+    constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves>);
 }
 
 // Compute units of the current device (host query, cached per device).
