@@ -3,8 +3,9 @@
  * for AMD Instinct MI355X (gfx950).
  *
  * The library runs one decode step of a sparse-attention block indexer on one
- * GPU. There are three stream-ordered steps (steps 2 and 3 can also run as
- * one launch, msa_top16_select_merge):
+ * GPU. There are three stream-ordered steps (steps 1 and 2 can also run as
+ * one launch, msa_score_select, and so can steps 2 and 3,
+ * msa_top16_select_merge):
  *
  *   1. msa_score_decode: the score plane. Each decode token's 4 fp8 index
  *      heads are scored against the paged fp8 index-K cache, with one column
@@ -110,6 +111,42 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
                      const int32_t* block_table, int64_t block_table_stride,
                      const int32_t* seq_lens, int32_t batch, int32_t page_size,
                      int32_t decode_query_len, float* score_out, int32_t cols, int32_t* errors,
+                     hipStream_t stream);
+
+/*
+ * Steps 1 and 2 in one launch: the score plane, and Top16 select per (token,
+ * head, column range) on it.
+ * Source: "prepare_msa_icp_indexer", decode: the chain score plane -> Top16
+ * select -> merge, whose first two steps a fused scorer
+ * (msa_icp_decode_score_publish) can replace, given caller-owned pool storage.
+ * Here the fused launch keeps both steps' outputs, those of msa_score_decode
+ * and msa_top16_select, and publishes nothing.
+ *
+ * Arguments are those of msa_score_decode, then:
+ * num_valid_pages  device int32 [batch * decode_query_len], as for msa_top16_select.
+ * init_blocks, local_blocks  >= 0, sum <= 16.
+ * num_ranges       R, 1 <= R <= min(cols, 768), with ceil(cols / R) <= 2048. Larger
+ *                  spans use the two separate calls.
+ * out              device [batch * decode_query_len, 4, R] rows.
+ * workspace        device int32 [batch * R], caller-owned. It must hold zeros when the
+ *                  call is made, and the launch leaves it holding zeros. Launches that
+ *                  share a workspace must not overlap. If `errors` counted a wait
+ *                  timeout (below), re-zero the workspace before the next call.
+ *
+ * score_out receives exactly what msa_score_decode writes, and out exactly what
+ * msa_top16_select(score_out, ..., num_ranges) then writes. The waves that score the
+ * plane also run the select jobs. A job waits until every column of its range that
+ * this launch writes has been stored. That wait is only for scoring work, and the
+ * launch is sized so every wave is resident at once. A wait still open after
+ * 2 seconds (possible only if other work holds the device's compute units) is
+ * counted in `errors`, and the job then reads the plane as it stands.
+ */
+int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                     const int32_t* block_table, int64_t block_table_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                     int32_t decode_query_len, float* score_out, int32_t cols,
+                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                     int32_t num_ranges, msa_top16_row* out, int32_t* workspace, int32_t* errors,
                      hipStream_t stream);
 
 /*

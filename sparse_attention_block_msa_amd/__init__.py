@@ -33,7 +33,7 @@ BLOCK_TOKENS = 128
 TOPK = 16
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
-EXPORTS = ("msa_score_decode", "msa_top16_select", "msa_top16_merge", "msa_top16_select_merge",
+EXPORTS = ("msa_score_decode", "msa_score_select", "msa_top16_select", "msa_top16_merge", "msa_top16_select_merge",
            "msa_score_columns", "msa_warmup", "msa_last_error")
 
 
@@ -62,6 +62,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.msa_score_decode.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, P]
     lib.msa_score_decode.restype = ctypes.c_int
+    lib.msa_score_select.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, i32, i32,
+                                     i32, P, P, P, P]
+    lib.msa_score_select.restype = ctypes.c_int
     lib.msa_top16_select.argtypes = [P, i32, i32, P, i32, i32, i32, P, P, P]
     lib.msa_top16_select.restype = ctypes.c_int
     lib.msa_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
@@ -145,12 +148,8 @@ def msa_warmup() -> None:
     _check(load().msa_warmup())
 
 
-def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
-                     seq_lens: torch.Tensor, score_out: torch.Tensor, *, page_size: int,
-                     decode_query_len: int, errors: torch.Tensor | None = None,
-                     stream=None) -> None:
-    """Writes the score plane score_out [T, 4, cols] (columns past each
-    request's roundup4(ceil(seq_len/128)) untouched). See msa_indexer.h."""
+def _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
+                decode_query_len):
     q = _u8(index_q, "index_q")
     k = _u8(index_k, "index_k")
     _dev(q, k, block_table, seq_lens, score_out)
@@ -166,11 +165,54 @@ def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
     _need(score_out.dtype == torch.float32 and score_out.dim() == 3 and
           score_out.shape[:2] == (B * decode_query_len, NUM_HEADS) and score_out.is_contiguous(),
           "score_out: contiguous float32 [T, 4, cols]")
-    lib = load()
-    _check(lib.msa_score_decode(
-        q.data_ptr(), k.data_ptr(), k.shape[0], block_table.data_ptr(), block_table.shape[1],
-        seq_lens.data_ptr(), B, page_size, decode_query_len, score_out.data_ptr(),
-        score_out.shape[2], _errors_ptr(errors), _stream_handle(stream)))
+    return (q.data_ptr(), k.data_ptr(), k.shape[0], block_table.data_ptr(), block_table.shape[1],
+            seq_lens.data_ptr(), B, page_size, decode_query_len, score_out.data_ptr(),
+            score_out.shape[2])
+
+
+def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, score_out: torch.Tensor, *, page_size: int,
+                     decode_query_len: int, errors: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """Writes the score plane score_out [T, 4, cols] (columns past each
+    request's roundup4(ceil(seq_len/128)) untouched). See msa_indexer.h."""
+    args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
+                       decode_query_len)
+    _check(load().msa_score_decode(*args, _errors_ptr(errors), _stream_handle(stream)))
+
+
+def score_select_workspace(batch: int, num_ranges: int, device="cuda") -> torch.Tensor:
+    """A zeroed int32 workspace [batch * num_ranges] for msa_score_select. The
+    launch leaves it zeroed, so one workspace serves every later call of that
+    size or smaller on the same stream."""
+    return torch.zeros(batch * num_ranges, dtype=torch.int32, device=device)
+
+
+def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, score_out: torch.Tensor,
+                     num_valid_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     *, page_size: int, decode_query_len: int, init_blocks: int,
+                     local_blocks: int, num_ranges: int = 1,
+                     errors: torch.Tensor | None = None, stream=None) -> None:
+    """Score plane and per-range Top16 rows in one launch: score_out as
+    msa_score_decode writes it, `out` [T, 4, R, 32] as msa_top16_select then
+    writes it. `workspace` is int32 [>= batch * R], zero on entry (see
+    score_select_workspace)."""
+    args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
+                       decode_query_len)
+    B = seq_lens.numel()
+    T = B * decode_query_len
+    _dev(score_out, num_valid_pages, out, workspace)
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, {num_ranges}, 32]")
+    _need(workspace.dtype == torch.int32 and workspace.is_contiguous() and
+          workspace.numel() >= B * num_ranges,
+          f"workspace: contiguous int32 with >= {B * num_ranges} elements")
+    _check(load().msa_score_select(*args, num_valid_pages.data_ptr(), init_blocks, local_blocks,
+                                   num_ranges, out.data_ptr(), workspace.data_ptr(),
+                                   _errors_ptr(errors), _stream_handle(stream)))
 
 
 def msa_top16_select(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,

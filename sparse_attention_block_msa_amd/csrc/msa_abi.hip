@@ -47,6 +47,48 @@ int check_forced(const char* fn, int32_t init_blocks, int32_t local_blocks)
     return MSA_OK;
 }
 
+// Host checks of the score-plane arguments shared by msa_score_decode and
+// msa_score_select; fills *p on success.
+int score_params(const char* fn, const uint8_t* index_q, const uint8_t* index_k,
+                 int64_t num_pages, const int32_t* block_table, int64_t block_table_stride,
+                 const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                 int32_t decode_query_len, float* score_out, int32_t cols, int32_t* errors,
+                 msa::ScoreParams* p)
+{
+    MSA_CHECK(index_q && index_k && block_table && seq_lens && score_out,
+              "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(index_q, 16) && aligned(index_k, 16) && aligned(score_out, 16),
+              "%s: index_q, index_k and score_out must be 16-byte aligned", fn);
+    MSA_CHECK(aligned(block_table, 4) && aligned(seq_lens, 4) && aligned(errors, 4),
+              "%s: int32 arrays must be 4-byte aligned", fn);
+    MSA_CHECK(page_size == 128 || page_size == 256, "%s: page_size (%d) must be 128 or 256", fn,
+              page_size);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn,
+              batch);
+    MSA_CHECK(num_pages >= 1, "%s: num_pages (%lld) must be >= 1", fn, (long long)num_pages);
+    MSA_CHECK(block_table_stride >= 1, "%s: block_table_stride (%lld) must be >= 1", fn,
+              (long long)block_table_stride);
+    p->q = index_q;
+    p->k = index_k;
+    p->num_pages = num_pages;
+    p->bt = block_table;
+    p->bt_stride = block_table_stride;
+    p->seq_lens = seq_lens;
+    p->out = score_out;
+    p->errors = errors;
+    p->batch = batch;
+    p->page_size = page_size;
+    p->dql = decode_query_len;
+    p->cols = cols;
+    return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,41 +117,56 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
                      hipStream_t stream)
 {
     g_last_error[0] = '\0';
-    const char* fn = "msa_score_decode";
-    MSA_CHECK(index_q && index_k && block_table && seq_lens && score_out,
-              "%s: null pointer argument", fn);
-    MSA_CHECK(aligned(index_q, 16) && aligned(index_k, 16) && aligned(score_out, 16),
-              "%s: index_q, index_k and score_out must be 16-byte aligned", fn);
-    MSA_CHECK(aligned(block_table, 4) && aligned(seq_lens, 4) && aligned(errors, 4),
-              "%s: int32 arrays must be 4-byte aligned", fn);
-    MSA_CHECK(page_size == 128 || page_size == 256, "%s: page_size (%d) must be 128 or 256", fn,
-              page_size);
-    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
-              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
-              decode_query_len);
-    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
-              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
-              MSA_MAX_SCORE_COLS);
-    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn,
-              batch);
-    MSA_CHECK(num_pages >= 1, "%s: num_pages (%lld) must be >= 1", fn, (long long)num_pages);
-    MSA_CHECK(block_table_stride >= 1, "%s: block_table_stride (%lld) must be >= 1", fn,
-              (long long)block_table_stride);
-
     msa::ScoreParams p;
-    p.q = index_q;
-    p.k = index_k;
-    p.num_pages = num_pages;
-    p.bt = block_table;
-    p.bt_stride = block_table_stride;
-    p.seq_lens = seq_lens;
-    p.out = score_out;
-    p.errors = errors;
-    p.batch = batch;
-    p.page_size = page_size;
-    p.dql = decode_query_len;
-    p.cols = cols;
-    return launch_result(msa::launch_score_decode(p, stream), fn);
+    const int rc = score_params("msa_score_decode", index_q, index_k, num_pages, block_table,
+                                block_table_stride, seq_lens, batch, page_size, decode_query_len,
+                                score_out, cols, errors, &p);
+    if (rc != MSA_OK)
+        return rc;
+    return launch_result(msa::launch_score_decode(p, stream), "msa_score_decode");
+}
+
+int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                     const int32_t* block_table, int64_t block_table_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                     int32_t decode_query_len, float* score_out, int32_t cols,
+                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                     int32_t num_ranges, msa_top16_row* out, int32_t* workspace, int32_t* errors,
+                     hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_score_select";
+    msa::ScoreSelectParams q;
+    int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
+                          seq_lens, batch, page_size, decode_query_len, score_out, cols, errors,
+                          &q.score);
+    if (rc != MSA_OK)
+        return rc;
+    MSA_CHECK(num_valid_pages && out && workspace, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(num_valid_pages, 4) && aligned(out, 4) && aligned(workspace, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    const int64_t tokens = (int64_t)batch * decode_query_len;
+    MSA_CHECK(tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
+              "%s: tokens*4*num_ranges must be < 2^31", fn);
+    const int32_t width = (cols + num_ranges - 1) / num_ranges;
+    MSA_CHECK(width <= msa::kMaxFusedWidth,
+              "%s: ceil(cols / num_ranges) = %d exceeds %d; use msa_score_decode + "
+              "msa_top16_select", fn, width, msa::kMaxFusedWidth);
+    rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+    q.nvp = num_valid_pages;
+    q.out = out;
+    q.counters = workspace;
+    q.init_blocks = init_blocks;
+    q.local_blocks = local_blocks;
+    q.num_ranges = num_ranges;
+    q.width = width;
+    q.spin_ticks = 0;
+    return launch_result(msa::launch_score_select(q, stream), fn);
 }
 
 int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,

@@ -74,7 +74,21 @@ struct SelectMergeParams {
     int32_t width;           // ceil(cols / R)
 };
 
+// Scorer plus per-range select in one launch (same ranges as SelectParams).
+struct ScoreSelectParams {
+    ScoreParams score;
+    const int32_t* nvp;      // [batch*dql]
+    msa_top16_row* out;      // [batch*dql, 4, R]
+    int32_t* counters;       // [batch, R]; zero on entry, zero again on exit
+    int32_t init_blocks;
+    int32_t local_blocks;
+    int32_t num_ranges;
+    int32_t width;           // ceil(cols / R) <= kMaxFusedWidth
+    int64_t spin_ticks;      // set by the launcher
+};
+
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream);
 hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream);
 hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream);

@@ -50,6 +50,7 @@
 #include <math.h>
 
 #include "msa_internal.h"
+#include "top16_device.h"
 
 namespace msa {
 namespace {
@@ -352,12 +353,13 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
 // 4-column groups, one per wave; a range may run across request boundaries.
 // Ragged batches therefore load every wave alike, and a wave pays its setup
 // (sequence lengths, Q tile) once rather than per request chunk.
-template <int NT, int kParts, int kWavesPerEU>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void score_decode_kernel(ScoreParams p)
+// segment_done(b, c_begin, c_end) runs after the wave has issued the plane
+// stores of columns [c_begin, c_end) of request b, once per request it
+// touches.
+template <int NT, int kParts, class SegmentDone>
+__device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* tile,
+                                                 float (*res)[kChunk], SegmentDone&& segment_done)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
-    __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -424,7 +426,8 @@ void score_decode_kernel(ScoreParams p)
         const int64_t row_base = (int64_t)b * rows;
         const int64_t g_end_b = base + wcols / 4;
         const int c_stop = (int)((min(g_hi, g_end_b) - base) * 4);
-        int c = (int)((gcur - base) * 4);
+        const int c_first = (int)((gcur - base) * 4);
+        int c = c_first;
 
         // Q tile loads and the first window's block-table loads go out
         // together; the tile is converted once both have landed.
@@ -454,9 +457,111 @@ void score_decode_kernel(ScoreParams p)
             c_end = min(c + kChunk, c_stop);
             wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane);
         }
+        segment_done(b, c_first, c_stop);
         gcur = min(g_hi, g_end_b);
         base = g_end_b;
         ++b;
+    }
+}
+
+template <int NT, int kParts, int kWavesPerEU>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void score_decode_kernel(ScoreParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
+    __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
+    score_wave_range<NT, kParts>(p, tile, res, [](int, int, int) {});
+}
+
+// Waits until the produced-column count in the low 16 bits of *ctr reaches
+// `expected`, for at most spin_ticks of the device's constant-rate clock, then
+// acquires (agent scope) what the producers released. Returns false on
+// timeout.
+__device__ __forceinline__ bool wait_for_columns(const int32_t* ctr, int expected,
+                                                 int64_t spin_ticks)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
+    while ((__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) <
+           expected) {
+        if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > spin_ticks) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return ok;
+}
+
+// Score plane and per-range Top16 rows in one launch. Every wave first scores
+// its columns exactly as score_decode_kernel does. After each request segment
+// it releases its plane stores (agent scope) and adds the segment's column
+// count, per column range, to counters[b * R + r]. It then runs select jobs
+// j = blockIdx.x, blockIdx.x + gridDim.x, ... over the (token, head, range)
+// rows, in the row order of the select kernel. A job waits until every column
+// of its range that this launch writes has been counted, then selects exactly
+// as the select kernel does, and adds 1 << 16 to the counter as a consumer
+// mark. The last of the range's 4*dql consumers resets the counter to zero,
+// so the counters are zero again when the launch ends. The wait is only for
+// scoring work, which waits on nothing, and the host keeps the grid within
+// the waves the device holds at once, so every wait ends; the clock limit
+// counts an error instead of spinning on if that fails, and a wave that has
+// timed out once counts its later unfinished waits without waiting.
+template <int NT, int kParts, int kWavesPerEU, int V>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void score_select_kernel(ScoreSelectParams q)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
+    __shared__ __attribute__((aligned(16))) float res[32][kChunk];
+    __shared__ topk::Candidate cand[64];
+    const ScoreParams& p = q.score;
+    const int lane = threadIdx.x;
+    const int R = q.num_ranges;
+    const int w = q.width;
+
+    score_wave_range<NT, kParts>(p, tile, res, [&](int b, int c_begin, int c_end) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) {
+            for (int r = c_begin / w; r * w < c_end; ++r) {
+                const int n = min(c_end, (r + 1) * w) - max(c_begin, r * w);
+                atomicAdd(q.counters + (int64_t)b * R + r, n);
+            }
+        }
+    });
+
+    const int rows = p.dql * kHeads;
+    const int64_t jobs = (int64_t)p.batch * rows * R;
+    bool patient = true;  // after one timed-out wait this wave waits no more
+    for (int64_t job = blockIdx.x; job < jobs; job += gridDim.x) {
+        const int r = (int)(job % R);
+        const int64_t th = job / R;  // t * 4 + h
+        const int t = (int)(th / kHeads);
+        const int b = t / p.dql;
+        int n = q.nvp[t];
+        if (n < 0 || n > p.cols) {
+            if (r == 0 && (th % kHeads) == 0 && lane == 0 && p.errors)
+                atomicAdd(p.errors, 1);
+            n = n < 0 ? 0 : p.cols;
+        }
+        const int lo = r * w;
+        const int hi = min(lo + w, p.cols);
+        bool clamped;
+        const int wb = written_cols(p.seq_lens[b], p.cols, clamped);
+        const int expected = max(0, min(hi, wb) - lo);
+        int32_t* ctr = q.counters + (int64_t)b * R + r;
+        if (expected > 0 && !(patient && wait_for_columns(ctr, expected, q.spin_ticks))) {
+            patient = false;
+            if (lane == 0 && p.errors)
+                atomicAdd(p.errors, 1);
+        }
+        topk::select_span<V>(p.out + th * p.cols, p.cols, lo, min(hi, n), n, q.init_blocks,
+                             q.local_blocks, q.out + job, lane, cand);
+        if (lane == 0) {
+            const int old = atomicAdd(ctr, 1 << 16);
+            if ((old >> 16) == rows - 1)
+                atomicExch(ctr, 0);
+        }
     }
 }
 
@@ -481,6 +586,13 @@ const void* score_kernel_fn()
     return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves>);
 }
 
+template <int NT, int V>
+const void* score_select_kernel_fn()
+{
+    constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
+    return reinterpret_cast<const void*>(&score_select_kernel<NT, kParts, kRegWaves, V>);
+}
+
 // Compute units of the current device (host query, cached per device).
 int device_cus()
 {
@@ -498,27 +610,87 @@ int device_cus()
     return cached[dev];
 }
 
-hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
+// Ticks of the device's constant-rate clock (s_memrealtime) in 2 seconds.
+int64_t spin_ticks_2s()
 {
-    // One wave per workgroup; no more waves than 4-column groups can exist.
+    static int64_t cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 200000000;  // 100 MHz
+    if (cached[dev] == 0) {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+            khz <= 0)
+            khz = 100000;
+        cached[dev] = (int64_t)khz * 2000;
+    }
+    return cached[dev];
+}
+
+// Scorer grid: one wave per workgroup, a whole number of waves per SIMD, no
+// more waves than 4-column groups can exist.
+int64_t score_grid(const ScoreParams& p)
+{
     const bool small_q = p.dql * kHeads <= 16;
     const int64_t waves =
         (int64_t)device_cus() * 4 * (small_q ? waves_per_simd<1>() : waves_per_simd<2>());
     const int64_t max_groups = (int64_t)p.batch * (p.cols / 4);
-    const dim3 grid((unsigned)(max_groups < waves ? max_groups : waves));
-    const dim3 block(64);
+    return max_groups < waves ? max_groups : waves;
+}
+
+hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
+{
     void* args[] = {const_cast<ScoreParams*>(&p)};
-    const void* fn = small_q ? score_kernel_fn<1>() : score_kernel_fn<2>();
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    const void* fn = p.dql * kHeads <= 16 ? score_kernel_fn<1>() : score_kernel_fn<2>();
+    return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
+}
+
+// Values per lane of the fused kernel's select: spans up to 256, 1024 and
+// 2048 columns.
+#define MSA_FOR_EACH_SCORE_SELECT(X) X(1, 4) X(1, 16) X(1, 32) X(2, 4) X(2, 16) X(2, 32)
+
+hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
+{
+    const int nt = q.score.dql * kHeads <= 16 ? 1 : 2;
+    const int v = q.width <= 256 ? 4 : q.width <= 1024 ? 16 : q.width <= kMaxFusedWidth ? 32 : 0;
+    const void* fn = nullptr;
+#define X(NT, V)                                \
+    if (nt == NT && v == V)                     \
+        fn = score_select_kernel_fn<NT, V>();
+    MSA_FOR_EACH_SCORE_SELECT(X)
+#undef X
+    if (fn == nullptr)
+        return hipErrorInvalidValue;
+    // Every wave must be resident at once (select jobs wait on other waves'
+    // scoring), so the grid is capped at what the device holds.
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
+    if (e != hipSuccess)
+        return e;
+    if (per_cu <= 0)
+        return hipErrorInvalidConfiguration;
+    int64_t grid = score_grid(q.score);
+    const int64_t resident = (int64_t)per_cu * device_cus();
+    if (grid > resident)
+        grid = resident;
+    ScoreSelectParams qq = q;
+    qq.spin_ticks = spin_ticks_2s();
+    void* args[] = {&qq};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), args, 0, stream);
 }
 
 hipError_t warmup_score_kernels()
 {
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, score_kernel_fn<1>());
-    if (e != hipSuccess)
-        return e;
-    return hipFuncGetAttributes(&attr, score_kernel_fn<2>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_kernel_fn<2>());
+#define X(NT, V)          \
+    if (e == hipSuccess)  \
+        e = hipFuncGetAttributes(&attr, score_select_kernel_fn<NT, V>());
+    MSA_FOR_EACH_SCORE_SELECT(X)
+#undef X
+    return e;
 }
 
 }  // namespace msa

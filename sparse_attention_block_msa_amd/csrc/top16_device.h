@@ -1,0 +1,276 @@
+// Wave-level Top16 selection shared by the select/merge kernels and the
+// fused scorer. Every routine here runs on one 64-lane wave.
+//
+// Rule ("flashinfer.msa_ops.msa_icp_topk_select_publish", description;
+// "flashinfer.msa_ops.prepare_msa_icp_indexer", init_blocks / local_blocks):
+// a row keeps its forced begin/end blocks ([0, init) and [n - local, n)
+// within the valid ids [0, n)) and the best 16 - |forced| of its other valid
+// blocks, ranked by score descending and then lower id, and lists them by
+// ascending id; unused slots hold (-inf, -1).
+//
+//  * Ranking key: the fp32 score mapped to an order-preserving uint32 (with -0
+//    mapped to +0, so -0 and +0 tie); non-candidates get key 0, below every
+//    real score. The K-th largest key is found by a 32-step bitwise descent in
+//    which each step counts keys >= a trial value with one ballot + popcount
+//    per register (no cross-lane reduction needed). Ties at that key are
+//    broken by element order using the same ballots and mbcnt.
+//  * Kept elements are compacted to their ascending-id slot with mbcnt.
+#pragma once
+
+#include <math.h>
+
+#include "msa_internal.h"
+
+namespace msa {
+namespace topk {
+
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ int is_forced(int id, int n, int init_blocks, int local_blocks)
+{
+    return id >= 0 && id < n && (id < init_blocks || id >= n - local_blocks);
+}
+
+// Wave-level select. Element i of this lane has key u[i] (0 = not a
+// candidate) and is forced if bit i of fbits is set. Keeps all forced
+// elements and the best min(budget, #candidates) candidates, and calls
+// emit(i, slot) for each kept element, slots ascending in element order.
+// Returns the number of kept elements (uniform).
+template <int V, class Emit>
+__device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbits, int budget,
+                                           Emit&& emit)
+{
+    int n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        n_cand += __popcll(__ballot(u[i] != 0u));
+    const int K = min(budget, n_cand);
+
+    uint32_t thr = 0xFFFFFFFFu;
+    int need = 0;
+    if (K > 0) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                cnt += __popcll(__ballot(u[i] >= trial));
+            if (cnt >= K)
+                prefix = trial;
+        }
+        thr = prefix;  // the K-th largest key
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            gt += __popcll(__ballot(u[i] > thr));
+        need = K - gt;  // how many keys equal to thr are kept (lowest ids first)
+    }
+
+    int base = 0, tie_base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool tie = K > 0 && u[i] == thr;
+        const uint64_t tie_mask = __ballot(tie);
+        const bool take = ((fbits >> i) & 1ull) ||
+                          (K > 0 && (u[i] > thr || (tie && tie_base + lanes_below(tie_mask) < need)));
+        const uint64_t take_mask = __ballot(take);
+        if (take)
+            emit(i, base + lanes_below(take_mask));
+        base += __popcll(take_mask);
+        tie_base += __popcll(tie_mask);
+    }
+    return base;
+}
+
+// Compaction buffer of one wave: up to 64 entries (key, raw score, id).
+struct Candidate {
+    uint32_t key;
+    float score;
+    int id;  // bit 30: forced
+};
+constexpr int kForcedFlag = 1 << 30;
+
+// Wave-level select, same contract as wave_select, for V > 1 values per lane.
+// Elements are (u[i], sv[i], id_of(i)). Every key of the best K is >= theta,
+// the K-th largest of the 64 per-lane maxima (at least K keys are >= it), so
+// when the keys >= theta plus the forced elements number at most 64 they are
+// compacted in element order into `buf` (one per lane) and ranked there with
+// one value per lane; otherwise the full V-value search runs.
+template <int V, class IdOf, class Emit>
+__device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], const float (&sv)[V],
+                                                    uint64_t fbits, int budget, int lane,
+                                                    Candidate* buf, IdOf&& id_of, Emit&& emit)
+{
+    int n_cand = 0, n_forced = 0;
+    uint32_t lane_max = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        n_cand += __popcll(__ballot(u[i] != 0u));
+        n_forced += __popcll(__ballot((fbits >> i) & 1ull));
+        lane_max = max(lane_max, u[i]);
+    }
+    const int K = min(budget, n_cand);
+    uint32_t theta = 1u;
+    if (K > 0) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            if (__popcll(__ballot(lane_max >= trial)) >= K)
+                prefix = trial;
+        }
+        theta = max(prefix, 1u);
+    }
+    int n_sel = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        n_sel += __popcll(__ballot(u[i] >= theta));
+    if (K > 0 && n_sel + n_forced > 64)
+        return wave_select<V>(u, fbits, budget, [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
+
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool forced = (fbits >> i) & 1ull;
+        const bool sel = forced || (K > 0 && u[i] >= theta);
+        const uint64_t mask = __ballot(sel);
+        if (sel) {
+            Candidate c;
+            c.key = forced ? 0u : u[i];
+            c.score = sv[i];
+            c.id = id_of(i) | (forced ? kForcedFlag : 0);
+            buf[base + lanes_below(mask)] = c;
+        }
+        base += __popcll(mask);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    Candidate mine = {0u, -INFINITY, -1};
+    if (lane < base)
+        mine = buf[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t u1[1] = {mine.key};
+    const uint64_t f1 = (lane < base && (mine.id & kForcedFlag)) ? 1ull : 0ull;
+    return wave_select<1>(u1, f1, budget,
+                          [&](int, int slot) { emit(mine.score, mine.id & ~kForcedFlag, slot); });
+}
+
+// Picks the search for V values per lane: direct for small V, filtered above.
+template <int V, class IdOf, class Emit>
+__device__ __forceinline__ int select_row(const uint32_t (&u)[V], const float (&sv)[V],
+                                          uint64_t fbits, int budget, int lane, Candidate* buf,
+                                          IdOf&& id_of, Emit&& emit)
+{
+    if (V <= 2)
+        return wave_select<V>(u, fbits, budget,
+                              [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
+    return wave_select_filtered<V>(u, sv, fbits, budget, lane, buf, id_of, emit);
+}
+
+__device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
+{
+    if (lane >= kept && lane < kTop) {
+        row->score[lane] = -INFINITY;
+        row->id[lane] = -1;
+    }
+}
+
+// Second level of a split row: the NW partial rows in LDS are merged by wave
+// 0 into `out`. Forced ids are recomputed from (n, init, local). The
+// candidate budget is `budget`, or 16 - (forced entries found) if budget < 0.
+// Returns the number of forced entries found (uniform in wave 0).
+template <int NW>
+__device__ __forceinline__ int merge_lds_rows(const msa_top16_row* part, int n, int init_blocks,
+                                              int local_blocks, int budget, msa_top16_row* out,
+                                              int lane)
+{
+    static_assert(NW * kTop <= 64, "partial rows must fit one wave");
+    uint32_t u[1] = {0u};
+    uint64_t fbits = 0;
+    float s = -INFINITY;
+    int id = -1;
+    if (lane < NW * kTop) {
+        s = part[lane / kTop].score[lane % kTop];
+        id = part[lane / kTop].id[lane % kTop];
+    }
+    const bool forced = is_forced(id, n, init_blocks, local_blocks);
+    if (forced)
+        fbits = 1;
+    else if (id >= 0)
+        u[0] = order_key(s);
+    const int n_forced = __popcll(__ballot(forced));
+    if (budget < 0)
+        budget = kTop - n_forced;
+    const int kept = wave_select<1>(u, fbits, budget, [&](int, int slot) {
+        out->score[slot] = s;
+        out->id[slot] = id;
+    });
+    pad_row(out, kept, lane);
+    return n_forced;
+}
+
+// |[0, min(init, n)) U [max(0, n - local), n)|
+__device__ __forceinline__ int forced_count(int n, int init_blocks, int local_blocks)
+{
+    if (n <= 0)
+        return 0;
+    const int a = min(init_blocks, n);
+    const int s = max(0, n - local_blocks);
+    return a + (n - s) - max(0, a - s);
+}
+
+// One wave selects over the span [span_lo, span_lo + 64V) of a row of `cols`
+// scores at srow (element i of lane l is span_lo + 64i + l). Valid ids are
+// those below vhi; forced ids follow (n, init, local). The candidate budget is
+// 16 minus the forced ids found in the span. Writes the kept entries and the
+// padding to dst and returns the number kept. All V loads are issued
+// unconditionally (index clamped into the row) so that they overlap; invalid
+// elements are masked afterwards.
+template <int V>
+__device__ __forceinline__ int select_span(const float* srow, int cols, int span_lo, int vhi,
+                                           int n, int init_blocks, int local_blocks,
+                                           msa_top16_row* dst, int lane, Candidate* buf)
+{
+    float sv[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        sv[i] = srow[min(span_lo + i * 64 + lane, cols - 1)];
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    int n_forced = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int id = span_lo + i * 64 + lane;
+        const bool valid = id < vhi;
+        const bool forced = valid && is_forced(id, n, init_blocks, local_blocks);
+        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
+        fbits |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+    const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, lane, buf,
+                                   [&](int i) { return span_lo + i * 64 + lane; },
+                                   [&](float score, int id, int slot) {
+                                       dst->score[slot] = score;
+                                       dst->id[slot] = id;
+                                   });
+    pad_row(dst, kept, lane);
+    return kept;
+}
+
+}  // namespace topk
+}  // namespace msa

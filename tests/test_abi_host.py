@@ -27,7 +27,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("msa_score_decode", "msa_top16_select", "msa_top16_merge",
+    for n in ("msa_score_decode", "msa_score_select", "msa_top16_select", "msa_top16_merge",
               "msa_top16_select_merge", "msa_score_columns", "msa_warmup", "msa_last_error"):
         assert n in names
     assert set(names) == set(msa.EXPORTS)
@@ -183,4 +183,41 @@ def _fused(lib, **kw):
 ])
 def test_select_merge_rejects(lib, kw, needle):
     assert _fused(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _score_select(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seq=FAKE, batch=2,
+             page_size=128, dql=1, out=FAKE, cols=32, nvp=FAKE, init=1, local=2, R=2,
+             rows=FAKE, ws=FAKE, errors=None, stream=None)
+    a.update(kw)
+    return lib.msa_score_select(a["q"], a["k"], a["num_pages"], a["bt"], a["bt_stride"],
+                                a["seq"], a["batch"], a["page_size"], a["dql"], a["out"],
+                                a["cols"], a["nvp"], a["init"], a["local"], a["R"], a["rows"],
+                                a["ws"], a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=None), "null"),
+    (dict(out=FAKE + 8), "aligned"),
+    (dict(page_size=64), "page_size"),
+    (dict(dql=9), "decode_query_len"),
+    (dict(cols=30), "cols"),
+    (dict(batch=0), "batch"),
+    (dict(nvp=None), "null"),
+    (dict(rows=None), "null"),
+    (dict(ws=None), "null"),
+    (dict(ws=FAKE + 2), "aligned"),
+    (dict(R=0), "num_ranges"),
+    (dict(R=33), "num_ranges"),
+    (dict(cols=8192, R=769), "num_ranges"),
+    (dict(cols=8192, R=3), "exceeds 2048"),
+    (dict(init=10, local=7), "exceeds"),
+    (dict(init=-1), ">= 0"),
+])
+def test_score_select_rejects(lib, kw, needle):
+    """Host checks of msa_score_select: the scorer's own checks, then the
+    select arguments, the fused span limit and the workspace pointer; nothing
+    is launched (the pointers are never dereferenced)."""
+    assert _score_select(lib, **kw) == msa.MSA_ERR_INVALID_ARG
     assert needle in lib.msa_last_error().decode()
