@@ -62,6 +62,7 @@ extern "C" {
 #define MSA_MAX_SCORE_COLS 8192  /* score_out: 0 < cols <= 8192, cols % 4 == 0             */
 #define MSA_MAX_SELECT_COLS 12287 /* select scores: 0 < K < 12288                          */
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
+#define MSA_SCORE_SELECT_COUNTER_STRIDE 32 /* int32 per msa_score_select counter (128 B)  */
 
 /*
  * One Top16 row (128 bytes). score[i] is the score-plane value of block
@@ -128,9 +129,10 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
  * num_ranges       R, 1 <= R <= min(cols, 768), with ceil(cols / R) <= 2048. Larger
  *                  spans use the two separate calls.
  * out              device [batch * decode_query_len, 4, R] rows.
- * workspace        device int32 [batch * R], caller-owned. It must hold zeros when the
- *                  call is made, and the launch leaves it holding zeros. Launches that
- *                  share a workspace must not overlap. If `errors` counted a wait
+ * workspace        device int32 [batch * R * MSA_SCORE_SELECT_COUNTER_STRIDE] (one
+ *                  counter per 128-byte line), caller-owned. It must hold zeros when
+ *                  the call is made, and the launch leaves it holding zeros. Launches
+ *                  that share a workspace must not overlap. If `errors` counted a wait
  *                  timeout (below), re-zero the workspace before the next call.
  *
  * score_out receives exactly what msa_score_decode writes, and out exactly what

@@ -31,6 +31,7 @@ NUM_HEADS = 4
 HEAD_DIM = 128
 BLOCK_TOKENS = 128
 TOPK = 16
+COUNTER_STRIDE = 32  # int32 words per msa_score_select workspace counter (128 bytes)
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
 EXPORTS = ("msa_score_decode", "msa_score_select", "msa_top16_select", "msa_top16_merge", "msa_top16_select_merge",
@@ -182,10 +183,11 @@ def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
 
 
 def score_select_workspace(batch: int, num_ranges: int, device="cuda") -> torch.Tensor:
-    """A zeroed int32 workspace [batch * num_ranges] for msa_score_select. The
-    launch leaves it zeroed, so one workspace serves every later call of that
-    size or smaller on the same stream."""
-    return torch.zeros(batch * num_ranges, dtype=torch.int32, device=device)
+    """A zeroed int32 workspace [batch * num_ranges * 32] for msa_score_select
+    (one counter per 128-byte line). The launch leaves it zeroed, so one
+    workspace serves every later call of that size or smaller on the same
+    stream."""
+    return torch.zeros(batch * num_ranges * COUNTER_STRIDE, dtype=torch.int32, device=device)
 
 
 def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
@@ -196,7 +198,7 @@ def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
                      errors: torch.Tensor | None = None, stream=None) -> None:
     """Score plane and per-range Top16 rows in one launch: score_out as
     msa_score_decode writes it, `out` [T, 4, R, 32] as msa_top16_select then
-    writes it. `workspace` is int32 [>= batch * R], zero on entry (see
+    writes it. `workspace` is int32 [>= batch * R * 32], zero on entry (see
     score_select_workspace)."""
     args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
                        decode_query_len)
@@ -208,8 +210,8 @@ def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
     _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
           out.is_contiguous(), f"out: contiguous int32 [{T}, 4, {num_ranges}, 32]")
     _need(workspace.dtype == torch.int32 and workspace.is_contiguous() and
-          workspace.numel() >= B * num_ranges,
-          f"workspace: contiguous int32 with >= {B * num_ranges} elements")
+          workspace.numel() >= B * num_ranges * COUNTER_STRIDE,
+          f"workspace: contiguous int32 with >= {B * num_ranges * COUNTER_STRIDE} elements")
     _check(load().msa_score_select(*args, num_valid_pages.data_ptr(), init_blocks, local_blocks,
                                    num_ranges, out.data_ptr(), workspace.data_ptr(),
                                    _errors_ptr(errors), _stream_handle(stream)))

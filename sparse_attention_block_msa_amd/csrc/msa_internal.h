@@ -75,11 +75,13 @@ struct SelectMergeParams {
 };
 
 // Scorer plus per-range select in one launch (same ranges as SelectParams).
+// One completion counter per (request, range), each on its own 128-byte line.
+constexpr int kCounterStride = MSA_SCORE_SELECT_COUNTER_STRIDE;
 struct ScoreSelectParams {
     ScoreParams score;
     const int32_t* nvp;      // [batch*dql]
     msa_top16_row* out;      // [batch*dql, 4, R]
-    int32_t* counters;       // [batch, R]; zero on entry, zero again on exit
+    int32_t* counters;       // [batch * R * kCounterStride]; zero on entry and on exit
     int32_t init_blocks;
     int32_t local_blocks;
     int32_t num_ranges;

@@ -49,6 +49,8 @@
 // B share gives the same sum.
 #include <math.h>
 
+#include <atomic>
+
 #include "msa_internal.h"
 #include "top16_device.h"
 
@@ -285,7 +287,7 @@ __device__ __forceinline__ WindowPages load_window_pages(const ScoreParams& p, i
 // block maxima collect in res and are stored once, after the window's last
 // block: on this ISA stores share the vector-memory counter with the DMA, so
 // a store issued mid-window would make every later DMA wait also wait for it.
-template <int NT, int kParts>
+template <int NT, int kParts, bool kDeviceScope>
 __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int seq, int nblk,
                                              int c_begin, int c_end, const WindowPages& wp,
                                              const Bf16Slice (&qb)[NT], const int (&pos)[NT],
@@ -341,7 +343,14 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
         const int rho = i / quads;
         const int q4 = i - rho * quads;
         const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
-        *reinterpret_cast<v4f*>(p.out + (row_base + rho) * p.cols + c_begin + q4 * 4) = v;
+        float* dst = p.out + (row_base + rho) * p.cols + c_begin + q4 * 4;
+        if (kDeviceScope) {  // written through to the device's coherence point
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            *reinterpret_cast<v4f*>(dst) = v;
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -355,8 +364,8 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
 // (sequence lengths, Q tile) once rather than per request chunk.
 // segment_done(b, c_begin, c_end) runs after the wave has issued the plane
 // stores of columns [c_begin, c_end) of request b, once per request it
-// touches.
-template <int NT, int kParts, class SegmentDone>
+// touches. With kDeviceScope the plane stores are agent-scope atomic stores.
+template <int NT, int kParts, bool kDeviceScope, class SegmentDone>
 __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* tile,
                                                  float (*res)[kChunk], SegmentDone&& segment_done)
 {
@@ -449,7 +458,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
             qb[n] = to_bf16(qraw[n]);
         }
         while (true) {
-            score_window<NT, kParts>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
+            score_window<NT, kParts, kDeviceScope>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
                                      g);
             c = c_end;
             if (c >= c_stop)
@@ -470,13 +479,14 @@ void score_decode_kernel(ScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
-    score_wave_range<NT, kParts>(p, tile, res, [](int, int, int) {});
+    score_wave_range<NT, kParts, false>(p, tile, res, [](int, int, int) {});
 }
 
 // Waits until the produced-column count in the low 16 bits of *ctr reaches
-// `expected`, for at most spin_ticks of the device's constant-rate clock, then
-// acquires (agent scope) what the producers released. Returns false on
-// timeout.
+// `expected`, for at most spin_ticks of the device's constant-rate clock.
+// Returns false on timeout. The plane values it waits for are read afterwards
+// with agent-scope atomic loads, so no cache invalidation is needed; the
+// workgroup-scope fence keeps those loads after the wait.
 __device__ __forceinline__ bool wait_for_columns(const int32_t* ctr, int expected,
                                                  int64_t spin_ticks)
 {
@@ -488,26 +498,37 @@ __device__ __forceinline__ bool wait_for_columns(const int32_t* ctr, int expecte
             ok = false;
             break;
         }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return ok;
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for every outstanding
+// vector-memory operation of the wave, stores included: vmcnt(0), with
+// expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Score plane and per-range Top16 rows in one launch. Every wave first scores
-// its columns exactly as score_decode_kernel does. After each request segment
-// it releases its plane stores (agent scope) and adds the segment's column
-// count, per column range, to counters[b * R + r]. It then runs select jobs
-// j = blockIdx.x, blockIdx.x + gridDim.x, ... over the (token, head, range)
-// rows, in the row order of the select kernel. A job waits until every column
-// of its range that this launch writes has been counted, then selects exactly
-// as the select kernel does, and adds 1 << 16 to the counter as a consumer
-// mark. The last of the range's 4*dql consumers resets the counter to zero,
-// so the counters are zero again when the launch ends. The wait is only for
-// scoring work, which waits on nothing, and the host keeps the grid within
-// the waves the device holds at once, so every wait ends; the clock limit
-// counts an error instead of spinning on if that fails, and a wave that has
-// timed out once counts its later unfinished waits without waiting.
+// its columns as score_decode_kernel does, but stores the plane with
+// agent-scope atomic stores (written through to the device's coherence
+// point). After each request segment it waits for those stores to complete
+// and adds the segment's column count, per column range, to the range's
+// counter (one per 128-byte line: counters sharing a line made the polling
+// below throttle the whole launch). It then runs select jobs j = blockIdx.x,
+// blockIdx.x + gridDim.x, ... over the (token, head, range) rows, in the row
+// order of the select kernel. A job waits until every column of its range
+// that this launch writes has been counted, reads the row with agent-scope
+// atomic loads and selects exactly as the select kernel does, then adds
+// 1 << 16 to the counter as a consumer mark. The last of the range's 4*dql
+// consumers resets the counter to zero, so the counters are zero again when
+// the launch ends. The protocol is the agent-scope release/acquire pair
+// without its whole-cache write-back and invalidation, which only non-atomic
+// accesses need (with them, the launch took three times as long). The wait is
+// only for scoring work, which waits on nothing, and the host keeps the grid
+// within the waves the device holds at once, so every wait ends; the clock
+// limit counts an error instead of spinning on if that fails, and a wave that
+// has timed out once counts its later unfinished waits without waiting.
 template <int NT, int kParts, int kWavesPerEU, int V>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_select_kernel(ScoreSelectParams q)
@@ -520,12 +541,12 @@ void score_select_kernel(ScoreSelectParams q)
     const int R = q.num_ranges;
     const int w = q.width;
 
-    score_wave_range<NT, kParts>(p, tile, res, [&](int b, int c_begin, int c_end) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    score_wave_range<NT, kParts, true>(p, tile, res, [&](int b, int c_begin, int c_end) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (lane == 0) {
             for (int r = c_begin / w; r * w < c_end; ++r) {
                 const int n = min(c_end, (r + 1) * w) - max(c_begin, r * w);
-                atomicAdd(q.counters + (int64_t)b * R + r, n);
+                atomicAdd(q.counters + ((int64_t)b * R + r) * kCounterStride, n);
             }
         }
     });
@@ -549,13 +570,13 @@ void score_select_kernel(ScoreSelectParams q)
         bool clamped;
         const int wb = written_cols(p.seq_lens[b], p.cols, clamped);
         const int expected = max(0, min(hi, wb) - lo);
-        int32_t* ctr = q.counters + (int64_t)b * R + r;
+        int32_t* ctr = q.counters + ((int64_t)b * R + r) * kCounterStride;
         if (expected > 0 && !(patient && wait_for_columns(ctr, expected, q.spin_ticks))) {
             patient = false;
             if (lane == 0 && p.errors)
                 atomicAdd(p.errors, 1);
         }
-        topk::select_span<V>(p.out + th * p.cols, p.cols, lo, min(hi, n), n, q.init_blocks,
+        topk::select_span<V, true>(p.out + th * p.cols, p.cols, lo, min(hi, n), n, q.init_blocks,
                              q.local_blocks, q.out + job, lane, cand);
         if (lane == 0) {
             const int old = atomicAdd(ctr, 1 << 16);
@@ -648,25 +669,44 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
 // Values per lane of the fused kernel's select: spans up to 256, 1024 and
 // 2048 columns.
 #define MSA_FOR_EACH_SCORE_SELECT(X) X(1, 4) X(1, 16) X(1, 32) X(2, 4) X(2, 16) X(2, 32)
+constexpr int kScoreSelectInstances = 6;
+
+// Workgroups (one wave each) of instance `which` that one CU holds at once,
+// queried once per device: the query costs far more host time than a launch.
+int resident_per_cu(const void* fn, int which)
+{
+    static std::atomic<int> cached[64][kScoreSelectInstances];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int per_cu = cached[dev][which].load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess)
+            return 0;
+        cached[dev][which].store(per_cu, std::memory_order_relaxed);
+    }
+    return per_cu;
+}
 
 hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
 {
     const int nt = q.score.dql * kHeads <= 16 ? 1 : 2;
     const int v = q.width <= 256 ? 4 : q.width <= 1024 ? 16 : q.width <= kMaxFusedWidth ? 32 : 0;
     const void* fn = nullptr;
+    int which = 0, index = 0;
 #define X(NT, V)                                \
-    if (nt == NT && v == V)                     \
-        fn = score_select_kernel_fn<NT, V>();
+    if (nt == NT && v == V) {                   \
+        fn = score_select_kernel_fn<NT, V>();   \
+        which = index;                          \
+    }                                           \
+    ++index;
     MSA_FOR_EACH_SCORE_SELECT(X)
 #undef X
     if (fn == nullptr)
         return hipErrorInvalidValue;
     // Every wave must be resident at once (select jobs wait on other waves'
     // scoring), so the grid is capped at what the device holds.
-    int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
-    if (e != hipSuccess)
-        return e;
+    const int per_cu = resident_per_cu(fn, which);
     if (per_cu <= 0)
         return hipErrorInvalidConfiguration;
     int64_t grid = score_grid(q.score);

@@ -240,16 +240,23 @@ __device__ __forceinline__ int forced_count(int n, int init_blocks, int local_bl
 // 16 minus the forced ids found in the span. Writes the kept entries and the
 // padding to dst and returns the number kept. All V loads are issued
 // unconditionally (index clamped into the row) so that they overlap; invalid
-// elements are masked afterwards.
-template <int V>
+// elements are masked afterwards. With kDeviceScope the loads are agent-scope
+// atomic loads, which read values other waves stored at agent scope without
+// a cache invalidation.
+template <int V, bool kDeviceScope = false>
 __device__ __forceinline__ int select_span(const float* srow, int cols, int span_lo, int vhi,
                                            int n, int init_blocks, int local_blocks,
                                            msa_top16_row* dst, int lane, Candidate* buf)
 {
     float sv[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-        sv[i] = srow[min(span_lo + i * 64 + lane, cols - 1)];
+    for (int i = 0; i < V; ++i) {
+        const float* src = srow + min(span_lo + i * 64 + lane, cols - 1);
+        if (kDeviceScope)
+            sv[i] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            sv[i] = *src;
+    }
     uint32_t u[V];
     uint64_t fbits = 0;
     int n_forced = 0;

@@ -48,7 +48,7 @@ def say(*a):
 def workspace():
     """One workspace shared by every test here: each launch must leave it zero."""
     if "ws" not in _WS:
-        _WS["ws"] = msa.score_select_workspace(1 << 16, 1, device=DEV)
+        _WS["ws"] = msa.score_select_workspace(1 << 12, 1, device=DEV)  # 4096 counters
     return _WS["ws"]
 
 
@@ -79,7 +79,7 @@ def run_both(w, *, R=None, cols=None, nvp=None, block_table=None, canary=CANARY_
     ref_err = int(err2.item())
 
     ws = workspace()
-    assert ws.numel() >= B * R
+    assert ws.numel() >= B * R * msa.COUNTER_STRIDE
     for rep in range(repeat):
         plane1 = torch.full((T, 4, cols), int(np.int32(np.uint32(canary))), dtype=torch.int32,
                             device=DEV).view(torch.float32)
