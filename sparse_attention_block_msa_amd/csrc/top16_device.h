@@ -234,21 +234,17 @@ __device__ __forceinline__ int forced_count(int n, int init_blocks, int local_bl
     return a + (n - s) - max(0, a - s);
 }
 
-// One wave selects over the span [span_lo, span_lo + 64V) of a row of `cols`
-// scores at srow (element i of lane l is span_lo + 64i + l). Valid ids are
-// those below vhi; forced ids follow (n, init, local). The candidate budget is
-// 16 minus the forced ids found in the span. Writes the kept entries and the
-// padding to dst and returns the number kept. All V loads are issued
-// unconditionally (index clamped into the row) so that they overlap; invalid
-// elements are masked afterwards. With kDeviceScope the loads are agent-scope
-// atomic loads, which read values other waves stored at agent scope without
-// a cache invalidation.
+// Loads the span [span_lo, span_lo + 64V) of a row of `cols` scores at srow
+// into sv (element i of lane l is span_lo + 64i + l). All V loads are issued
+// unconditionally (index clamped into the row) so that they overlap; callers
+// issue them before anything else that waits on memory, and invalid elements
+// are masked by select_loaded. With kDeviceScope the loads are agent-scope
+// atomic loads, which read values other waves stored at agent scope without a
+// cache invalidation.
 template <int V, bool kDeviceScope = false>
-__device__ __forceinline__ int select_span(const float* srow, int cols, int span_lo, int vhi,
-                                           int n, int init_blocks, int local_blocks,
-                                           msa_top16_row* dst, int lane, Candidate* buf)
+__device__ __forceinline__ void load_span(const float* srow, int cols, int span_lo, int lane,
+                                          float (&sv)[V])
 {
-    float sv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const float* src = srow + min(span_lo + i * 64 + lane, cols - 1);
@@ -257,6 +253,17 @@ __device__ __forceinline__ int select_span(const float* srow, int cols, int span
         else
             sv[i] = *src;
     }
+}
+
+// Selects over a span loaded by load_span. Valid ids are those below vhi;
+// forced ids follow (n, init, local). The candidate budget is 16 minus the
+// forced ids found in the span. Writes the kept entries and the padding to
+// dst and returns the number kept.
+template <int V>
+__device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, int vhi, int n,
+                                             int init_blocks, int local_blocks,
+                                             msa_top16_row* dst, int lane, Candidate* buf)
+{
     uint32_t u[V];
     uint64_t fbits = 0;
     int n_forced = 0;
