@@ -77,6 +77,9 @@ namespace {
 #ifndef MSA_SCORE_WAVES_PER_SIMD_32
 #define MSA_SCORE_WAVES_PER_SIMD_32 2  // grid: waves per SIMD for 17..32 query rows
 #endif
+#ifndef MSA_SCORE_LATENCY_WAVES_PER_SIMD
+#define MSA_SCORE_LATENCY_WAVES_PER_SIMD 2  // small batches: batch*cols <= CUs*4*this
+#endif
 #ifndef MSA_SCORE_REG_WAVES_16
 #define MSA_SCORE_REG_WAVES_16 MSA_SCORE_WAVES_PER_SIMD_16  // register cap: waves per SIMD
 #endif
@@ -282,12 +285,13 @@ __device__ __forceinline__ WindowPages load_window_pages(const ScoreParams& p, i
     return w;
 }
 
-// Scores one window: columns [c_begin, c_end) of request b (at most kChunk,
-// multiples of 4, c_begin < nblk), whose block-table entries are in wp. The
+// Scores one window: columns [c_begin, c_end) of request b (at most kChunk;
+// multiples of kUnit = 4, or any columns for kUnit = 1), whose block-table
+// entries are in wp. Columns at or past nblk are padding (-inf). The
 // block maxima collect in res and are stored once, after the window's last
 // block: on this ISA stores share the vector-memory counter with the DMA, so
 // a store issued mid-window would make every later DMA wait also wait for it.
-template <int NT, int kParts, bool kDeviceScope>
+template <int NT, int kParts, bool kDeviceScope, int kUnit>
 __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int seq, int nblk,
                                              int c_begin, int c_end, const WindowPages& wp,
                                              const Bf16Slice (&qb)[NT], const int (&pos)[NT],
@@ -297,7 +301,7 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
     const int rows = p.dql * kHeads;
     const int64_t row_base = (int64_t)b * rows;
     const int ps_shift = p.page_size == 256 ? 1 : 0;  // log2(B128 blocks per page)
-    const int c_last = min(c_end, nblk) - 1;           // >= c_begin
+    const int c_last = min(c_end, nblk) - 1;  // < c_begin if the window is all padding
     const int pg_begin = c_begin >> ps_shift;
     const int my_page = wp.page;
     const uint64_t bad_mask = wp.bad_mask;
@@ -338,7 +342,15 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int quads = (c_end - c_begin) / 4;  // float4 groups per row
+    if (kUnit == 1) {  // single-column stores: windows need not be 4-aligned
+        const int ncol = c_end - c_begin;
+        for (int i = lane; i < rows * ncol; i += 64) {
+            const int rho = i / ncol;
+            const int c = i - rho * ncol;
+            p.out[(row_base + rho) * p.cols + c_begin + c] = res[rho][c];
+        }
+    }
+    const int quads = kUnit == 4 ? (c_end - c_begin) / 4 : 0;  // float4 groups per row
     for (int i = lane; i < rows * quads; i += 64) {
         const int rho = i / quads;
         const int q4 = i - rho * quads;
@@ -359,13 +371,14 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
 
 // Work split: the plane columns every request writes (a multiple of 4 each)
 // are laid end to end and cut into gridDim.x equal, contiguous ranges of
-// 4-column groups, one per wave; a range may run across request boundaries.
+// kUnit-column units (4, or 1 for small batches), one per wave; a range may
+// run across request boundaries.
 // Ragged batches therefore load every wave alike, and a wave pays its setup
 // (sequence lengths, Q tile) once rather than per request chunk.
 // segment_done(b, c_begin, c_end) runs after the wave has issued the plane
 // stores of columns [c_begin, c_end) of request b, once per request it
 // touches. With kDeviceScope the plane stores are agent-scope atomic stores.
-template <int NT, int kParts, bool kDeviceScope, class SegmentDone>
+template <int NT, int kParts, bool kDeviceScope, int kUnit, class SegmentDone>
 __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* tile,
                                                  float (*res)[kChunk], SegmentDone&& segment_done)
 {
@@ -382,7 +395,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     int64_t base = 0;
     if (p.batch <= 64) {
         bool clamped;
-        const int gb = lane < p.batch ? written_cols(p.seq_lens[lane], p.cols, clamped) / 4 : 0;
+        const int gb = lane < p.batch ? written_cols(p.seq_lens[lane], p.cols, clamped) / kUnit : 0;
         const int incl = wave_inclusive_scan(gb, lane);
         const int64_t total = __shfl(incl, 63);
         g_lo = total * (int64_t)blockIdx.x / gridDim.x;
@@ -397,7 +410,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
             bool clamped;
             const int bb = b0 + lane;
-            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / 4 : 0;
+            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / kUnit : 0;
             total += wave_sum(gb);
         }
         g_lo = total * (int64_t)blockIdx.x / gridDim.x;
@@ -407,7 +420,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
             bool clamped;
             const int bb = b0 + lane;
-            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / 4 : 0;
+            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / kUnit : 0;
             const int incl = wave_inclusive_scan(gb, lane);
             const int chunk_total = __shfl(incl, 63);
             if (base + chunk_total > g_lo) {
@@ -433,9 +446,9 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
             atomicAdd(p.errors, 1);
         const int nblk = (int)(((int64_t)seq + kBlockTokens - 1) / kBlockTokens);
         const int64_t row_base = (int64_t)b * rows;
-        const int64_t g_end_b = base + wcols / 4;
-        const int c_stop = (int)((min(g_hi, g_end_b) - base) * 4);
-        const int c_first = (int)((gcur - base) * 4);
+        const int64_t g_end_b = base + wcols / kUnit;
+        const int c_stop = (int)((min(g_hi, g_end_b) - base) * kUnit);
+        const int c_first = (int)((gcur - base) * kUnit);
         int c = c_first;
 
         // Q tile loads and the first window's block-table loads go out
@@ -458,7 +471,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
             qb[n] = to_bf16(qraw[n]);
         }
         while (true) {
-            score_window<NT, kParts, kDeviceScope>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
+            score_window<NT, kParts, kDeviceScope, kUnit>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
                                      g);
             c = c_end;
             if (c >= c_stop)
@@ -473,13 +486,13 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     }
 }
 
-template <int NT, int kParts, int kWavesPerEU>
+template <int NT, int kParts, int kWavesPerEU, int kUnit>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_decode_kernel(ScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
-    score_wave_range<NT, kParts, false>(p, tile, res, [](int, int, int) {});
+    score_wave_range<NT, kParts, false, kUnit>(p, tile, res, [](int, int, int) {});
 }
 
 // Waits until the produced-column count in the low 16 bits of *ctr reaches
@@ -541,7 +554,7 @@ void score_select_kernel(ScoreSelectParams q)
     const int R = q.num_ranges;
     const int w = q.width;
 
-    score_wave_range<NT, kParts, true>(p, tile, res, [&](int b, int c_begin, int c_end) {
+    score_wave_range<NT, kParts, true, 4>(p, tile, res, [&](int b, int c_begin, int c_end) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (lane == 0) {
             for (int r = c_begin / w; r * w < c_end; ++r) {
@@ -606,7 +619,17 @@ template <int NT>
 const void* score_kernel_fn()
 {
     constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
-    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves>);
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4>);
+}
+
+// Small batches: one column per work unit and a whole block per DMA round
+// trip (16 KiB LDS tile), so that every block gets its own wave and pays one
+// memory latency instead of four.
+template <int NT>
+const void* score_latency_kernel_fn()
+{
+    return reinterpret_cast<const void*>(
+        &score_decode_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, 1>);
 }
 
 template <int NT, int V>
@@ -664,7 +687,14 @@ int64_t score_grid(const ScoreParams& p)
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
 {
     void* args[] = {const_cast<ScoreParams*>(&p)};
-    const void* fn = p.dql * kHeads <= 16 ? score_kernel_fn<1>() : score_kernel_fn<2>();
+    const bool small_q = p.dql * kHeads <= 16;
+    const int64_t max_cols = (int64_t)p.batch * p.cols;
+    const int64_t latency_waves = (int64_t)device_cus() * 4 * MSA_SCORE_LATENCY_WAVES_PER_SIMD;
+    if (max_cols <= latency_waves) {
+        const void* fn = small_q ? score_latency_kernel_fn<1>() : score_latency_kernel_fn<2>();
+        return hipLaunchKernel(fn, dim3((unsigned)max_cols), dim3(64), args, 0, stream);
+    }
+    const void* fn = small_q ? score_kernel_fn<1>() : score_kernel_fn<2>();
     return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
 }
 
@@ -727,6 +757,10 @@ hipError_t warmup_score_kernels()
     hipError_t e = hipFuncGetAttributes(&attr, score_kernel_fn<1>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_kernel_fn<2>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<1>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<2>());
 #define X(NT, V)          \
     if (e == hipSuccess)  \
         e = hipFuncGetAttributes(&attr, score_select_kernel_fn<NT, V>());
