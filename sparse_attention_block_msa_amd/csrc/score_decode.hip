@@ -342,7 +342,8 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (kUnit == 1) {  // single-column stores: windows need not be 4-aligned
+    static_assert(kUnit == 4 || (kUnit == 1 && !kDeviceScope), "unsupported store mode");
+    if constexpr (kUnit == 1) {  // single-column stores: windows need not be 4-aligned
         const int ncol = c_end - c_begin;
         for (int i = lane; i < rows * ncol; i += 64) {
             const int rho = i / ncol;
@@ -350,18 +351,20 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
             p.out[(row_base + rho) * p.cols + c_begin + c] = res[rho][c];
         }
     }
-    const int quads = kUnit == 4 ? (c_end - c_begin) / 4 : 0;  // float4 groups per row
-    for (int i = lane; i < rows * quads; i += 64) {
-        const int rho = i / quads;
-        const int q4 = i - rho * quads;
-        const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
-        float* dst = p.out + (row_base + rho) * p.cols + c_begin + q4 * 4;
-        if (kDeviceScope) {  // written through to the device's coherence point
+    if constexpr (kUnit == 4) {
+        const int quads = (c_end - c_begin) / 4;  // float4 groups per row
+        for (int i = lane; i < rows * quads; i += 64) {
+            const int rho = i / quads;
+            const int q4 = i - rho * quads;
+            const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
+            float* dst = p.out + (row_base + rho) * p.cols + c_begin + q4 * 4;
+            if (kDeviceScope) {  // written through to the device's coherence point
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            *reinterpret_cast<v4f*>(dst) = v;
+                for (int e = 0; e < 4; ++e)
+                    __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                *reinterpret_cast<v4f*>(dst) = v;
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

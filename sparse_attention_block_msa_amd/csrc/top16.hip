@@ -110,7 +110,7 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
     const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
     msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
     const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
-    const int kept = select_row<V>(u, sv, fbits, budget, lane, cand[wave],
+    const int kept = select_row<V>(u, sv, fbits, budget, count_keys<V>(u), lane, cand[wave],
                                    [&](int i) { return iv[i]; },
                                    [&](float score, int id, int slot) {
                                        dst->score[slot] = score;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
     }
     msa_top16_row* dst = p.out + th;
     const int kept_m = select_row<VM>(um, mv, fm, kTop - forced_count(n, p.init_blocks, p.local_blocks),
-                                      lane, cand[0], [&](int i) { return iv[i]; },
+                                      count_keys<VM>(um), lane, cand[0], [&](int i) { return iv[i]; },
                                       [&](float score, int id, int slot) {
                                           dst->score[slot] = score;
                                           dst->id[slot] = id;

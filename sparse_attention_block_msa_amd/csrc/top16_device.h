@@ -43,19 +43,27 @@ __device__ __forceinline__ int is_forced(int id, int n, int init_blocks, int loc
     return id >= 0 && id < n && (id < init_blocks || id >= n - local_blocks);
 }
 
-// Wave-level select. Element i of this lane has key u[i] (0 = not a
-// candidate) and is forced if bit i of fbits is set. Keeps all forced
-// elements and the best min(budget, #candidates) candidates, and calls
-// emit(i, slot) for each kept element, slots ascending in element order.
-// Returns the number of kept elements (uniform).
-template <int V, class Emit>
-__device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbits, int budget,
-                                           Emit&& emit)
+// Number of candidate keys (u != 0) in the wave.
+template <int V>
+__device__ __forceinline__ int count_keys(const uint32_t (&u)[V])
 {
-    int n_cand = 0;
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i)
-        n_cand += __popcll(__ballot(u[i] != 0u));
+        n += __popcll(__ballot(u[i] != 0u));
+    return n;
+}
+
+// Wave-level select. Element i of this lane has key u[i] (0 = not a
+// candidate) and is forced if bit i of fbits is set; n_cand is the number of
+// candidates (count_keys). Keeps all forced elements and the best
+// min(budget, n_cand) candidates, and calls emit(i, slot) for each kept
+// element, slots ascending in element order. Returns the number of kept
+// elements (uniform).
+template <int V, class Emit>
+__device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbits, int budget,
+                                           int n_cand, Emit&& emit)
+{
     const int K = min(budget, n_cand);
 
     uint32_t thr = 0xFFFFFFFFu;
@@ -108,20 +116,18 @@ constexpr int kForcedFlag = 1 << 30;
 // the K-th largest of the 64 per-lane maxima (at least K keys are >= it), so
 // when the keys >= theta plus the forced elements number at most 64 they are
 // compacted in element order into `buf` (one per lane) and ranked there with
-// one value per lane; otherwise the full V-value search runs.
+// one value per lane; otherwise (the compaction counts them as it goes and
+// stops writing past 64) the full V-value search runs.
 template <int V, class IdOf, class Emit>
 __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], const float (&sv)[V],
-                                                    uint64_t fbits, int budget, int lane,
-                                                    Candidate* buf, IdOf&& id_of, Emit&& emit)
+                                                    uint64_t fbits, int budget, int n_cand,
+                                                    int lane, Candidate* buf, IdOf&& id_of,
+                                                    Emit&& emit)
 {
-    int n_cand = 0, n_forced = 0;
     uint32_t lane_max = 0;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        n_cand += __popcll(__ballot(u[i] != 0u));
-        n_forced += __popcll(__ballot((fbits >> i) & 1ull));
+    for (int i = 0; i < V; ++i)
         lane_max = max(lane_max, u[i]);
-    }
     const int K = min(budget, n_cand);
     uint32_t theta = 1u;
     if (K > 0) {
@@ -133,28 +139,25 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
         }
         theta = max(prefix, 1u);
     }
-    int n_sel = 0;
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-        n_sel += __popcll(__ballot(u[i] >= theta));
-    if (K > 0 && n_sel + n_forced > 64)
-        return wave_select<V>(u, fbits, budget, [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
-
     int base = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const bool forced = (fbits >> i) & 1ull;
         const bool sel = forced || (K > 0 && u[i] >= theta);
         const uint64_t mask = __ballot(sel);
-        if (sel) {
+        const int slot = base + lanes_below(mask);
+        if (sel && slot < 64) {
             Candidate c;
             c.key = forced ? 0u : u[i];
             c.score = sv[i];
             c.id = id_of(i) | (forced ? kForcedFlag : 0);
-            buf[base + lanes_below(mask)] = c;
+            buf[slot] = c;
         }
         base += __popcll(mask);
     }
+    if (base > 64)  // heavy ties at theta: rank all V values per lane instead
+        return wave_select<V>(u, fbits, budget, n_cand,
+                              [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -166,20 +169,21 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t u1[1] = {mine.key};
     const uint64_t f1 = (lane < base && (mine.id & kForcedFlag)) ? 1ull : 0ull;
-    return wave_select<1>(u1, f1, budget,
+    return wave_select<1>(u1, f1, budget, n_cand,
                           [&](int, int slot) { emit(mine.score, mine.id & ~kForcedFlag, slot); });
 }
 
 // Picks the search for V values per lane: direct for small V, filtered above.
+// n_cand is the number of candidate keys (u != 0).
 template <int V, class IdOf, class Emit>
 __device__ __forceinline__ int select_row(const uint32_t (&u)[V], const float (&sv)[V],
-                                          uint64_t fbits, int budget, int lane, Candidate* buf,
-                                          IdOf&& id_of, Emit&& emit)
+                                          uint64_t fbits, int budget, int n_cand, int lane,
+                                          Candidate* buf, IdOf&& id_of, Emit&& emit)
 {
     if (V <= 2)
-        return wave_select<V>(u, fbits, budget,
+        return wave_select<V>(u, fbits, budget, n_cand,
                               [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
-    return wave_select_filtered<V>(u, sv, fbits, budget, lane, buf, id_of, emit);
+    return wave_select_filtered<V>(u, sv, fbits, budget, n_cand, lane, buf, id_of, emit);
 }
 
 __device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
@@ -216,7 +220,7 @@ __device__ __forceinline__ int merge_lds_rows(const msa_top16_row* part, int n, 
     const int n_forced = __popcll(__ballot(forced));
     if (budget < 0)
         budget = kTop - n_forced;
-    const int kept = wave_select<1>(u, fbits, budget, [&](int, int slot) {
+    const int kept = wave_select<1>(u, fbits, budget, count_keys<1>(u), [&](int, int slot) {
         out->score[slot] = s;
         out->id[slot] = id;
     });
@@ -264,19 +268,34 @@ __device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, 
                                              int init_blocks, int local_blocks,
                                              msa_top16_row* dst, int lane, Candidate* buf)
 {
+    // Valid ids of the span: [span_lo, valid_hi) (vhi <= n). Forced ids are
+    // those of [0, init) and [n - local, n) within [0, n); both counts are
+    // interval arithmetic, so no ballots are spent on them.
+    const int valid_hi = min(vhi, span_lo + V * 64);
+    const int n_valid = max(0, valid_hi - span_lo);
+    const int init_end = min(init_blocks, n);
+    const int local_begin = max(0, n - local_blocks);
+    const int n_init = max(0, min(valid_hi, init_end) - span_lo);
+    const int n_local = max(0, valid_hi - max(span_lo, local_begin));
+    const int n_both = max(0, min(valid_hi, init_end) - max(span_lo, local_begin));
+    const int n_forced = n_init + n_local - n_both;
     uint32_t u[V];
     uint64_t fbits = 0;
-    int n_forced = 0;
+    if (n_forced == 0) {  // the usual case away from a row's ends
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const int id = span_lo + i * 64 + lane;
-        const bool valid = id < vhi;
-        const bool forced = valid && is_forced(id, n, init_blocks, local_blocks);
-        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
-        fbits |= (uint64_t)forced << i;
-        n_forced += __popcll(__ballot(forced));
+        for (int i = 0; i < V; ++i)
+            u[i] = span_lo + i * 64 + lane < valid_hi ? order_key(sv[i]) : 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int id = span_lo + i * 64 + lane;
+            const bool valid = id < valid_hi;
+            const bool forced = valid && is_forced(id, n, init_blocks, local_blocks);
+            u[i] = valid && !forced ? order_key(sv[i]) : 0u;
+            fbits |= (uint64_t)forced << i;
+        }
     }
-    const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, lane, buf,
+    const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, n_valid - n_forced, lane, buf,
                                    [&](int i) { return span_lo + i * 64 + lane; },
                                    [&](float score, int id, int slot) {
                                        dst->score[slot] = score;
