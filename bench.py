@@ -6,9 +6,11 @@ plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
 
     msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
 
-The same step with select and merge in one launch
-(msa_top16_select_merge, per-range rows also written) is timed beside it
-and reported under e2e.fused_select_merge.
+Two fused variants of the step are timed beside it: select and merge in one
+launch (msa_top16_select_merge, per-range rows also written;
+e2e.fused_select_merge), and the plane with the per-range rows in one launch
+followed by the merge (msa_score_select -> msa_top16_merge;
+e2e.score_select_then_merge).
 
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
 timing. Before every step a read pass over a 1 GiB buffer evicts index-K
@@ -198,6 +200,35 @@ def main():
         torch.cuda.synchronize()
         fused_ms = sum(ev[0].elapsed_time(ev[1]) for ev in fused_events) / args.steps
 
+    # Timed region 1c: the same K steps with the plane and the range rows from
+    # one launch (msa_score_select), then msa_top16_merge; reported beside the
+    # headline.
+    ws = msa.score_select_workspace(w.batch, R, device=dev)
+
+    def step_score_select():
+        msa.msa_score_select(q, k, bt, sl, plane, nvp, part, ws, page_size=w.page_size,
+                             decode_query_len=w.dql, init_blocks=w.init_blocks,
+                             local_blocks=w.local_blocks, num_ranges=R, errors=errors,
+                             stream=stream)
+        if R > 1:
+            msa.msa_top16_merge(part, nvp, final, init_blocks=w.init_blocks,
+                                local_blocks=w.local_blocks, errors=errors, stream=stream)
+
+    score_select_ms = None
+    if -(-w.cols // R) <= 2048:
+        for _ in range(args.warmup):
+            step_score_select()
+        ss_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                     for _ in range(args.steps)]
+        for i in range(args.steps):
+            if not args.no_flush:
+                flush.sum()
+            ss_events[i][0].record(stream)
+            step_score_select()
+            ss_events[i][1].record(stream)
+        torch.cuda.synchronize()
+        score_select_ms = sum(ev[0].elapsed_time(ev[1]) for ev in ss_events) / args.steps
+
     # Timed region 2: the same K steps with an event between every kernel,
     # for per-kernel durations (the events themselves lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -258,6 +289,12 @@ def main():
                     "ms_per_step": fused_ms, "keys_per_s": keys / (fused_ms * 1e-3),
                     "hbm_gbps": launch_bytes / (fused_ms * 1e-3) / 1e9,
                     "frac_of_peak": launch_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "score_select_then_merge": None if score_select_ms is None else {
+                    "ms_per_step": score_select_ms,
+                    "keys_per_s": keys / (score_select_ms * 1e-3),
+                    "hbm_gbps": launch_bytes / (score_select_ms * 1e-3) / 1e9,
+                    "frac_of_peak":
+                        launch_bytes / (score_select_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                 "wall_s_all_steps_incl_flush": wall},
         "roofline": {"kernel": "score_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
