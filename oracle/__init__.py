@@ -55,6 +55,13 @@ class Oracle:
         lib.oracle_top16_select.restype = i64
         lib.oracle_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P]
         lib.oracle_top16_merge.restype = i64
+        lib.oracle_written_columns_sharded.argtypes = [i64, i32]
+        lib.oracle_written_columns_sharded.restype = i64
+        lib.oracle_score_decode_sharded.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32,
+                                                    i32, P, i32, P]
+        lib.oracle_score_decode_sharded.restype = i64
+        lib.oracle_top16_select_mapped.argtypes = [P, i32, i32, P, i32, i32, i32, i32, i32, P]
+        lib.oracle_top16_select_mapped.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -126,6 +133,56 @@ class Oracle:
             _ptr(q), _ptr(k), k.shape[0], _ptr(bt), bt.shape[1], _ptr(sl), page_size,
             decode_query_len, _ptr(r), _ptr(c), n, _ptr(s), _ptr(a))
         return s, a, int(bad)
+
+    def written_columns_sharded(self, seq_len: int, page_size: int) -> int:
+        return int(self.lib.oracle_written_columns_sharded(int(seq_len), int(page_size)))
+
+    def score_decode_sharded(self, index_q, index_k_shard, block_table, seq_lens, *,
+                             page_size: int, decode_query_len: int, rank: int, world_size: int,
+                             cols: int, plane: np.ndarray | None = None,
+                             want_amax: bool = False):
+        """Rank `rank`'s plane [T, 4, cols] of a cache whose pages are split
+        by rows over world_size ranks (index_k_shard [pages, page_size /
+        world_size, 128]). Returns (plane, amax|None, bad)."""
+        q = _c(index_q, np.uint8)
+        k = _c(index_k_shard, np.uint8)
+        bt = _c(block_table, np.int32)
+        sl = _c(seq_lens, np.int32)
+        batch = sl.shape[0]
+        T = batch * decode_query_len
+        assert q.size == T * HEADS * DIM
+        assert k.ndim == 3 and k.shape[1] * world_size == page_size and k.shape[2] == DIM
+        if plane is None:
+            plane = np.full((T, HEADS, cols), np.nan, dtype=np.float32)
+        else:
+            plane = np.array(plane, dtype=np.float32, order="C", copy=True)
+        amax = np.zeros((T, HEADS, cols), dtype=np.float64) if want_amax else None
+        bad = self.lib.oracle_score_decode_sharded(
+            _ptr(q), _ptr(k), k.shape[0], _ptr(bt), bt.shape[1], _ptr(sl), batch, page_size,
+            decode_query_len, rank, world_size, _ptr(plane), cols,
+            _ptr(amax) if want_amax else None)
+        if bad < 0:
+            raise ValueError("oracle_score_decode_sharded: invalid arguments")
+        return plane, amax, int(bad)
+
+    def top16_select_mapped(self, scores, num_valid_pages, *, init_blocks: int,
+                            local_blocks: int, num_ranges: int = 1, index_scale: int = 1,
+                            index_offset: int = 0):
+        """Top16 rows with plane column c standing for global id
+        index_scale * c + index_offset. Returns (scores, ids, bad) as
+        top16_select."""
+        s = _c(scores, np.float32)
+        T, H, cols = s.shape
+        assert H == HEADS
+        nvp = _c(num_valid_pages, np.int32)
+        assert nvp.shape == (T,)
+        out = np.empty((T, HEADS, num_ranges), dtype=_ROW)
+        bad = self.lib.oracle_top16_select_mapped(_ptr(s), T, cols, _ptr(nvp), init_blocks,
+                                                  local_blocks, num_ranges, index_scale,
+                                                  index_offset, _ptr(out))
+        if bad < 0:
+            raise ValueError("oracle_top16_select_mapped: invalid arguments")
+        return out["score"].copy(), out["id"].copy(), int(bad)
 
     def top16_select(self, scores, num_valid_pages, *, init_blocks: int, local_blocks: int,
                      num_ranges: int = 1):
@@ -215,3 +272,15 @@ def top16_select(*args, **kwargs):
 
 def top16_merge(*args, **kwargs):
     return default().top16_merge(*args, **kwargs)
+
+
+def written_columns_sharded(seq_len, page_size):
+    return default().written_columns_sharded(seq_len, page_size)
+
+
+def score_decode_sharded(*args, **kwargs):
+    return default().score_decode_sharded(*args, **kwargs)
+
+
+def top16_select_mapped(*args, **kwargs):
+    return default().top16_select_mapped(*args, **kwargs)

@@ -181,6 +181,27 @@ int64_t oracle_written_columns(int64_t seq_len)
     return (blocks + 3) / 4 * 4;
 }
 
+/* Key p is visible to a token at position pos of a request of seq_len keys
+ * when p < seq_len and p <= pos [P1 index_q: the token's position]. */
+static int key_visible(int64_t p, int64_t seq_len, int64_t pos)
+{
+    return p < seq_len && p <= pos;
+}
+
+/* Folds one visible key into a block's running maximum: best holds the max
+ * exact dot product, best_abs the max sum |q_i k_i| (both in 2^-18 units). */
+static void take_key(const uint8_t* q_row, const uint8_t* key, int* have, int64_t* best,
+                     int64_t* best_abs)
+{
+    int64_t abs_units = 0;
+    int64_t u = dot_units(q_row, key, &abs_units, NULL);
+    if (!*have || u > *best)
+        *best = u;
+    if (!*have || abs_units > *best_abs)
+        *best_abs = abs_units;
+    *have = 1;
+}
+
 /* Score of one plane element [P1 description, index_q, index_k, block_table]:
  * q_row is the token's 128-byte head row, pos its position
  * (seq_len - decode_query_len + j). Column c covers keys [128c, 128c + 128);
@@ -197,21 +218,15 @@ int oracle_score_element(const uint8_t* q_row, const uint8_t* index_k, int64_t n
     int have = 0, bad = 0;
     int64_t best = 0, best_abs = 0;
     for (int64_t p = c * ORACLE_BLOCK; p < (c + 1) * ORACLE_BLOCK; ++p) {
-        if (p >= seq_len || p > pos)
+        if (!key_visible(p, seq_len, pos))
             continue;
         int64_t page = block_table_row[p / page_size];
         if (page < 0 || page >= num_pages) {
             bad = 1;
             continue;
         }
-        const uint8_t* key = index_k + ((page * page_size) + (p % page_size)) * ORACLE_DIM;
-        int64_t abs_units = 0;
-        int64_t u = dot_units(q_row, key, &abs_units, NULL);
-        if (!have || u > best)
-            best = u;
-        if (!have || abs_units > best_abs)
-            best_abs = abs_units;
-        have = 1;
+        take_key(q_row, index_k + ((page * page_size) + (p % page_size)) * ORACLE_DIM, &have,
+                 &best, &best_abs);
     }
     *score = have ? units_to_float(best) : -INFINITY;
     if (amax)
@@ -349,6 +364,12 @@ static void emit_row(entry* forced, int n_forced, int budget, entry* cand, int64
     }
 }
 
+/* Columns per select range: w = ceil(cols / num_ranges). */
+static int64_t range_width(int32_t cols, int32_t num_ranges)
+{
+    return ((int64_t)cols + num_ranges - 1) / num_ranges;
+}
+
 /* Top16 select of every (token, head, range) row [P3 description]:
  * scores [T, 4, cols]; range r covers columns [r*w, min((r+1)*w, cols)),
  * w = ceil(cols / num_ranges). Valid ids are [0, n), n = num_valid_pages[t]
@@ -362,7 +383,7 @@ int64_t oracle_top16_select(const float* scores, int32_t num_tokens, int32_t col
     if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > ORACLE_TOPK ||
         num_ranges < 1 || cols < 1)
         return -1;
-    int64_t width = ((int64_t)cols + num_ranges - 1) / num_ranges;
+    int64_t width = range_width(cols, num_ranges);
     int64_t bad = 0;
     entry* cand = (entry*)malloc(sizeof(entry) * (size_t)(width > 0 ? width : 1));
     for (int64_t t = 0; t < num_tokens; ++t) {
@@ -457,4 +478,150 @@ int64_t oracle_top16_merge(const oracle_row* partial, int32_t num_tokens, int32_
     free(all);
     free(cand);
     return missing_rows;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row-sharded scoring and the column -> global id mapping                   */
+/* [P1 description, index_k, rank/world_size, Layout].                        */
+/* ------------------------------------------------------------------------ */
+
+/* Written columns of a request on one rank of a row-sharded cache: the
+ * request's ceil(seq_len / page_size) pages rounded up to a multiple of four
+ * [P1 description]. */
+int64_t oracle_written_columns_sharded(int64_t seq_len, int32_t page_size)
+{
+    if (seq_len <= 0)
+        return 0;
+    int64_t pages = (seq_len + page_size - 1) / page_size;
+    return (pages + 3) / 4 * 4;
+}
+
+/* One element of rank `rank`'s plane. The rank holds rows
+ * [rank * R, rank * R + R) of every page, R = page_size / world_size, as
+ * index_k_shard [num_pages, R, 128] [P1 index_k]. Column c is page c of the
+ * request (at page_size 128 that page is global B128 block c; at 256 the
+ * rank's rows lie in global block 2c + rank * 2 / world_size [P1
+ * description]), so its keys here are p = c * page_size + rank * R + i,
+ * i < R, read from index_k_shard[block_table_row[c], i, :]. Visible keys,
+ * value and amax as in oracle_score_element. */
+int oracle_score_element_sharded(const uint8_t* q_row, const uint8_t* index_k_shard,
+                                 int64_t num_pages, int32_t page_size, int32_t rank,
+                                 int32_t world_size, const int32_t* block_table_row,
+                                 int64_t seq_len, int64_t pos, int64_t c, float* score,
+                                 double* amax)
+{
+    ensure_table();
+    const int64_t rows = page_size / world_size;
+    int have = 0, bad = 0;
+    int64_t best = 0, best_abs = 0;
+    for (int64_t i = 0; i < rows; ++i) {
+        int64_t p = c * page_size + (int64_t)rank * rows + i;
+        if (!key_visible(p, seq_len, pos))
+            continue;
+        int64_t page = block_table_row[c];
+        if (page < 0 || page >= num_pages) {
+            bad = 1;
+            continue;
+        }
+        take_key(q_row, index_k_shard + (page * rows + i) * ORACLE_DIM, &have, &best,
+                 &best_abs);
+    }
+    *score = have ? units_to_float(best) : -INFINITY;
+    if (amax)
+        *amax = have ? ldexp((double)best_abs, -18) : 0.0;
+    return bad ? -1 : 0;
+}
+
+/* Rank `rank`'s whole plane: columns c < min(written_columns_sharded, cols)
+ * of every (token, head) row, others untouched. Returns the number of
+ * elements that met an out-of-range block_table entry, or -1 for invalid
+ * arguments (world_size must divide page_size, 0 <= rank < world_size). */
+int64_t oracle_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shard,
+                                    int64_t num_pages, const int32_t* block_table,
+                                    int64_t block_table_stride, const int32_t* seq_lens,
+                                    int32_t batch, int32_t page_size, int32_t decode_query_len,
+                                    int32_t rank, int32_t world_size, float* score_out,
+                                    int32_t cols, double* amax_out)
+{
+    if (world_size < 1 || page_size % world_size != 0 || rank < 0 || rank >= world_size)
+        return -1;
+    ensure_table();
+    int64_t bad = 0;
+    int64_t rows = (int64_t)batch * decode_query_len * ORACLE_HEADS;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t t = row / ORACLE_HEADS;
+        int64_t b = t / decode_query_len;
+        int64_t j = t % decode_query_len;
+        int64_t seq_len = seq_lens[b];
+        int64_t pos = seq_len - decode_query_len + j;
+        int64_t written = oracle_written_columns_sharded(seq_len, page_size);
+        if (written > cols)
+            written = cols;
+        const uint8_t* q_row = index_q + row * ORACLE_DIM;
+        for (int64_t c = 0; c < written; ++c) {
+            float s;
+            double a;
+            if (oracle_score_element_sharded(q_row, index_k_shard, num_pages, page_size, rank,
+                                             world_size, block_table + b * block_table_stride,
+                                             seq_len, pos, c, &s, &a) != 0)
+                ++bad;
+            score_out[row * cols + c] = s;
+            if (amax_out)
+                amax_out[row * cols + c] = a;
+        }
+    }
+    return bad;
+}
+
+/* Top16 select with plane column c standing for global block id
+ * index_scale * c + index_offset (index_scale >= 1, index_offset >= 0): the
+ * select rule of oracle_top16_select applied to the global ids, so validity
+ * (id < n), the forced ids and the tie order are all taken on global ids and
+ * the rows list global ids. n outside [0, index_scale * cols + index_offset]
+ * is counted and clamped. With index_scale 1 and index_offset 0 this is
+ * oracle_top16_select. Returns the count, or -1 for invalid arguments. */
+int64_t oracle_top16_select_mapped(const float* scores, int32_t num_tokens, int32_t cols,
+                                   const int32_t* num_valid_pages, int32_t init_blocks,
+                                   int32_t local_blocks, int32_t num_ranges, int32_t index_scale,
+                                   int32_t index_offset, oracle_row* out)
+{
+    if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > ORACLE_TOPK ||
+        num_ranges < 1 || cols < 1 || index_scale < 1 || index_offset < 0)
+        return -1;
+    int64_t width = range_width(cols, num_ranges);
+    int64_t n_max = (int64_t)index_scale * cols + index_offset;
+    int64_t bad = 0;
+    entry* cand = (entry*)malloc(sizeof(entry) * (size_t)(width > 0 ? width : 1));
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t n = num_valid_pages[t];
+        if (n < 0 || n > n_max) {
+            ++bad;
+            n = n < 0 ? 0 : n_max;
+        }
+        for (int h = 0; h < ORACLE_HEADS; ++h) {
+            const float* srow = scores + (t * ORACLE_HEADS + h) * (int64_t)cols;
+            for (int32_t r = 0; r < num_ranges; ++r) {
+                int64_t lo = r * width;
+                int64_t hi = lo + width < cols ? lo + width : cols;
+                entry forced[ORACLE_TOPK];
+                int n_forced = 0;
+                int64_t n_cand = 0;
+                for (int64_t c = lo; c < hi; ++c) {
+                    int64_t id = (int64_t)index_scale * c + index_offset;
+                    if (id >= n)
+                        continue;
+                    entry e = {srow[c], (int32_t)id};
+                    if (is_forced(id, n, init_blocks, local_blocks))
+                        forced[n_forced++] = e;
+                    else
+                        cand[n_cand++] = e;
+                }
+                emit_row(forced, n_forced, ORACLE_TOPK - n_forced, cand, n_cand,
+                         out + (t * ORACLE_HEADS + h) * num_ranges + r);
+            }
+        }
+    }
+    free(cand);
+    return bad;
 }

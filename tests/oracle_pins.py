@@ -385,8 +385,219 @@ def pin_merge_missing_forced(orc):
     assert missing == 1
 
 
+# ----------------------------------------------------------------------------
+# row-sharded scoring and the column -> global id mapping
+# ----------------------------------------------------------------------------
+
+def shard_index_map(page_size: int, rank: int, world_size: int):
+    """(index_scale, index_offset) taking rank `rank`'s plane column c to its
+    global B128 block id: c itself at page_size 128, 2c + rank*2//world_size
+    at page_size 256, where a column is a local page ("flashinfer.msa_ops.
+    msa_icp_decode_index_score_sharded", description)."""
+    if page_size == 128:
+        return 1, 0
+    return 2, rank * 2 // world_size
+
+
+def brute_force_plane_sharded(index_q, index_k, block_table, seq_lens, page_size, dql, cols,
+                              rank, world_size):
+    """One rank's plane by whole-request matrices over the FULL cache: the
+    rank owns rows [rank*R, rank*R + R) of every page (R = page_size /
+    world_size); column c is the request's page c, so its keys are the
+    positions p with p // page_size == c and rank*R <= p % page_size < rank*R + R.
+    Written columns: the request's pages rounded up to four. float64 products
+    (exact), explicit mask, one rounding. Unwritten entries are NaN."""
+    q = np.asarray(index_q, dtype=np.uint8)
+    k = np.asarray(index_k, dtype=np.uint8)
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    R = page_size // world_size
+    B = sl.shape[0]
+    out = np.full((B * dql, 4, cols), np.nan, dtype=np.float32)
+    amax = np.zeros((B * dql, 4, cols), dtype=np.float64)
+    for b in range(B):
+        s = int(sl[b])
+        if s <= 0:
+            continue
+        p = np.arange(s)
+        kd = torch_decode(k[bt[b, p // page_size], p % page_size])
+        qd = torch_decode(q[b * dql:(b + 1) * dql]).reshape(dql * 4, 128)
+        S = qd @ kd.T
+        A = np.abs(qd) @ np.abs(kd).T
+        mine = (p % page_size >= rank * R) & (p % page_size < rank * R + R)
+        ncols = min(-(-(-(-s // page_size)) // 4) * 4, cols)
+        for r in range(dql * 4):
+            j = r // 4
+            vis = mine & (p <= s - dql + j)
+            for c in range(ncols):
+                sel = vis & (p // page_size == c)
+                if sel.any():
+                    out[b * dql + j, r % 4, c] = np.float32(S[r, sel].max())
+                    amax[b * dql + j, r % 4, c] = A[r, sel].max()
+                else:
+                    out[b * dql + j, r % 4, c] = NEG_INF
+    return out, amax
+
+
+def _sharded_cases():
+    # (workload, world_size)
+    yield workloads.generate(batch=3, seq=("list", [300, 1000, 129]), page_size=128, dql=1,
+                             seed=21), 2
+    yield workloads.generate(batch=3, seq=("list", [700, 64, 1025]), page_size=128, dql=3,
+                             seed=22, scale=0.5), 4
+    yield workloads.generate(batch=4, seq=("list", [700, 256, 513, 1]), page_size=256, dql=2,
+                             seed=23, outlier_frac=0.05), 2
+    yield workloads.generate(batch=3, seq=("list", [0, 200, 1100]), page_size=256, dql=5,
+                             seed=24), 4
+
+
+def pin_sharded_plane_brute_force(orc):
+    """A rank's plane == brute force over the full cache, bit for bit
+    (values, amax and the written range, with spare columns that must stay
+    unwritten)."""
+    for w, ws in _sharded_cases():
+        # 8 spare columns past the widest request's written range
+        cols = max(4, -(-(-(-int(w.seq_lens.max()) // w.page_size)) // 4) * 4) + 8
+        for rank in range(ws):
+            shard = workloads.shard_rows(w.index_k, rank, ws).numpy()
+            args = (w.index_q.numpy(), shard, w.block_table.numpy(), w.seq_lens.numpy())
+            plane, amax, bad = orc.score_decode_sharded(
+                *args, page_size=w.page_size, decode_query_len=w.dql, rank=rank,
+                world_size=ws, cols=cols, want_amax=True)
+            ref, ref_amax = brute_force_plane_sharded(
+                w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(),
+                w.seq_lens.numpy(), w.page_size, w.dql, cols, rank, ws)
+            assert bad == 0
+            written = ~np.isnan(ref)
+            assert np.array_equal(np.isnan(plane), np.isnan(ref)), (w.name, rank)
+            assert np.array_equal(plane[written], ref[written]), (w.name, rank)
+            assert np.array_equal(amax[written], ref_amax[written]), (w.name, rank)
+
+
+def pin_sharded_rows_partition(orc):
+    """The ranks' rows partition every page, so per global B128 block the max
+    over the ranks that hold its rows equals the unsharded plane's column
+    (page_size 128: every rank holds part of block c; 256: rank r holds part
+    of block 2c + r*2//world_size)."""
+    for w, ws in _sharded_cases():
+        args = (w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(),
+                w.seq_lens.numpy())
+        full, _, _ = orc.score_decode(*args, page_size=w.page_size, decode_query_len=w.dql,
+                                      cols=w.cols)
+        scols = max(4, -(-(-(-int(w.seq_lens.max()) // w.page_size)) // 4) * 4)
+        combined = np.full(full.shape, -np.inf, dtype=np.float32)
+        for rank in range(ws):
+            shard = workloads.shard_rows(w.index_k, rank, ws).numpy()
+            plane, _, _ = orc.score_decode_sharded(
+                args[0], shard, args[2], args[3], page_size=w.page_size,
+                decode_query_len=w.dql, rank=rank, world_size=ws, cols=scols)
+            scale, offset = shard_index_map(w.page_size, rank, ws)
+            for c in range(scols):
+                gid = scale * c + offset
+                if gid >= w.cols:
+                    continue
+                col = np.where(np.isnan(plane[:, :, c]), -np.inf, plane[:, :, c])
+                combined[:, :, gid] = np.maximum(combined[:, :, gid], col)
+        written = ~np.isnan(full)
+        assert np.array_equal(combined[written], full[written]), w.name
+
+
+def brute_select_row_mapped(srow, n, lo, hi, init, local, scale, offset):
+    """Top16 row of columns [lo, hi) whose global ids are scale*c + offset, by
+    rank counting on global ids (valid: id < n). Returns (ids, columns)."""
+    cols = [c for c in range(lo, hi) if scale * c + offset < n]
+    gid = {c: scale * c + offset for c in cols}
+    forced = [c for c in cols if gid[c] < init or gid[c] >= n - local]
+    cand = [c for c in cols if c not in forced]
+    budget = 16 - len(forced)
+    taken = []
+    for x in cand:
+        beat = sum(1 for y in cand if y != x and (srow[y] > srow[x] or
+                                                  (srow[y] == srow[x] and gid[y] < gid[x])))
+        if beat < budget:
+            taken.append(x)
+    chosen = sorted(forced + taken, key=lambda c: gid[c])
+    return [gid[c] for c in chosen], chosen
+
+
+def pin_mapped_select(orc, seed=25):
+    """Mapped select: identity mapping == plain select; other mappings ==
+    rank counting on global ids (ids, raw scores, padding)."""
+    rng = np.random.default_rng(seed)
+    for ties in (False, True):
+        T, cols = 3, 70
+        s = _random_plane(rng, T, cols, ties)
+        nvp = np.array([cols, 9, int(rng.integers(0, cols + 1))], np.int32)
+        a = orc.top16_select(s, nvp, init_blocks=2, local_blocks=3, num_ranges=3)
+        b = orc.top16_select_mapped(s, nvp, init_blocks=2, local_blocks=3, num_ranges=3)
+        assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32),
+                                                             b[0].view(np.uint32))
+        for scale, offset, init, local, R in [(2, 0, 1, 2, 1), (2, 1, 4, 4, 3),
+                                              (1, 0, 0, 16, 2), (2, 1, 16, 0, 1)]:
+            nvp2 = np.array([scale * cols + offset, 17, int(rng.integers(0, 2 * cols))],
+                            np.int32)
+            sc, ids, bad = orc.top16_select_mapped(s, nvp2, init_blocks=init,
+                                                   local_blocks=local, num_ranges=R,
+                                                   index_scale=scale, index_offset=offset)
+            assert bad == 0
+            w = -(-cols // R)
+            for t in range(T):
+                for h in range(4):
+                    for r in range(R):
+                        exp_ids, exp_cols = brute_select_row_mapped(
+                            s[t, h], int(nvp2[t]), r * w, min(r * w + w, cols), init, local,
+                            scale, offset)
+                        m = len(exp_ids)
+                        got = [int(x) for x in ids[t, h, r]]
+                        assert got[:m] == exp_ids and all(x == -1 for x in got[m:])
+                        assert np.array_equal(sc[t, h, r, :m].view(np.uint32),
+                                              s[t, h, exp_cols].view(np.uint32))
+                        assert np.all(np.isneginf(sc[t, h, r, m:]))
+
+
+def pin_sharded_chain_exact(orc):
+    """Each rank's plane, mapped select over R ranges, then the merge of all
+    ranks' rows == select over the unsharded plane, bit for bit (the merge
+    keeps an id's highest score, and a block's max over its row shards is
+    its unsharded max)."""
+    for w, ws in _sharded_cases():
+        args = (w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(),
+                w.seq_lens.numpy())
+        nvp = w.num_valid_pages.numpy()
+        full, _, _ = orc.score_decode(*args, page_size=w.page_size, decode_query_len=w.dql,
+                                      cols=w.cols)
+        full = np.where(np.isnan(full), np.float32(-np.inf), full)
+        ref_s, ref_i, _ = orc.top16_select(full, nvp, init_blocks=w.init_blocks,
+                                           local_blocks=w.local_blocks)
+        scols = max(4, -(-(-(-int(w.seq_lens.max()) // w.page_size)) // 4) * 4)
+        R = 2
+        rows_s, rows_i = [], []
+        for rank in range(ws):
+            shard = workloads.shard_rows(w.index_k, rank, ws).numpy()
+            plane, _, _ = orc.score_decode_sharded(
+                args[0], shard, args[2], args[3], page_size=w.page_size,
+                decode_query_len=w.dql, rank=rank, world_size=ws, cols=scols)
+            plane = np.where(np.isnan(plane), np.float32(-np.inf), plane)
+            scale, offset = shard_index_map(w.page_size, rank, ws)
+            ps, pi, bad = orc.top16_select_mapped(plane, nvp, init_blocks=w.init_blocks,
+                                                  local_blocks=w.local_blocks, num_ranges=R,
+                                                  index_scale=scale, index_offset=offset)
+            assert bad == 0
+            rows_s.append(ps)
+            rows_i.append(pi)
+        ms, mi, missing = orc.top16_merge(np.concatenate(rows_s, axis=2),
+                                          np.concatenate(rows_i, axis=2), nvp,
+                                          init_blocks=w.init_blocks,
+                                          local_blocks=w.local_blocks)
+        assert missing == 0, w.name
+        assert np.array_equal(mi, ref_i[:, :, 0]), w.name
+        assert np.array_equal(ms.view(np.uint32), ref_s[:, :, 0].view(np.uint32)), w.name
+
+
 ALL_PINS = [
     pin_e4m3_table, pin_dots_vs_float64, pin_code_pairs, pin_plane_brute_force,
     pin_plane_closed_form, pin_written_range, pin_column_counts_golden, pin_select_brute_force,
     pin_select_invariants, pin_merge_split_equivalence, pin_merge_missing_forced,
+    pin_sharded_plane_brute_force, pin_sharded_rows_partition, pin_mapped_select,
+    pin_sharded_chain_exact,
 ]

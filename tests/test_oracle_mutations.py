@@ -13,12 +13,12 @@ import oracle_pins as P
 
 # (name, exact text in msa_oracle.c, replacement)
 MUTATIONS = [
-    ("mask_off_by_one", "if (p >= seq_len || p > pos)", "if (p >= seq_len || p >= pos)"),
+    ("mask_off_by_one", "return p < seq_len && p <= pos;", "return p < seq_len && p < pos;"),
     ("normal_exponent", "(int64_t)(8 + mantissa) << (exponent - 1)",
      "(int64_t)(8 + mantissa) << exponent"),
     ("subnormal_as_normal", "magnitude_units = mantissa;", "magnitude_units = 8 + mantissa;"),
     ("dropped_sign", "        acc += prod;\n", "        acc += prod < 0 ? -prod : prod;\n"),
-    ("max_becomes_min", "if (!have || u > best)", "if (!have || u < best)"),
+    ("max_becomes_min", "if (!*have || u > *best)", "if (!*have || u < *best)"),
     ("page_row_index", "((page * page_size) + (p % page_size))",
      "((page * page_size) + (p % ORACLE_BLOCK))"),
     ("unpadded_columns", "return (blocks + 3) / 4 * 4;", "return blocks;"),
@@ -28,13 +28,26 @@ MUTATIONS = [
      "    if (a->score < b->score)\n        return 1;\n    return (a->id < b->id) - (a->id > b->id);"),
     ("forced_end_off_by_one", "return id < init_blocks || id >= n - local_blocks;",
      "return id < init_blocks || id > n - local_blocks;"),
-    ("range_width_floor", "int64_t width = ((int64_t)cols + num_ranges - 1) / num_ranges;",
-     "int64_t width = (int64_t)cols / num_ranges;"),
+    ("range_width_floor", "return ((int64_t)cols + num_ranges - 1) / num_ranges;",
+     "return (int64_t)cols / num_ranges;"),
     ("merge_budget", "ORACLE_TOPK - (int)expected_forced, cand",
      "ORACLE_TOPK - (int)expected_forced - 1, cand"),
     ("amax_signed", "acc_abs += prod < 0 ? -prod : prod;", "acc_abs += prod;"),
     ("ascending_by_score", "qsort(chosen, (size_t)m, sizeof(entry), id_cmp);",
      "qsort(chosen, (size_t)m, sizeof(entry), rank_cmp);"),
+    # row-sharded scoring and the column -> global id mapping
+    ("shard_rank_offset_dropped", "int64_t p = c * page_size + (int64_t)rank * rows + i;",
+     "int64_t p = c * page_size + i;"),
+    ("shard_key_row", "index_k_shard + (page * rows + i) * ORACLE_DIM",
+     "index_k_shard + (page * rows + (rows - 1 - i)) * ORACLE_DIM"),
+    ("sharded_columns_unpadded", "return (pages + 3) / 4 * 4;", "return pages;"),
+    ("sharded_columns_in_blocks", "int64_t pages = (seq_len + page_size - 1) / page_size;",
+     "int64_t pages = (seq_len + ORACLE_BLOCK - 1) / ORACLE_BLOCK;"),
+    ("mapped_offset_dropped", "int64_t id = (int64_t)index_scale * c + index_offset;",
+     "int64_t id = (int64_t)index_scale * c;"),
+    ("mapped_forced_on_columns",
+     "entry e = {srow[c], (int32_t)id};\n                    if (is_forced(id, n,",
+     "entry e = {srow[c], (int32_t)id};\n                    if (is_forced(c, n,"),
 ]
 
 

@@ -203,3 +203,16 @@ def config(n: int, **overrides) -> Workload:
 def index_k_bytes(w: Workload) -> int:
     """Algorithmic index-K bytes of one pass: 128 bytes per key of every request."""
     return w.total_keys * DIM
+
+
+def shard_rows(index_k, rank: int, world_size: int):
+    """Rank `rank`'s shard of a cache whose pages are split by rows over
+    world_size ranks: rows [rank * R, (rank + 1) * R) of every page,
+    R = page_size / world_size, as a contiguous [pages, R, 128] tensor (the
+    layout one rank holds). Pure data movement."""
+    pages, page_size, dim = index_k.shape
+    if page_size % world_size != 0 or not 0 <= rank < world_size:
+        raise ValueError("world_size must divide page_size and 0 <= rank < world_size")
+    r = page_size // world_size
+    return index_k[:, rank * r:(rank + 1) * r, :].contiguous()
+
