@@ -21,8 +21,11 @@
  *   "flashinfer.msa_ops.msa_icp_topk_select_publish"         (step 2, row format)
  *   "flashinfer.msa_ops.prepare_msa_icp_indexer"             (the decode chain
  *       score -> select -> merge; forced init/local blocks)
- * Here one GPU holds every page's full rows. There is no rank, world size,
- * peer publish or receive row.
+ * By default one GPU holds every page's full rows. Three entry points serve
+ * one rank's share of a cache whose pages are split by rows over 2 or 4
+ * ranks (the pages' sharded layout): msa_score_decode_sharded,
+ * msa_top16_select_mapped and msa_top16_merge_dedup. There is no peer
+ * publish or receive row: the rows stay on this GPU.
  *
  * Conventions for every entry point:
  *  - Pointers named as device buffers are device memory that the caller
@@ -115,6 +118,36 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
                      hipStream_t stream);
 
 /*
+ * Step 1 on one rank of a row-sharded cache.
+ * Source: "msa_icp_decode_index_score_sharded" (description: the written
+ * columns, and the global block a column stands for at page_size 256;
+ * index_k: the [pages, page_size / world_size, 128] shard; rank, world_size;
+ * Layout: world_size 2 or 4).
+ *
+ * Arguments are those of msa_score_decode, except:
+ * index_k_shard  device, e4m3fn bytes [num_pages, page_size / world_size, 128], contiguous,
+ *                16-byte aligned: rows [rank*R, rank*R + R) of every page,
+ *                R = page_size / world_size.
+ * rank, world_size  world_size 2 or 4, 0 <= rank < world_size.
+ *
+ * Column c of request b is the request's page c (block_table[b, c]). Its keys
+ * on this rank are the positions p = c*page_size + rank*R + i, i < R: part of
+ * global B128 block c at page_size 128, part of global block
+ * 2c + rank*2/world_size at 256. Writes columns c < min(roundup4(ceil(seq_len /
+ * page_size)), cols) (a W cut short by cols is counted in `errors`); other
+ * columns are not touched. The value is the maximum, over those keys with
+ * p < seq_len and p <= the token's position, of the dot product (fp8 products,
+ * fp32 accumulation), or -inf if there is none. The maximum over the ranks that
+ * hold a block's rows is that block's msa_score_decode column.
+ */
+int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shard,
+                             int64_t num_pages, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                             int32_t page_size, int32_t decode_query_len, int32_t rank,
+                             int32_t world_size, float* score_out, int32_t cols, int32_t* errors,
+                             hipStream_t stream);
+
+/*
  * Steps 1 and 2 in one launch: the score plane, and Top16 select per (token,
  * head, column range) on it.
  * Source: "prepare_msa_icp_indexer", decode: the chain score plane -> Top16
@@ -178,6 +211,28 @@ int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
                      int32_t num_ranges, msa_top16_row* out, int32_t* errors, hipStream_t stream);
 
 /*
+ * Step 2 on a plane whose column c stands for global block id
+ * index_scale * c + index_offset.
+ * Source: "msa_icp_topk_select_publish" (index_scale, index_offset: the page
+ * defers their meaning to a page that is not available, and this library
+ * reads them as that linear map) and "msa_icp_decode_index_score_sharded"
+ * (at page_size 256 a rank's column c is global block 2c + rank*2/world_size:
+ * index_scale 2, index_offset rank*2/world_size; at 128 the identity).
+ *
+ * Arguments are those of msa_top16_select, and index_scale >= 1, index_offset >= 0,
+ * index_scale*cols + index_offset < 2^31. Every id-based step is taken on global ids:
+ * validity (id < n), the forced ids [0, init) and [n - local, n), the tie order, and
+ * the ids written. num_valid_pages outside [0, index_scale*cols + index_offset] is
+ * counted in `errors` and clamped. With index_scale 1 and index_offset 0 this is
+ * msa_top16_select.
+ */
+int msa_top16_select_mapped(const float* scores, int32_t num_tokens, int32_t cols,
+                            const int32_t* num_valid_pages, int32_t init_blocks,
+                            int32_t local_blocks, int32_t num_ranges, int32_t index_scale,
+                            int32_t index_offset, msa_top16_row* out, int32_t* errors,
+                            hipStream_t stream);
+
+/*
  * Step 3: merge of the R per-range rows of each (token, head).
  * Source: "prepare_msa_icp_indexer" (decode: score plane -> Top16 select ->
  * merge). On one GPU the merge reduces the split-column lists of a row.
@@ -197,6 +252,27 @@ int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
 int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
                     const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
                     msa_top16_row* out, int32_t* errors, hipStream_t stream);
+
+/*
+ * Step 3 for partial rows in any order that may name the same id: the rows of
+ * ranks that each hold part of every page's rows (msa_score_decode_sharded at
+ * page_size 128, or at 256 with world_size 4) carry each rank's partial
+ * maximum of a block.
+ * Source: "prepare_msa_icp_indexer" (decode: the owner merge of the ranks'
+ * rows) and "msa_icp_decode_index_score_sharded" (index_k shard).
+ *
+ * partial          device [num_tokens, 4, R] rows, 1 <= R <= 64, in any order.
+ * Other arguments as for msa_top16_merge.
+ *
+ * Applies the select rule to the union of the rows' entries, an id met more than
+ * once keeping its highest score (a block's maximum over its rows is the maximum
+ * of its shards' maxima). Forced ids are recomputed over [0, n); one missing from
+ * the union is counted in `errors`. Every row of out is written on every call.
+ */
+int msa_top16_merge_dedup(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
+                          const int32_t* num_valid_pages, int32_t init_blocks,
+                          int32_t local_blocks, msa_top16_row* out, int32_t* errors,
+                          hipStream_t stream);
 
 /*
  * Steps 2 and 3 in one launch: Top16 select over R column ranges, then the

@@ -34,7 +34,8 @@ TOPK = 16
 COUNTER_STRIDE = 32  # int32 words per msa_score_select workspace counter (128 bytes)
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
-EXPORTS = ("msa_score_decode", "msa_score_select", "msa_top16_select", "msa_top16_merge", "msa_top16_select_merge",
+EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
+           "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
            "msa_score_columns", "msa_warmup", "msa_last_error")
 
 
@@ -66,6 +67,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_score_select.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, i32, i32,
                                      i32, P, P, P, P]
     lib.msa_score_select.restype = ctypes.c_int
+    lib.msa_score_decode_sharded.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32, i32, P,
+                                             i32, P, P]
+    lib.msa_score_decode_sharded.restype = ctypes.c_int
+    lib.msa_top16_select_mapped.argtypes = [P, i32, i32, P, i32, i32, i32, i32, i32, P, P, P]
+    lib.msa_top16_select_mapped.restype = ctypes.c_int
+    lib.msa_top16_merge_dedup.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
+    lib.msa_top16_merge_dedup.restype = ctypes.c_int
     lib.msa_top16_select.argtypes = [P, i32, i32, P, i32, i32, i32, P, P, P]
     lib.msa_top16_select.restype = ctypes.c_int
     lib.msa_top16_merge.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
@@ -150,7 +158,7 @@ def msa_warmup() -> None:
 
 
 def _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
-                decode_query_len):
+                decode_query_len, world_size=1):
     q = _u8(index_q, "index_q")
     k = _u8(index_k, "index_k")
     _dev(q, k, block_table, seq_lens, score_out)
@@ -158,8 +166,9 @@ def _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
     _need(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens: int32 [B]")
     _need(q.shape == (B * decode_query_len, NUM_HEADS, HEAD_DIM) and q.is_contiguous(),
           f"index_q: expected contiguous [{B * decode_query_len}, 4, 128], got {tuple(q.shape)}")
-    _need(k.dim() == 3 and k.shape[1] == page_size and k.shape[2] == HEAD_DIM and k.is_contiguous(),
-          f"index_k: expected contiguous [pages, {page_size}, 128], got {tuple(k.shape)}")
+    rows = page_size // world_size
+    _need(k.dim() == 3 and k.shape[1] == rows and k.shape[2] == HEAD_DIM and k.is_contiguous(),
+          f"index_k: expected contiguous [pages, {rows}, 128], got {tuple(k.shape)}")
     _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
           block_table.shape[0] == B and block_table.is_contiguous(),
           "block_table: contiguous int32 [B, width]")
@@ -180,6 +189,23 @@ def msa_score_decode(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
     args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
                        decode_query_len)
     _check(load().msa_score_decode(*args, _errors_ptr(errors), _stream_handle(stream)))
+
+
+def msa_score_decode_sharded(index_q: torch.Tensor, index_k_shard: torch.Tensor,
+                             block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             score_out: torch.Tensor, *, page_size: int, decode_query_len: int,
+                             rank: int, world_size: int, errors: torch.Tensor | None = None,
+                             stream=None) -> None:
+    """Rank `rank`'s score plane of a cache whose pages are split by rows over
+    world_size ranks: index_k_shard [pages, page_size / world_size, 128] holds
+    rows [rank*R, rank*R + R) of every page; column c is the request's page c.
+    See msa_indexer.h."""
+    _need(world_size in (2, 4) and page_size % world_size == 0,
+          "world_size must be 2 or 4")
+    args = _score_args(index_q, index_k_shard, block_table, seq_lens, score_out, page_size,
+                       decode_query_len, world_size)
+    _check(load().msa_score_decode_sharded(*args[:9], rank, world_size, *args[9:],
+                                           _errors_ptr(errors), _stream_handle(stream)))
 
 
 def score_select_workspace(batch: int, num_ranges: int, device="cuda") -> torch.Tensor:
@@ -234,6 +260,45 @@ def msa_top16_select(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: t
     _check(lib.msa_top16_select(scores.data_ptr(), T, cols, num_valid_pages.data_ptr(),
                                 init_blocks, local_blocks, num_ranges, out.data_ptr(),
                                 _errors_ptr(errors), _stream_handle(stream)))
+
+
+def msa_top16_select_mapped(scores: torch.Tensor, num_valid_pages: torch.Tensor,
+                            out: torch.Tensor, *, init_blocks: int, local_blocks: int,
+                            num_ranges: int = 1, index_scale: int = 1, index_offset: int = 0,
+                            errors: torch.Tensor | None = None, stream=None) -> None:
+    """Top16 rows [T, 4, R] with plane column c standing for global block id
+    index_scale * c + index_offset."""
+    _dev(scores, num_valid_pages, out)
+    _need(scores.dtype == torch.float32 and scores.dim() == 3 and scores.shape[1] == NUM_HEADS and
+          scores.is_contiguous(), "scores: contiguous float32 [T, 4, cols]")
+    T, _, cols = scores.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, {num_ranges}, 32]")
+    _check(load().msa_top16_select_mapped(scores.data_ptr(), T, cols, num_valid_pages.data_ptr(),
+                                          init_blocks, local_blocks, num_ranges, index_scale,
+                                          index_offset, out.data_ptr(), _errors_ptr(errors),
+                                          _stream_handle(stream)))
+
+
+def msa_top16_merge_dedup(partial: torch.Tensor, num_valid_pages: torch.Tensor,
+                          out: torch.Tensor, *, init_blocks: int, local_blocks: int,
+                          errors: torch.Tensor | None = None, stream=None) -> None:
+    """Merges partial rows [T, 4, R, 32] in any order, an id in several rows
+    keeping its highest score, into rows [T, 4, 32] (R <= 64)."""
+    _dev(partial, num_valid_pages, out)
+    _need(partial.dtype == torch.int32 and partial.dim() == 4 and partial.shape[1] == NUM_HEADS
+          and partial.shape[3] == ROW_WORDS and partial.is_contiguous(),
+          "partial: contiguous int32 [T, 4, R, 32]")
+    T, _, R, _ = partial.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
+          "num_valid_pages: int32 [T]")
+    _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, ROW_WORDS) and
+          out.is_contiguous(), f"out: contiguous int32 [{T}, 4, 32]")
+    _check(load().msa_top16_merge_dedup(partial.data_ptr(), T, R, num_valid_pages.data_ptr(),
+                                        init_blocks, local_blocks, out.data_ptr(),
+                                        _errors_ptr(errors), _stream_handle(stream)))
 
 
 def msa_top16_merge(partial: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,

@@ -86,6 +86,76 @@ int score_params(const char* fn, const uint8_t* index_q, const uint8_t* index_k,
     p->page_size = page_size;
     p->dql = decode_query_len;
     p->cols = cols;
+    p->rank = 0;
+    p->world_size = 1;
+    return MSA_OK;
+}
+
+int select_impl(const char* fn, const float* scores, int32_t num_tokens, int32_t cols,
+                const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                int32_t num_ranges, int32_t index_scale, int32_t index_offset,
+                msa_top16_row* out, int32_t* errors, hipStream_t stream)
+{
+    MSA_CHECK(scores && num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(scores, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
+                  aligned(errors, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4*ranges < 2^31", fn, num_tokens);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SELECT_COLS,
+              "%s: cols (%d) must satisfy 0 < cols <= %d", fn, cols, MSA_MAX_SELECT_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    MSA_CHECK(index_scale >= 1 && index_offset >= 0,
+              "%s: index_scale (%d) must be >= 1 and index_offset (%d) >= 0", fn, index_scale,
+              index_offset);
+    MSA_CHECK((int64_t)index_scale * cols + index_offset <= 0x7FFFFFFF,
+              "%s: index_scale * cols + index_offset must be < 2^31", fn);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+
+    msa::SelectParams p;
+    p.scores = scores;
+    p.nvp = num_valid_pages;
+    p.out = out;
+    p.errors = errors;
+    p.num_tokens = num_tokens;
+    p.cols = cols;
+    p.init_blocks = init_blocks;
+    p.local_blocks = local_blocks;
+    p.num_ranges = num_ranges;
+    p.width = (cols + num_ranges - 1) / num_ranges;
+    p.index_scale = index_scale;
+    p.index_offset = index_offset;
+    return launch_result(msa::launch_top16_select(p, stream), fn);
+}
+
+int merge_impl(const char* fn, const msa_top16_row* partial, int32_t num_tokens,
+               int32_t num_ranges, int32_t max_ranges, const int32_t* num_valid_pages,
+               int32_t init_blocks, int32_t local_blocks, msa_top16_row* out, int32_t* errors,
+               msa::MergeParams* p)
+{
+    MSA_CHECK(partial && num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(partial, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
+                  aligned(errors, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4 < 2^31", fn, num_tokens);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= max_ranges,
+              "%s: num_ranges (%d) must be in [1, %d]", fn, num_ranges, max_ranges);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+    p->partial = partial;
+    p->nvp = num_valid_pages;
+    p->out = out;
+    p->errors = errors;
+    p->num_tokens = num_tokens;
+    p->num_ranges = num_ranges;
+    p->init_blocks = init_blocks;
+    p->local_blocks = local_blocks;
     return MSA_OK;
 }
 
@@ -124,6 +194,30 @@ int msa_score_decode(const uint8_t* index_q, const uint8_t* index_k, int64_t num
     if (rc != MSA_OK)
         return rc;
     return launch_result(msa::launch_score_decode(p, stream), "msa_score_decode");
+}
+
+int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shard,
+                             int64_t num_pages, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* seq_lens, int32_t batch,
+                             int32_t page_size, int32_t decode_query_len, int32_t rank,
+                             int32_t world_size, float* score_out, int32_t cols, int32_t* errors,
+                             hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    const char* fn = "msa_score_decode_sharded";
+    msa::ScoreParams p;
+    const int rc = score_params(fn, index_q, index_k_shard, num_pages, block_table,
+                                block_table_stride, seq_lens, batch, page_size, decode_query_len,
+                                score_out, cols, errors, &p);
+    if (rc != MSA_OK)
+        return rc;
+    MSA_CHECK(world_size == 2 || world_size == 4, "%s: world_size (%d) must be 2 or 4", fn,
+              world_size);
+    MSA_CHECK(rank >= 0 && rank < world_size, "%s: rank (%d) must be in [0, world_size)", fn,
+              rank);
+    p.rank = rank;
+    p.world_size = world_size;
+    return launch_result(msa::launch_score_decode(p, stream), fn);
 }
 
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
@@ -174,34 +268,20 @@ int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,
                      int32_t num_ranges, msa_top16_row* out, int32_t* errors, hipStream_t stream)
 {
     g_last_error[0] = '\0';
-    const char* fn = "msa_top16_select";
-    MSA_CHECK(scores && num_valid_pages && out, "%s: null pointer argument", fn);
-    MSA_CHECK(aligned(scores, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
-                  aligned(errors, 4),
-              "%s: arrays must be 4-byte aligned", fn);
-    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
-              "%s: num_tokens (%d) must be >= 1 and tokens*4*ranges < 2^31", fn, num_tokens);
-    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SELECT_COLS,
-              "%s: cols (%d) must satisfy 0 < cols <= %d", fn, cols, MSA_MAX_SELECT_COLS);
-    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
-              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
-              MSA_MAX_RANGES);
-    int rc = check_forced(fn, init_blocks, local_blocks);
-    if (rc != MSA_OK)
-        return rc;
+    return select_impl("msa_top16_select", scores, num_tokens, cols, num_valid_pages, init_blocks,
+                       local_blocks, num_ranges, 1, 0, out, errors, stream);
+}
 
-    msa::SelectParams p;
-    p.scores = scores;
-    p.nvp = num_valid_pages;
-    p.out = out;
-    p.errors = errors;
-    p.num_tokens = num_tokens;
-    p.cols = cols;
-    p.init_blocks = init_blocks;
-    p.local_blocks = local_blocks;
-    p.num_ranges = num_ranges;
-    p.width = (cols + num_ranges - 1) / num_ranges;
-    return launch_result(msa::launch_top16_select(p, stream), fn);
+int msa_top16_select_mapped(const float* scores, int32_t num_tokens, int32_t cols,
+                            const int32_t* num_valid_pages, int32_t init_blocks,
+                            int32_t local_blocks, int32_t num_ranges, int32_t index_scale,
+                            int32_t index_offset, msa_top16_row* out, int32_t* errors,
+                            hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    return select_impl("msa_top16_select_mapped", scores, num_tokens, cols, num_valid_pages,
+                       init_blocks, local_blocks, num_ranges, index_scale, index_offset, out,
+                       errors, stream);
 }
 
 int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
@@ -209,29 +289,27 @@ int msa_top16_merge(const msa_top16_row* partial, int32_t num_tokens, int32_t nu
                     msa_top16_row* out, int32_t* errors, hipStream_t stream)
 {
     g_last_error[0] = '\0';
-    const char* fn = "msa_top16_merge";
-    MSA_CHECK(partial && num_valid_pages && out, "%s: null pointer argument", fn);
-    MSA_CHECK(aligned(partial, 4) && aligned(num_valid_pages, 4) && aligned(out, 4) &&
-                  aligned(errors, 4),
-              "%s: arrays must be 4-byte aligned", fn);
-    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS <= 0x7FFFFFFF,
-              "%s: num_tokens (%d) must be >= 1 and tokens*4 < 2^31", fn, num_tokens);
-    MSA_CHECK(num_ranges >= 1 && num_ranges <= MSA_MAX_RANGES,
-              "%s: num_ranges (%d) must be in [1, %d]", fn, num_ranges, MSA_MAX_RANGES);
-    int rc = check_forced(fn, init_blocks, local_blocks);
+    msa::MergeParams p;
+    const int rc = merge_impl("msa_top16_merge", partial, num_tokens, num_ranges, MSA_MAX_RANGES,
+                              num_valid_pages, init_blocks, local_blocks, out, errors, &p);
     if (rc != MSA_OK)
         return rc;
+    return launch_result(msa::launch_top16_merge(p, stream), "msa_top16_merge");
+}
 
+int msa_top16_merge_dedup(const msa_top16_row* partial, int32_t num_tokens, int32_t num_ranges,
+                          const int32_t* num_valid_pages, int32_t init_blocks,
+                          int32_t local_blocks, msa_top16_row* out, int32_t* errors,
+                          hipStream_t stream)
+{
+    g_last_error[0] = '\0';
     msa::MergeParams p;
-    p.partial = partial;
-    p.nvp = num_valid_pages;
-    p.out = out;
-    p.errors = errors;
-    p.num_tokens = num_tokens;
-    p.num_ranges = num_ranges;
-    p.init_blocks = init_blocks;
-    p.local_blocks = local_blocks;
-    return launch_result(msa::launch_top16_merge(p, stream), fn);
+    const int rc = merge_impl("msa_top16_merge_dedup", partial, num_tokens, num_ranges,
+                              msa::kMaxDedupRanges, num_valid_pages, init_blocks, local_blocks,
+                              out, errors, &p);
+    if (rc != MSA_OK)
+        return rc;
+    return launch_result(msa::launch_top16_merge_dedup(p, stream), "msa_top16_merge_dedup");
 }
 
 int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols,

@@ -29,6 +29,8 @@ struct ScoreParams {
     int32_t page_size;       // 128 or 256
     int32_t dql;             // 1..8
     int32_t cols;            // multiple of 4, <= 8192
+    int32_t rank;            // row-sharded cache: this rank (0 when world_size == 1)
+    int32_t world_size;      // 1: full page rows; 2 or 4: index_k holds rank's rows
 };
 
 struct SelectParams {
@@ -42,6 +44,8 @@ struct SelectParams {
     int32_t local_blocks;
     int32_t num_ranges;
     int32_t width;           // ceil(cols / R)
+    int32_t index_scale;     // column c stands for global id index_scale * c + index_offset
+    int32_t index_offset;
 };
 
 struct MergeParams {
@@ -58,6 +62,8 @@ struct MergeParams {
 // Fused select + merge: at most this many ranges (one wave each) and at
 // most 2048 columns per range.
 constexpr int kMaxFusedRanges = 16;
+// Duplicate-aware merge: one wave sorts at most this many rows' entries.
+constexpr int kMaxDedupRanges = 64;
 constexpr int kMaxFusedWidth = 2048;
 
 struct SelectMergeParams {
@@ -94,6 +100,7 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream);
 hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream);
 hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_top16_merge_dedup(const MergeParams& p, hipStream_t stream);
 
 // Loads the kernels of each file into the current device's context.
 hipError_t warmup_score_kernels();

@@ -179,7 +179,8 @@ __device__ __forceinline__ float max4(v4f a)
 template <int NT, int kParts, bool kMask>
 __device__ __forceinline__ void score_block(const uint8_t* block, uint8_t* tile,
                                             const Bf16Slice (&qb)[NT], int lane, int r16, int g,
-                                            const int (&lim)[NT], float (&mx)[NT])
+                                            const int (&lim)[NT], float (&mx)[NT],
+                                            int parts = kParts)
 {
     constexpr int kTiles = 8 / kParts;
     constexpr int kPieceRows = kTiles * 16;
@@ -189,6 +190,8 @@ __device__ __forceinline__ void score_block(const uint8_t* block, uint8_t* tile,
         mx[n] = -INFINITY;
 #pragma unroll
     for (int part = 0; part < kParts; ++part) {
+        if (part >= parts)  // a row-sharded column holds fewer keys
+            break;
         stage_piece<kPieceRows>(block + part * kPieceRows * kDim, tile, lane);
         __builtin_amdgcn_s_waitcnt(0);  // the piece's DMA has landed in LDS
 #pragma unroll
@@ -220,14 +223,17 @@ __device__ __forceinline__ void score_block(const uint8_t* block, uint8_t* tile,
     }
 }
 
-// Written plane columns of a request: roundup4(ceil(seq / 128)) clamped to
-// the plane width (*clamped says whether the width cut it short).
-__device__ __forceinline__ int written_cols(int seq, int cols, bool& clamped)
+// Written plane columns of a request: roundup4(ceil(seq / col_stride))
+// clamped to the plane width (*clamped says whether the width cut it short).
+// col_stride is 128 (a column per B128 block), or page_size on a row-sharded
+// cache (a column per page).
+__device__ __forceinline__ int written_cols(int seq, int cols, bool& clamped,
+                                            int col_stride = kBlockTokens)
 {
     clamped = false;
     if (seq <= 0)
         return 0;
-    const int64_t nblk = ((int64_t)seq + kBlockTokens - 1) / kBlockTokens;
+    const int64_t nblk = ((int64_t)seq + col_stride - 1) / col_stride;
     const int64_t w = (nblk + 3) / 4 * 4;
     clamped = w > cols;
     return clamped ? cols : (int)w;
@@ -252,6 +258,57 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v;
 }
 
+// Where a plane column's keys are.
+//  * Full page rows ("flashinfer.msa_ops.msa_icp_decode_index_score_sharded",
+//    with every page's rows on this device): column c is global B128 block
+//    c, keys [128c, 128c + 128), rows [(c % cpp) * 128, +128) of page
+//    c / cpp (cpp = page_size / 128 columns per page).
+//  * Row-sharded cache (same page, index_k shard [pages, page_size /
+//    world_size, 128] and the description's columns): the rank holds rows
+//    [rank * R, rank * R + R) of every page, R = page_size / world_size;
+//    column c is the request's page c, its keys are the positions
+//    c * page_size + rank * R + i (i < R), rows [0, R) of the shard page.
+struct ColumnGeometry {
+    int col_shift;   // log2(columns per block-table entry)
+    int col_stride;  // key positions per column step
+    int pos_off;     // position of a column's first key minus c * col_stride
+    int page_rows;   // key rows per stored page
+    int col_rows;    // keys per column
+    int parts;       // 32-key DMA pieces per column
+};
+
+template <bool kSharded>
+__device__ __forceinline__ ColumnGeometry column_geometry(const ScoreParams& p)
+{
+    ColumnGeometry gm;
+    if constexpr (kSharded) {
+        const int r = p.page_size / p.world_size;
+        gm.col_shift = 0;
+        gm.col_stride = p.page_size;
+        gm.pos_off = p.rank * r;
+        gm.page_rows = r;
+        gm.col_rows = r;
+        gm.parts = r / 32;
+    } else {
+        gm.col_shift = p.page_size == 256 ? 1 : 0;
+        gm.col_stride = kBlockTokens;
+        gm.pos_off = 0;
+        gm.page_rows = p.page_size;
+        gm.col_rows = kBlockTokens;
+        gm.parts = 4;
+    }
+    return gm;
+}
+
+// Columns of a request with at least one key below seq (the rest of its
+// written columns are padding, -inf).
+__device__ __forceinline__ int key_columns(int seq, const ColumnGeometry& gm)
+{
+    if (seq <= gm.pos_off)
+        return 0;
+    return (int)(((int64_t)seq - gm.pos_off + gm.col_stride - 1) / gm.col_stride);
+}
+
 // Block-table entries of a window, one per lane.
 struct WindowPages {
     int page;           // this lane's page (0 for an entry that is out of range)
@@ -261,9 +318,8 @@ struct WindowPages {
 // Issues the loads of the block-table entries of columns [c_begin, c_last]
 // of request b (at most kChunk pages), one per lane.
 __device__ __forceinline__ WindowPages load_window_pages(const ScoreParams& p, int b, int c_begin,
-                                                         int c_last, int lane)
+                                                         int c_last, int lane, int ps_shift)
 {
-    const int ps_shift = p.page_size == 256 ? 1 : 0;
     const int pg_begin = c_begin >> ps_shift;
     const int pg_count = (c_last >> ps_shift) - pg_begin + 1;
     WindowPages w;
@@ -292,15 +348,15 @@ __device__ __forceinline__ WindowPages load_window_pages(const ScoreParams& p, i
 // block: on this ISA stores share the vector-memory counter with the DMA, so
 // a store issued mid-window would make every later DMA wait also wait for it.
 template <int NT, int kParts, bool kDeviceScope, int kUnit>
-__device__ __forceinline__ void score_window(const ScoreParams& p, int b, int seq, int nblk,
-                                             int c_begin, int c_end, const WindowPages& wp,
-                                             const Bf16Slice (&qb)[NT], const int (&pos)[NT],
-                                             uint8_t* tile, float (*res)[kChunk], int lane,
-                                             int r16, int g)
+__device__ __forceinline__ void score_window(const ScoreParams& p, const ColumnGeometry& gm,
+                                             int b, int seq, int nblk, int c_begin, int c_end,
+                                             const WindowPages& wp, const Bf16Slice (&qb)[NT],
+                                             const int (&pos)[NT], uint8_t* tile,
+                                             float (*res)[kChunk], int lane, int r16, int g)
 {
     const int rows = p.dql * kHeads;
     const int64_t row_base = (int64_t)b * rows;
-    const int ps_shift = p.page_size == 256 ? 1 : 0;  // log2(B128 blocks per page)
+    const int ps_shift = gm.col_shift;  // log2(columns per page)
     const int c_last = min(c_end, nblk) - 1;  // < c_begin if the window is all padding
     const int pg_begin = c_begin >> ps_shift;
     const int my_page = wp.page;
@@ -311,26 +367,29 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
     auto block_ptr = [&](int c) -> const uint8_t* {
         const int page = __builtin_amdgcn_readlane(my_page, (c >> ps_shift) - pg_begin);
         const int half = c & ((1 << ps_shift) - 1);
-        return p.k + ((int64_t)page * p.page_size + half * kBlockTokens) * kDim;
+        return p.k + ((int64_t)page * gm.page_rows + half * kBlockTokens) * kDim;
     };
 
-    const int first_masked = seq - p.dql;  // blocks reaching past this key need the mask
+    const int first_masked = seq - p.dql;  // columns reaching past this key need the mask
     for (int c = c_begin; c < c_end; ++c) {
         float mx[NT];
         int lim[NT];
+        const int key0 = c * gm.col_stride + gm.pos_off;  // position of the column's first key
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-            lim[n] = pos[n] - c * kBlockTokens;
+            lim[n] = pos[n] - key0;
         const bool has_keys =
             c <= c_last && !((bad_mask >> ((min(c, c_last) >> ps_shift) - pg_begin)) & 1ull);
         if (!has_keys) {
 #pragma unroll
             for (int n = 0; n < NT; ++n)
                 mx[n] = -INFINITY;
-        } else if (c * kBlockTokens + (kBlockTokens - 1) > first_masked) {
-            score_block<NT, kParts, true>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
+        } else if (key0 + (gm.col_rows - 1) > first_masked) {
+            score_block<NT, kParts, true>(block_ptr(c), tile, qb, lane, r16, g, lim, mx,
+                                          gm.parts);
         } else {
-            score_block<NT, kParts, false>(block_ptr(c), tile, qb, lane, r16, g, lim, mx);
+            score_block<NT, kParts, false>(block_ptr(c), tile, qb, lane, r16, g, lim, mx,
+                                           gm.parts);
         }
         // lanes of group g == n keep query row 16n + lane%16
 #pragma unroll
@@ -381,10 +440,11 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, int b, int se
 // segment_done(b, c_begin, c_end) runs after the wave has issued the plane
 // stores of columns [c_begin, c_end) of request b, once per request it
 // touches. With kDeviceScope the plane stores are agent-scope atomic stores.
-template <int NT, int kParts, bool kDeviceScope, int kUnit, class SegmentDone>
+template <int NT, int kParts, bool kDeviceScope, int kUnit, bool kSharded, class SegmentDone>
 __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* tile,
                                                  float (*res)[kChunk], SegmentDone&& segment_done)
 {
+    const ColumnGeometry gm = column_geometry<kSharded>(p);
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -398,7 +458,9 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     int64_t base = 0;
     if (p.batch <= 64) {
         bool clamped;
-        const int gb = lane < p.batch ? written_cols(p.seq_lens[lane], p.cols, clamped) / kUnit : 0;
+        const int gb = lane < p.batch
+                           ? written_cols(p.seq_lens[lane], p.cols, clamped, gm.col_stride) / kUnit
+                           : 0;
         const int incl = wave_inclusive_scan(gb, lane);
         const int64_t total = __shfl(incl, 63);
         g_lo = total * (int64_t)blockIdx.x / gridDim.x;
@@ -413,7 +475,9 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
             bool clamped;
             const int bb = b0 + lane;
-            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / kUnit : 0;
+            const int gb = bb < p.batch
+                               ? written_cols(p.seq_lens[bb], p.cols, clamped, gm.col_stride) / kUnit
+                               : 0;
             total += wave_sum(gb);
         }
         g_lo = total * (int64_t)blockIdx.x / gridDim.x;
@@ -423,7 +487,9 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
             bool clamped;
             const int bb = b0 + lane;
-            const int gb = bb < p.batch ? written_cols(p.seq_lens[bb], p.cols, clamped) / kUnit : 0;
+            const int gb = bb < p.batch
+                               ? written_cols(p.seq_lens[bb], p.cols, clamped, gm.col_stride) / kUnit
+                               : 0;
             const int incl = wave_inclusive_scan(gb, lane);
             const int chunk_total = __shfl(incl, 63);
             if (base + chunk_total > g_lo) {
@@ -440,14 +506,14 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     while (gcur < g_hi) {
         const int seq = p.seq_lens[b];
         bool clamped;
-        const int wcols = written_cols(seq, p.cols, clamped);
+        const int wcols = written_cols(seq, p.cols, clamped, gm.col_stride);
         if (wcols == 0) {  // requests with no columns own no groups
             ++b;
             continue;
         }
         if (clamped && gcur == base && lane == 0 && p.errors)
             atomicAdd(p.errors, 1);
-        const int nblk = (int)(((int64_t)seq + kBlockTokens - 1) / kBlockTokens);
+        const int nblk = key_columns(seq, gm);
         const int64_t row_base = (int64_t)b * rows;
         const int64_t g_end_b = base + wcols / kUnit;
         const int c_stop = (int)((min(g_hi, g_end_b) - base) * kUnit);
@@ -465,7 +531,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
                 qraw[n] = load_row_slice(p.q + (row_base + rho) * kDim, g);
         }
         int c_end = min(c + kChunk, c_stop);
-        WindowPages wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane);
+        WindowPages wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane, gm.col_shift);
         Bf16Slice qb[NT];
         int pos[NT];
 #pragma unroll
@@ -474,13 +540,13 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
             qb[n] = to_bf16(qraw[n]);
         }
         while (true) {
-            score_window<NT, kParts, kDeviceScope, kUnit>(p, b, seq, nblk, c, c_end, wp, qb, pos, tile, res, lane, r16,
-                                     g);
+            score_window<NT, kParts, kDeviceScope, kUnit>(p, gm, b, seq, nblk, c, c_end, wp, qb,
+                                                          pos, tile, res, lane, r16, g);
             c = c_end;
             if (c >= c_stop)
                 break;
             c_end = min(c + kChunk, c_stop);
-            wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane);
+            wp = load_window_pages(p, b, c, min(c_end, nblk) - 1, lane, gm.col_shift);
         }
         segment_done(b, c_first, c_stop);
         gcur = min(g_hi, g_end_b);
@@ -489,13 +555,13 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     }
 }
 
-template <int NT, int kParts, int kWavesPerEU, int kUnit>
+template <int NT, int kParts, int kWavesPerEU, int kUnit, bool kSharded>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_decode_kernel(ScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];  // block maxima of a window
-    score_wave_range<NT, kParts, false, kUnit>(p, tile, res, [](int, int, int) {});
+    score_wave_range<NT, kParts, false, kUnit, kSharded>(p, tile, res, [](int, int, int) {});
 }
 
 // Waits until the produced-column count in the low 16 bits of *ctr reaches
@@ -557,7 +623,7 @@ void score_select_kernel(ScoreSelectParams q)
     const int R = q.num_ranges;
     const int w = q.width;
 
-    score_wave_range<NT, kParts, true, 4>(p, tile, res, [&](int b, int c_begin, int c_end) {
+    score_wave_range<NT, kParts, true, 4, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (lane == 0) {
             for (int r = c_begin / w; r * w < c_end; ++r) {
@@ -594,8 +660,9 @@ void score_select_kernel(ScoreSelectParams q)
         }
         float sv[V];
         topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
-        topk::select_loaded<V>(sv, lo, min(hi, n), n, q.init_blocks, q.local_blocks, q.out + job,
-                               lane, cand);
+        topk::select_loaded<V>(sv, lo, hi,
+                               topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
+                               q.out + job, lane, cand);
         if (lane == 0) {
             const int old = atomicAdd(ctr, 1 << 16);
             if ((old >> 16) == rows - 1)
@@ -622,7 +689,15 @@ template <int NT>
 const void* score_kernel_fn()
 {
     constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
-    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4>);
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, false>);
+}
+
+// Row-sharded cache: one rank's share, streaming grid.
+template <int NT>
+const void* score_sharded_kernel_fn()
+{
+    constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, true>);
 }
 
 // Small batches: one column per work unit and a whole block per DMA round
@@ -632,7 +707,7 @@ template <int NT>
 const void* score_latency_kernel_fn()
 {
     return reinterpret_cast<const void*>(
-        &score_decode_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, 1>);
+        &score_decode_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, 1, false>);
 }
 
 template <int NT, int V>
@@ -691,6 +766,10 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
 {
     void* args[] = {const_cast<ScoreParams*>(&p)};
     const bool small_q = p.dql * kHeads <= 16;
+    if (p.world_size > 1) {
+        const void* fn = small_q ? score_sharded_kernel_fn<1>() : score_sharded_kernel_fn<2>();
+        return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
+    }
     const int64_t max_cols = (int64_t)p.batch * p.cols;
     const int64_t latency_waves = (int64_t)device_cus() * 4 * MSA_SCORE_LATENCY_WAVES_PER_SIMD;
     if (max_cols <= latency_waves) {
@@ -760,6 +839,10 @@ hipError_t warmup_score_kernels()
     hipError_t e = hipFuncGetAttributes(&attr, score_kernel_fn<1>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_kernel_fn<2>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<1>());
     if (e == hipSuccess)

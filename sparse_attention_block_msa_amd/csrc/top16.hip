@@ -44,16 +44,20 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
     float sv[V];
     load_span<V>(p.scores + th * p.cols, p.cols, span_lo, lane, sv);
 
+    // valid global ids: [0, n); the largest this plane can name is
+    // index_scale * (cols - 1) + index_offset
+    const int64_t n_max = (int64_t)p.index_scale * p.cols + p.index_offset;
     int n = p.nvp[t];
-    if (n < 0 || n > p.cols) {
+    if (n < 0 || n > n_max) {
         if (r == 0 && (th % kHeads) == 0 && threadIdx.x == 0 && p.errors)
             atomicAdd(p.errors, 1);
-        n = n < 0 ? 0 : p.cols;
+        n = n < 0 ? 0 : (int)n_max;
     }
     const int hi = min(lo + p.width, p.cols);
-    const int vhi = min(hi, n);
+    const ColumnIds ci = column_ids(n, p.init_blocks, p.local_blocks, p.index_scale,
+                                    p.index_offset);
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
-    select_loaded<V>(sv, span_lo, vhi, n, p.init_blocks, p.local_blocks, dst, lane, cand[wave]);
+    select_loaded<V>(sv, span_lo, hi, ci, dst, lane, cand[wave]);
 
     if (NW > 1) {
         __syncthreads();
@@ -129,6 +133,110 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 }
 
+// Merge of partial rows in any order, an id possibly in several of them
+// (rows from ranks that each hold part of every page's rows): one wave per
+// (token, head). The row's R * 16 entries go to LDS as 64-bit keys
+// (id << 32 | ~rank key of the score) with their position in the
+// concatenated rows and the raw score alongside, and a bitonic network sorts
+// them by (key, position), so each id's entries are adjacent with its highest
+// score first (the earliest of equal ones, e.g. -0 and +0). The first entry
+// of each id is kept (the
+// merge of row shards keeps an id's highest partial score: a block's max over
+// its rows is the max over the shards of their maxima). The select then runs
+// over the sorted entries, whose element order is id order. Forced ids are
+// recomputed over [0, n); one missing from the union is counted.
+template <int V>
+__global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
+{
+    constexpr int kN = 64 * V;
+    __shared__ uint64_t key[kN];
+    __shared__ uint32_t raw[kN];
+    __shared__ uint32_t at[kN];  // position in the concatenated rows
+    __shared__ Candidate cand[64];
+    const int lane = threadIdx.x;
+    const int64_t th = blockIdx.x;  // t * 4 + h
+    const int t = (int)(th / kHeads);
+    const int total = p.num_ranges * kTop;
+    const msa_top16_row* rows = p.partial + th * p.num_ranges;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = i * 64 + lane;
+        const int ec = min(e, total - 1);
+        int id = rows[ec / kTop].id[ec % kTop];
+        float sc = rows[ec / kTop].score[ec % kTop];
+        if (e >= total || id < 0) {
+            id = 0x7FFFFFFF;  // sorts after every real id; dropped below
+            sc = -INFINITY;
+        }
+        key[e] = ((uint64_t)(uint32_t)id << 32) | (uint64_t)(~order_key(sc));
+        raw[e] = __float_as_uint(sc);
+        at[e] = (uint32_t)e;
+    }
+    const int n = max(0, p.nvp[t]);
+    for (int k = 2; k <= kN; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int e = i * 64 + lane;
+                const int f = e ^ j;
+                if (f > e) {
+                    const uint64_t a = key[e];
+                    const uint64_t b = key[f];
+                    const uint32_t pa = at[e];
+                    const uint32_t pb = at[f];
+                    const bool a_after_b = a > b || (a == b && pa > pb);
+                    const bool up = (e & k) == 0;
+                    if (up == a_after_b) {
+                        key[e] = b;
+                        key[f] = a;
+                        at[e] = pb;
+                        at[f] = pa;
+                        const uint32_t ra = raw[e];
+                        raw[e] = raw[f];
+                        raw[f] = ra;
+                    }
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    float sv[V];
+    int iv[V];
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    int n_forced = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = i * 64 + lane;
+        const int id = (int)(key[e] >> 32);
+        const int prev = e > 0 ? (int)(key[e - 1] >> 32) : -1;
+        const bool kept = id != 0x7FFFFFFF && id != prev;
+        sv[i] = __uint_as_float(raw[e]);
+        iv[i] = id;
+        const bool forced = kept && is_forced(id, n, p.init_blocks, p.local_blocks);
+        u[i] = kept && !forced ? order_key(sv[i]) : 0u;
+        fbits |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+    const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
+    if (n_forced < expected_forced && lane == 0 && p.errors)
+        atomicAdd(p.errors, 1);
+    msa_top16_row* dst = p.out + th;
+    const int kept = select_row<V>(u, sv, fbits, kTop - expected_forced, count_keys<V>(u), lane,
+                                   cand, [&](int i) { return iv[i]; },
+                                   [&](float score, int id, int slot) {
+                                       dst->score[slot] = score;
+                                       dst->id[slot] = id;
+                                   });
+    pad_row(dst, kept, lane);
+}
+
 // Select over R ranges and merge, one (token, head) row per workgroup: wave
 // r selects range r exactly as top16_select_kernel does with one wave per
 // range, writes its row to `partial` (when given) and to LDS, and wave 0 then
@@ -153,9 +261,10 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
             atomicAdd(p.errors, 1);
         n = n < 0 ? 0 : p.cols;
     }
-    const int vhi = min(min(lo + p.width, p.cols), n);
     msa_top16_row* mine = &part[r];
-    select_loaded<V>(sv, lo, vhi, n, p.init_blocks, p.local_blocks, mine, lane, cand[r]);
+    select_loaded<V>(sv, lo, min(lo + p.width, p.cols), column_ids(n, p.init_blocks,
+                                                                  p.local_blocks, 1, 0),
+                     mine, lane, cand[r]);
     __syncthreads();
     if (p.partial && lane < 2 * kTop)
         reinterpret_cast<int*>(p.partial + th * p.num_ranges + r)[lane] =
@@ -263,6 +372,17 @@ hipError_t launch_top16_merge(const MergeParams& p, hipStream_t stream)
     return hipErrorInvalidValue;
 }
 
+#define MSA_FOR_EACH_DEDUP_SHAPE(X) X(1) X(2) X(4) X(8) X(16)
+
+template <int V>
+hipError_t launch_dedup_shape(const MergeParams& p, hipStream_t stream)
+{
+    void* args[] = {const_cast<MergeParams*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_merge_dedup_kernel<V>),
+                           dim3((unsigned)((int64_t)p.num_tokens * kHeads)), dim3(64), args, 0,
+                           stream);
+}
+
 template <int V, int VM>
 hipError_t launch_fused_shape(const SelectMergeParams& p, hipStream_t stream)
 {
@@ -292,6 +412,20 @@ hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t str
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_top16_merge_dedup(const MergeParams& p, hipStream_t stream)
+{
+    // one wave; 64 * V >= R * 16 entries (R <= 64)
+    int v = 1;
+    while (v * 64 < p.num_ranges * kTop)
+        v *= 2;
+#define X(V)        \
+    if (v == V)     \
+        return launch_dedup_shape<V>(p, stream);
+    MSA_FOR_EACH_DEDUP_SHAPE(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
 hipError_t warmup_top16_kernels()
 {
     hipFuncAttributes attr;
@@ -308,6 +442,11 @@ hipError_t warmup_top16_kernels()
         e = hipFuncGetAttributes(&attr,                                                        \
                                  reinterpret_cast<const void*>(&top16_select_merge_kernel<V, VM>));
     MSA_FOR_EACH_FUSED_SHAPE(X)
+#undef X
+#define X(V)                                                                                      \
+    if (e == hipSuccess)                                                                          \
+        e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_merge_dedup_kernel<V>));
+    MSA_FOR_EACH_DEDUP_SHAPE(X)
 #undef X
     return e;
 }

@@ -259,25 +259,53 @@ __device__ __forceinline__ void load_span(const float* srow, int cols, int span_
     }
 }
 
-// Selects over a span loaded by load_span. Valid ids are those below vhi;
-// forced ids follow (n, init, local). The candidate budget is 16 minus the
-// forced ids found in the span. Writes the kept entries and the padding to
-// dst and returns the number kept.
-template <int V>
-__device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, int vhi, int n,
-                                             int init_blocks, int local_blocks,
-                                             msa_top16_row* dst, int lane, Candidate* buf)
+// Column c of a select row stands for global block id scale * c + offset
+// (scale 1, offset 0 when the plane's columns are the global blocks). With n
+// valid global ids, the valid, init-forced and local-forced ids are then the
+// columns [0, valid_end), [0, init_end) and [local_begin, valid_end).
+struct ColumnIds {
+    int scale;
+    int offset;
+    int valid_end;
+    int init_end;
+    int local_begin;
+};
+
+// Smallest column whose id is >= id (0 if every column's is).
+__device__ __forceinline__ int first_column_at_least(int id, int scale, int offset)
 {
-    // Valid ids of the span: [span_lo, valid_hi) (vhi <= n). Forced ids are
-    // those of [0, init) and [n - local, n) within [0, n); both counts are
-    // interval arithmetic, so no ballots are spent on them.
-    const int valid_hi = min(vhi, span_lo + V * 64);
+    return id <= offset ? 0 : (id - offset + scale - 1) / scale;
+}
+
+__device__ __forceinline__ ColumnIds column_ids(int n, int init_blocks, int local_blocks,
+                                                int scale, int offset)
+{
+    ColumnIds ci;
+    ci.scale = scale;
+    ci.offset = offset;
+    ci.valid_end = first_column_at_least(n, scale, offset);
+    ci.init_end = first_column_at_least(min(init_blocks, n), scale, offset);
+    ci.local_begin = first_column_at_least(max(0, n - local_blocks), scale, offset);
+    return ci;
+}
+
+// Selects over a span loaded by load_span, within the column range ending at
+// hi. The candidate budget is 16 minus the forced ids found in the span.
+// Writes the kept entries (global ids) and the padding to dst and returns the
+// number kept.
+template <int V>
+__device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, int hi,
+                                             const ColumnIds& ci, msa_top16_row* dst, int lane,
+                                             Candidate* buf)
+{
+    // Valid columns of the span: [span_lo, valid_hi). Forced columns are
+    // [0, init_end) and [local_begin, valid_end); both counts are interval
+    // arithmetic, so no ballots are spent on them.
+    const int valid_hi = min(min(hi, ci.valid_end), span_lo + V * 64);
     const int n_valid = max(0, valid_hi - span_lo);
-    const int init_end = min(init_blocks, n);
-    const int local_begin = max(0, n - local_blocks);
-    const int n_init = max(0, min(valid_hi, init_end) - span_lo);
-    const int n_local = max(0, valid_hi - max(span_lo, local_begin));
-    const int n_both = max(0, min(valid_hi, init_end) - max(span_lo, local_begin));
+    const int n_init = max(0, min(valid_hi, ci.init_end) - span_lo);
+    const int n_local = max(0, valid_hi - max(span_lo, ci.local_begin));
+    const int n_both = max(0, min(valid_hi, ci.init_end) - max(span_lo, ci.local_begin));
     const int n_forced = n_init + n_local - n_both;
     uint32_t u[V];
     uint64_t fbits = 0;
@@ -288,15 +316,15 @@ __device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, 
     } else {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const int id = span_lo + i * 64 + lane;
-            const bool valid = id < valid_hi;
-            const bool forced = valid && is_forced(id, n, init_blocks, local_blocks);
+            const int c = span_lo + i * 64 + lane;
+            const bool valid = c < valid_hi;
+            const bool forced = valid && (c < ci.init_end || c >= ci.local_begin);
             u[i] = valid && !forced ? order_key(sv[i]) : 0u;
             fbits |= (uint64_t)forced << i;
         }
     }
     const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, n_valid - n_forced, lane, buf,
-                                   [&](int i) { return span_lo + i * 64 + lane; },
+                                   [&](int i) { return ci.scale * (span_lo + i * 64 + lane) + ci.offset; },
                                    [&](float score, int id, int slot) {
                                        dst->score[slot] = score;
                                        dst->id[slot] = id;

@@ -27,8 +27,10 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("msa_score_decode", "msa_score_select", "msa_top16_select", "msa_top16_merge",
-              "msa_top16_select_merge", "msa_score_columns", "msa_warmup", "msa_last_error"):
+    for n in ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
+              "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge",
+              "msa_top16_merge_dedup", "msa_top16_select_merge", "msa_score_columns",
+              "msa_warmup", "msa_last_error"):
         assert n in names
     assert set(names) == set(msa.EXPORTS)
 
@@ -220,4 +222,73 @@ def test_score_select_rejects(lib, kw, needle):
     select arguments, the fused span limit and the workspace pointer; nothing
     is launched (the pointers are never dereferenced)."""
     assert _score_select(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _score_sharded(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seq=FAKE, batch=2,
+             page_size=256, dql=1, rank=1, ws=2, out=FAKE, cols=32, errors=None, stream=None)
+    a.update(kw)
+    return lib.msa_score_decode_sharded(a["q"], a["k"], a["num_pages"], a["bt"], a["bt_stride"],
+                                        a["seq"], a["batch"], a["page_size"], a["dql"],
+                                        a["rank"], a["ws"], a["out"], a["cols"], a["errors"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(k=None), "null"),
+    (dict(page_size=64), "page_size"),
+    (dict(cols=30), "cols"),
+    (dict(ws=1), "world_size"),
+    (dict(ws=3), "world_size"),
+    (dict(ws=8), "world_size"),
+    (dict(rank=2), "rank"),
+    (dict(rank=-1), "rank"),
+])
+def test_score_decode_sharded_rejects(lib, kw, needle):
+    assert _score_sharded(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _select_mapped(lib, **kw):
+    a = dict(scores=FAKE, T=4, cols=64, nvp=FAKE, init=1, local=2, R=2, scale=2, offset=1,
+             out=FAKE, errors=None, stream=None)
+    a.update(kw)
+    return lib.msa_top16_select_mapped(a["scores"], a["T"], a["cols"], a["nvp"], a["init"],
+                                       a["local"], a["R"], a["scale"], a["offset"], a["out"],
+                                       a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(scores=None), "null"),
+    (dict(cols=0), "cols"),
+    (dict(R=65), "num_ranges"),
+    (dict(scale=0), "index_scale"),
+    (dict(offset=-1), "index_offset"),
+    (dict(cols=12000, scale=200000), "2^31"),
+    (dict(init=9, local=8), "exceeds"),
+])
+def test_select_mapped_rejects(lib, kw, needle):
+    assert _select_mapped(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _merge_dedup(lib, **kw):
+    a = dict(partial=FAKE, T=4, R=16, nvp=FAKE, init=1, local=2, out=FAKE, errors=None,
+             stream=None)
+    a.update(kw)
+    return lib.msa_top16_merge_dedup(a["partial"], a["T"], a["R"], a["nvp"], a["init"],
+                                     a["local"], a["out"], a["errors"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(partial=None), "null"),
+    (dict(T=0), "num_tokens"),
+    (dict(R=0), "num_ranges"),
+    (dict(R=65), "num_ranges"),
+    (dict(init=-1), ">= 0"),
+    (dict(out=FAKE + 2), "aligned"),
+])
+def test_merge_dedup_rejects(lib, kw, needle):
+    assert _merge_dedup(lib, **kw) == msa.MSA_ERR_INVALID_ARG
     assert needle in lib.msa_last_error().decode()
