@@ -10,7 +10,10 @@ Two fused variants of the step are timed beside it: select and merge in one
 launch (msa_top16_select_merge, per-range rows also written;
 e2e.fused_select_merge), and the plane with the per-range rows in one launch
 followed by the merge (msa_score_select -> msa_top16_merge;
-e2e.score_select_then_merge).
+e2e.score_select_then_merge). One rank's share of the same workload on a
+cache split by rows over 2 or 4 ranks (msa_score_decode_sharded ->
+msa_top16_select_mapped, then the owner's msa_top16_merge_dedup) is
+reported under e2e.sharded_rank_share.
 
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
 timing. Before every step a read pass over a 1 GiB buffer evicts index-K
@@ -229,6 +232,69 @@ def main():
         torch.cuda.synchronize()
         score_select_ms = sum(ev[0].elapsed_time(ev[1]) for ev in ss_events) / args.steps
 
+    # Timed region 1d: one rank's share of the same workload on a cache whose
+    # pages are split by rows over world_size ranks (msa_score_decode_sharded
+    # -> msa_top16_select_mapped over R ranges), and the owner's merge of all
+    # ranks' rows (msa_top16_merge_dedup), for world_size 2 and 4.
+    sharded = {}
+    if w.page_size % 128 == 0:
+        for ws_n in (2, 4):
+            rows_per_rank = w.page_size // ws_n
+            shard = workloads.shard_rows(w.index_k, 0, ws_n).to(dev)
+            scols = max(4, -(-(-(-int(w.seq_lens.max()) // w.page_size)) // 4) * 4)
+            splane = torch.empty((T, 4, scols), dtype=torch.float32, device=dev)
+            spart = msa.new_rows(T, 4, R, device=dev)
+            scale, offset = (1, 0) if w.page_size == 128 else (2, 0)
+            # rank 0 holds the positions p with p % page_size < rows_per_rank
+            rank_keys = 0
+            for sl_b in w.seq_lens.tolist():
+                full, rem = divmod(max(0, sl_b), w.page_size)
+                rank_keys += full * rows_per_rank + min(rem, rows_per_rank)
+
+            def step_rank():
+                msa.msa_score_decode_sharded(q, shard, bt, sl, splane, page_size=w.page_size,
+                                             decode_query_len=w.dql, rank=0, world_size=ws_n,
+                                             errors=errors, stream=stream)
+                msa.msa_top16_select_mapped(splane, nvp, spart, init_blocks=w.init_blocks,
+                                            local_blocks=w.local_blocks, num_ranges=R,
+                                            index_scale=scale, index_offset=offset,
+                                            errors=errors, stream=stream)
+
+            for _ in range(args.warmup):
+                step_rank()
+            ev_r = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    for _ in range(args.steps)]
+            for i in range(args.steps):
+                if not args.no_flush:
+                    flush.sum()
+                ev_r[i][0].record(stream)
+                step_rank()
+                ev_r[i][1].record(stream)
+            # owner merge of every rank's rows (rank 0's rows stand in for all)
+            all_rows = spart.repeat(1, 1, ws_n, 1).contiguous()
+            merged = msa.new_rows(T, 4, device=dev)
+            for _ in range(args.warmup):
+                msa.msa_top16_merge_dedup(all_rows, nvp, merged, init_blocks=w.init_blocks,
+                                          local_blocks=w.local_blocks, stream=stream)
+            ev_m = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    for _ in range(args.steps)]
+            for i in range(args.steps):
+                ev_m[i][0].record(stream)
+                msa.msa_top16_merge_dedup(all_rows, nvp, merged, init_blocks=w.init_blocks,
+                                          local_blocks=w.local_blocks, stream=stream)
+                ev_m[i][1].record(stream)
+            torch.cuda.synchronize()
+            rank_ms = sum(e[0].elapsed_time(e[1]) for e in ev_r) / args.steps
+            merge_ms = sum(e[0].elapsed_time(e[1]) for e in ev_m) / args.steps
+            rank_bytes = rank_keys * 128
+            sharded[f"world_size_{ws_n}"] = {
+                "rank": 0, "rank_keys": rank_keys,
+                "rank_step_ms": rank_ms,
+                "rank_hbm_gbps": rank_bytes / (rank_ms * 1e-3) / 1e9,
+                "rank_frac_of_peak": rank_bytes / (rank_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "owner_merge_ms": merge_ms, "merged_rows_per_head": ws_n * R}
+            del shard, splane, spart, all_rows, merged
+
     # Timed region 2: the same K steps with an event between every kernel,
     # for per-kernel durations (the events themselves lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -295,6 +361,7 @@ def main():
                     "hbm_gbps": launch_bytes / (score_select_ms * 1e-3) / 1e9,
                     "frac_of_peak":
                         launch_bytes / (score_select_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "sharded_rank_share": sharded or None,
                 "wall_s_all_steps_incl_flush": wall},
         "roofline": {"kernel": "score_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -133,31 +133,96 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 }
 
+// One bitonic compare-exchange of a wave-wide sort: this lane's element
+// (key, at, raw) against the partner's (okey, oat, oraw); the element keeps
+// the smaller of the two if keep_min, else the larger ((key, at) order).
+__device__ __forceinline__ void keep_one(uint64_t& key, uint32_t& at, uint32_t& raw,
+                                         uint64_t okey, uint32_t oat, uint32_t oraw,
+                                         bool keep_min)
+{
+    const bool mine_first = key < okey || (key == okey && at < oat);
+    if (mine_first != keep_min) {
+        key = okey;
+        at = oat;
+        raw = oraw;
+    }
+}
+
+// Sorts the wave's 64V elements ascending by (key, at); element i of lane l
+// is element 64i + l. Stages whose partner is 64 or more elements away swap
+// registers within a lane; nearer partners are read with cross-lane
+// shuffles. The network is fully unrolled, so every register index is a
+// compile-time constant.
+template <int V>
+__device__ __forceinline__ void bitonic_sort_wave(uint64_t (&key)[V], uint32_t (&at)[V],
+                                                  uint32_t (&raw)[V], int lane)
+{
+    constexpr int kN = 64 * V;
+#pragma unroll
+    for (int k = 2; k <= kN; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j >= 64) {
+                constexpr int kLaneBits = 6;
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const int i2 = i ^ (j >> kLaneBits);
+                    if (i2 > i) {
+                        const bool up = ((i * 64) & k) == 0;  // k >= 128: lane bits don't matter
+                        uint64_t ka = key[i], kb = key[i2];
+                        uint32_t aa = at[i], ab = at[i2], ra = raw[i], rb = raw[i2];
+                        const bool a_first = ka < kb || (ka == kb && aa < ab);
+                        if (a_first != up) {  // the lower slot keeps the min when up
+                            key[i] = kb;
+                            key[i2] = ka;
+                            at[i] = ab;
+                            at[i2] = aa;
+                            raw[i] = rb;
+                            raw[i2] = ra;
+                        }
+                    }
+                }
+            } else {
+                const bool lower = (lane & j) == 0;
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const int e = i * 64 + lane;
+                    const bool up = (e & k) == 0;
+                    const uint32_t klo = (uint32_t)key[i], khi = (uint32_t)(key[i] >> 32);
+                    const uint64_t okey = ((uint64_t)(uint32_t)__shfl_xor((int)khi, j) << 32) |
+                                          (uint32_t)__shfl_xor((int)klo, j);
+                    const uint32_t oat = (uint32_t)__shfl_xor((int)at[i], j);
+                    const uint32_t oraw = (uint32_t)__shfl_xor((int)raw[i], j);
+                    keep_one(key[i], at[i], raw[i], okey, oat, oraw, lower == up);
+                }
+            }
+        }
+    }
+}
+
 // Merge of partial rows in any order, an id possibly in several of them
 // (rows from ranks that each hold part of every page's rows): one wave per
-// (token, head). The row's R * 16 entries go to LDS as 64-bit keys
+// (token, head). The row's R * 16 entries become 64-bit keys
 // (id << 32 | ~rank key of the score) with their position in the
-// concatenated rows and the raw score alongside, and a bitonic network sorts
-// them by (key, position), so each id's entries are adjacent with its highest
-// score first (the earliest of equal ones, e.g. -0 and +0). The first entry
-// of each id is kept (the
-// merge of row shards keeps an id's highest partial score: a block's max over
-// its rows is the max over the shards of their maxima). The select then runs
-// over the sorted entries, whose element order is id order. Forced ids are
-// recomputed over [0, n); one missing from the union is counted.
+// concatenated rows and the raw score alongside, and a wave-wide bitonic
+// network sorts them by (key, position), so each id's entries are adjacent
+// with its highest score first (the earliest of equal ones, e.g. -0 and +0).
+// The first entry of each id is kept (the merge of row shards keeps an id's
+// highest partial score: a block's max over its rows is the max over the
+// shards of their maxima). The select then runs over the sorted entries,
+// whose element order is id order. Forced ids are recomputed over [0, n);
+// one missing from the union is counted.
 template <int V>
 __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
 {
-    constexpr int kN = 64 * V;
-    __shared__ uint64_t key[kN];
-    __shared__ uint32_t raw[kN];
-    __shared__ uint32_t at[kN];  // position in the concatenated rows
     __shared__ Candidate cand[64];
     const int lane = threadIdx.x;
     const int64_t th = blockIdx.x;  // t * 4 + h
     const int t = (int)(th / kHeads);
     const int total = p.num_ranges * kTop;
     const msa_top16_row* rows = p.partial + th * p.num_ranges;
+    uint64_t key[V];
+    uint32_t at[V], raw[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int e = i * 64 + lane;
@@ -168,43 +233,12 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
             id = 0x7FFFFFFF;  // sorts after every real id; dropped below
             sc = -INFINITY;
         }
-        key[e] = ((uint64_t)(uint32_t)id << 32) | (uint64_t)(~order_key(sc));
-        raw[e] = __float_as_uint(sc);
-        at[e] = (uint32_t)e;
+        key[i] = ((uint64_t)(uint32_t)id << 32) | (uint64_t)(~order_key(sc));
+        at[i] = (uint32_t)e;
+        raw[i] = __float_as_uint(sc);
     }
     const int n = max(0, p.nvp[t]);
-    for (int k = 2; k <= kN; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const int e = i * 64 + lane;
-                const int f = e ^ j;
-                if (f > e) {
-                    const uint64_t a = key[e];
-                    const uint64_t b = key[f];
-                    const uint32_t pa = at[e];
-                    const uint32_t pb = at[f];
-                    const bool a_after_b = a > b || (a == b && pa > pb);
-                    const bool up = (e & k) == 0;
-                    if (up == a_after_b) {
-                        key[e] = b;
-                        key[f] = a;
-                        at[e] = pb;
-                        at[f] = pa;
-                        const uint32_t ra = raw[e];
-                        raw[e] = raw[f];
-                        raw[f] = ra;
-                    }
-                }
-            }
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bitonic_sort_wave<V>(key, at, raw, lane);
 
     float sv[V];
     int iv[V];
@@ -213,11 +247,19 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
     int n_forced = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int e = i * 64 + lane;
-        const int id = (int)(key[e] >> 32);
-        const int prev = e > 0 ? (int)(key[e - 1] >> 32) : -1;
+        const int id = (int)(key[i] >> 32);
+        // the previous element (64i + lane - 1) is lane - 1's slot i, or lane
+        // 63's slot i - 1
+        const int up_id = __shfl_up(id, 1);
+        int prev = up_id;
+        if (i > 0) {
+            const int last = __shfl((int)(key[i - 1] >> 32), 63);
+            prev = lane == 0 ? last : up_id;
+        } else if (lane == 0) {
+            prev = -1;
+        }
         const bool kept = id != 0x7FFFFFFF && id != prev;
-        sv[i] = __uint_as_float(raw[e]);
+        sv[i] = __uint_as_float(raw[i]);
         iv[i] = id;
         const bool forced = kept && is_forced(id, n, p.init_blocks, p.local_blocks);
         u[i] = kept && !forced ? order_key(sv[i]) : 0u;
