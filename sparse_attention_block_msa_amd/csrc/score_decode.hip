@@ -1,4 +1,4 @@
-// Score-plane kernel for gfx950.
+// Score-plane kernels for gfx950.
 //
 // Operation ("flashinfer.msa_ops.msa_icp_decode_index_score_sharded",
 // description and parameters): for each request b, decode token j and index
@@ -6,23 +6,27 @@
 //   plane[(b*dql + j), h, c] = max over keys p of block c with p < seq_len and
 //                              p <= seq_len - dql + j of  q[b*dql + j, h, :] . k[p, :]
 // (-inf if the block has no such key). Columns are written up to the request's
-// block count rounded up to a multiple of four and no further.
+// block count rounded up to a multiple of four and no further. On a cache
+// whose pages are split by rows over ranks, a rank's column is a page of its
+// row shard instead (ColumnGeometry below).
 //
 // Design (one wave = 64 lanes per workgroup):
-//  * A fixed grid of waves splits all requests' plane columns into equal
-//    contiguous ranges (see score_decode_kernel). A wave converts the Q tile
-//    of the request it is in (4*dql <= 32 rows of 128 fp8 bytes) to bf16
-//    once and keeps it in registers as the B operand of the MFMA.
+//  * Work split: a fixed grid of waves (a whole number per SIMD) cuts all
+//    requests' written columns, laid end to end, into equal contiguous ranges
+//    of 4-column groups (score_wave_range). A wave converts the Q tile of the
+//    request it is in (4*dql <= 32 rows of 128 fp8 bytes) to bf16 once and
+//    keeps it in registers as the B operand of the MFMA. Small batches use
+//    single columns as the unit instead (latency mode).
 //  * A B128 block is 128 keys x 128 bytes = 16 KiB, contiguous inside one
 //    page. It is staged through a per-wave 4 KiB LDS tile in four pieces of
-//    32 keys with global_load_lds_dwordx4: each DMA instruction moves 1 KiB
-//    of whole 128-byte rows (a fully contiguous, non-temporal read), and the
-//    per-lane source addresses are chosen so the tile lands XOR-swizzled,
-//    letting the MFMA-layout ds_read_b128s hit every LDS bank once. Loads
-//    never occupy VGPRs. (Loading the MFMA layout straight into
-//    registers needs half-row 64-byte accesses per instruction; measured on
-//    MI355X, that pattern streams at about 5.2 TB/s against 6.5 TB/s for
-//    whole-row DMA.)
+//    32 keys with global_load_lds_dwordx4 (latency mode: one 16 KiB piece):
+//    each DMA instruction moves 1 KiB of whole 128-byte rows (a fully
+//    contiguous, non-temporal read), and the per-lane source addresses are
+//    chosen so the tile lands XOR-swizzled, letting the MFMA-layout
+//    ds_read_b128s hit every LDS bank once. Loads never occupy VGPRs.
+//    (Loading the MFMA layout straight into registers needs half-row 64-byte
+//    accesses per instruction; measured on MI355X, that pattern streams at
+//    about 5.2 TB/s against 6.5 TB/s for whole-row DMA.)
 //  * Contraction: every e4m3fn value is exactly a bf16 value, so each key
 //    tile is converted with v_cvt_scalef32_pk_bf16_fp8 (scale 1.0, two values
 //    per instruction) and contracted with v_mfma_f32_16x16x32_bf16, four
@@ -37,9 +41,11 @@
 //    row l%16, so the block max is a per-lane max over 8 tiles x 4 values
 //    followed by a max across the four 16-lane groups. The causal mask is
 //    applied only in blocks that reach past the first token's position.
-//  * The chunk's block maxima collect in a small per-wave LDS array and are
-//    stored to the plane (64 contiguous bytes per query row) only when the
-//    chunk is done, so no DMA wait ever waits on a plane store.
+//  * A window's (<= 16 columns) block maxima collect in a small per-wave LDS
+//    array and are stored to the plane only when the window is done, so no
+//    DMA wait ever waits on a plane store.
+//  * score_select_kernel runs the same scoring and then the per-range Top16
+//    select in the same launch (see its comment).
 //
 // Byte order inside a lane's operands: the 32 bytes a lane supplies per row
 // are bytes [16g, 16g+16) and [64+16g, 64+16g+16) of the 128-byte row
