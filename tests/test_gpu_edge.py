@@ -295,3 +295,13 @@ def test_select_merge_fused(cols, R, init, local, kind, with_partial):
         pc = part.cpu()
         assert_rows_equal(msa.row_scores(pc).numpy(), msa.row_ids(pc).numpy(), os_, oi,
                           f"fused ranges cols={cols} R={R} {kind}")
+
+
+def test_scorer_large_batch():
+    """5000 short requests: the streaming grid's two-pass request search runs
+    over 79 chunks of 64 requests; the plane matches the oracle everywhere."""
+    w = workloads.generate(batch=5000, seq=("loguniform", 1, 3000), page_size=128, dql=2,
+                           seed=91)
+    got, err = run_scorer(w, w.cols, extra=4)
+    assert err == 0
+    check_plane(w, got, w.cols + 4)

@@ -314,3 +314,15 @@ def test_merge_dedup_equal_duplicates_keep_earliest():
     o = out.cpu()
     assert_rows_equal(msa.row_scores(o).numpy(), msa.row_ids(o).numpy(), rs, ri, "zeros")
     assert np.float32(rs[0, 0, 0]).view(np.uint32) == np.float32(-0.0).view(np.uint32)
+
+
+@pytest.mark.parametrize("page_size,ws", [(128, 4), (256, 2)])
+def test_sharded_plane_batch_above_64(page_size, ws):
+    """Batches above 64 take the two-pass request search."""
+    w = workloads.generate(batch=300, seq=("loguniform", 1, 9000), page_size=page_size, dql=3,
+                           seed=502 + ws)
+    cols = sharded_cols(w) + 4
+    for rank in (0, ws - 1):
+        got, err = gpu_plane_sharded(w, rank, ws, cols)
+        assert err == 0
+        check_rank_plane(w, rank, ws, got.cpu().numpy(), cols)
