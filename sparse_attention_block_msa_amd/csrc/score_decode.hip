@@ -723,38 +723,41 @@ const void* score_select_kernel_fn()
     return reinterpret_cast<const void*>(&score_select_kernel<NT, kParts, kRegWaves, V>);
 }
 
-// Compute units of the current device (host query, cached per device).
+// Compute units of the current device (host query, cached per device; the
+// cache is safe to fill from several host threads at once).
 int device_cus()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Ticks of the device's constant-rate clock (s_memrealtime) in 2 seconds.
 int64_t spin_ticks_2s()
 {
-    static int64_t cached[64] = {0};
+    static std::atomic<int64_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 200000000;  // 100 MHz
-    if (cached[dev] == 0) {
+    int64_t ticks = cached[dev].load(std::memory_order_relaxed);
+    if (ticks == 0) {
         int khz = 0;
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
             khz <= 0)
             khz = 100000;
-        cached[dev] = (int64_t)khz * 2000;
+        ticks = (int64_t)khz * 2000;
+        cached[dev].store(ticks, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return ticks;
 }
 
 // Scorer grid: one wave per workgroup, a whole number of waves per SIMD, no

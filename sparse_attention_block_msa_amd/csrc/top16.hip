@@ -133,67 +133,70 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 }
 
-// One bitonic compare-exchange of a wave-wide sort: this lane's element
-// (key, at, raw) against the partner's (okey, oat, oraw); the element keeps
-// the smaller of the two if keep_min, else the larger ((key, at) order).
-__device__ __forceinline__ void keep_one(uint64_t& key, uint32_t& at, uint32_t& raw,
-                                         uint64_t okey, uint32_t oat, uint32_t oraw,
-                                         bool keep_min)
+// Inverse of order_key, up to the sign of zero (order_key maps -0 to +0).
+__device__ __forceinline__ uint32_t key_to_bits(uint32_t k)
 {
-    const bool mine_first = key < okey || (key == okey && at < oat);
-    if (mine_first != keep_min) {
-        key = okey;
-        at = oat;
-        raw = oraw;
-    }
+    return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
 }
 
-// Sorts the wave's 64V elements ascending by (key, at); element i of lane l
-// is element 64i + l. Stages whose partner is 64 or more elements away swap
-// registers within a lane; nearer partners are read with cross-lane
-// shuffles. The network is fully unrolled, so every register index is a
+// Sort element of the duplicate-aware merge: hi = id (0x7FFFFFFF for an
+// empty slot), lo = ~order_key(score), tag = position in the concatenated
+// rows (low 16 bits) | 0x80000000 if the score is -0. Ordered by
+// (hi, lo, position): ascending id, then score descending, then earliest.
+struct SortEl {
+    uint32_t hi, lo, tag;
+};
+
+__device__ __forceinline__ bool sort_before(const SortEl& a, const SortEl& b)
+{
+    if (a.hi != b.hi)
+        return a.hi < b.hi;
+    if (a.lo != b.lo)
+        return a.lo < b.lo;
+    return (a.tag & 0xFFFFu) < (b.tag & 0xFFFFu);
+}
+
+// Sorts the wave's 64V elements by sort_before. Element e = V * lane + i sits
+// in slot i of `lane` (lane-major), so stages whose partner is fewer than V
+// elements away swap registers within a lane and only the stages with
+// partners V or more apart read the partner lane (three shuffles per
+// element). The network is fully unrolled, so every register index is a
 // compile-time constant.
 template <int V>
-__device__ __forceinline__ void bitonic_sort_wave(uint64_t (&key)[V], uint32_t (&at)[V],
-                                                  uint32_t (&raw)[V], int lane)
+__device__ __forceinline__ void bitonic_sort_wave(SortEl (&el)[V], int lane)
 {
     constexpr int kN = 64 * V;
 #pragma unroll
     for (int k = 2; k <= kN; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j >= 64) {
-                constexpr int kLaneBits = 6;
+            if (j < V) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
-                    const int i2 = i ^ (j >> kLaneBits);
+                    const int i2 = i ^ j;
                     if (i2 > i) {
-                        const bool up = ((i * 64) & k) == 0;  // k >= 128: lane bits don't matter
-                        uint64_t ka = key[i], kb = key[i2];
-                        uint32_t aa = at[i], ab = at[i2], ra = raw[i], rb = raw[i2];
-                        const bool a_first = ka < kb || (ka == kb && aa < ab);
-                        if (a_first != up) {  // the lower slot keeps the min when up
-                            key[i] = kb;
-                            key[i2] = ka;
-                            at[i] = ab;
-                            at[i2] = aa;
-                            raw[i] = rb;
-                            raw[i2] = ra;
+                        const bool up = ((V * lane + i) & k) == 0;
+                        if (sort_before(el[i2], el[i]) == up) {
+                            const SortEl t = el[i];
+                            el[i] = el[i2];
+                            el[i2] = t;
                         }
                     }
                 }
             } else {
-                const bool lower = (lane & j) == 0;
+                const int lj = j / V;  // partner lane distance
+                const bool lower = (lane & lj) == 0;
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
-                    const int e = i * 64 + lane;
-                    const bool up = (e & k) == 0;
-                    const uint32_t klo = (uint32_t)key[i], khi = (uint32_t)(key[i] >> 32);
-                    const uint64_t okey = ((uint64_t)(uint32_t)__shfl_xor((int)khi, j) << 32) |
-                                          (uint32_t)__shfl_xor((int)klo, j);
-                    const uint32_t oat = (uint32_t)__shfl_xor((int)at[i], j);
-                    const uint32_t oraw = (uint32_t)__shfl_xor((int)raw[i], j);
-                    keep_one(key[i], at[i], raw[i], okey, oat, oraw, lower == up);
+                    const bool up = ((V * lane + i) & k) == 0;
+                    SortEl o;
+                    o.hi = (uint32_t)__shfl_xor((int)el[i].hi, lj);
+                    o.lo = (uint32_t)__shfl_xor((int)el[i].lo, lj);
+                    o.tag = (uint32_t)__shfl_xor((int)el[i].tag, lj);
+                    // the lower element keeps the min when up, the max otherwise
+                    const bool keep_min = lower == up;
+                    if (sort_before(o, el[i]) == keep_min)
+                        el[i] = o;
                 }
             }
         }
@@ -202,30 +205,31 @@ __device__ __forceinline__ void bitonic_sort_wave(uint64_t (&key)[V], uint32_t (
 
 // Merge of partial rows in any order, an id possibly in several of them
 // (rows from ranks that each hold part of every page's rows): one wave per
-// (token, head). The row's R * 16 entries become 64-bit keys
-// (id << 32 | ~rank key of the score) with their position in the
-// concatenated rows and the raw score alongside, and a wave-wide bitonic
-// network sorts them by (key, position), so each id's entries are adjacent
-// with its highest score first (the earliest of equal ones, e.g. -0 and +0).
-// The first entry of each id is kept (the merge of row shards keeps an id's
-// highest partial score: a block's max over its rows is the max over the
-// shards of their maxima). The select then runs over the sorted entries,
-// whose element order is id order. Forced ids are recomputed over [0, n);
-// one missing from the union is counted.
+// (token, head). The row's R * 16 entries are sorted by (id ascending, score
+// descending, position) with a wave-wide bitonic network in registers, so
+// each id's entries are adjacent with its highest score first (the earliest
+// of equal ones, e.g. -0 and +0). The first entry of each id is kept (the
+// merge of row shards keeps an id's highest partial score: a block's max over
+// its rows is the max over the shards of their maxima). The kept entries go
+// through LDS into the select's element order (element i of lane l is sorted
+// position 64i + l, so element order is id order) and the usual selection
+// runs. Forced ids are recomputed over [0, n); one missing from the union is
+// counted.
 template <int V>
 __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
 {
+    __shared__ uint32_t sid[64 * V];
+    __shared__ uint32_t sraw[64 * V];
     __shared__ Candidate cand[64];
     const int lane = threadIdx.x;
     const int64_t th = blockIdx.x;  // t * 4 + h
     const int t = (int)(th / kHeads);
     const int total = p.num_ranges * kTop;
     const msa_top16_row* rows = p.partial + th * p.num_ranges;
-    uint64_t key[V];
-    uint32_t at[V], raw[V];
+    SortEl el[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int e = i * 64 + lane;
+        const int e = V * lane + i;
         const int ec = min(e, total - 1);
         int id = rows[ec / kTop].id[ec % kTop];
         float sc = rows[ec / kTop].score[ec % kTop];
@@ -233,12 +237,27 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
             id = 0x7FFFFFFF;  // sorts after every real id; dropped below
             sc = -INFINITY;
         }
-        key[i] = ((uint64_t)(uint32_t)id << 32) | (uint64_t)(~order_key(sc));
-        at[i] = (uint32_t)e;
-        raw[i] = __float_as_uint(sc);
+        el[i].hi = (uint32_t)id;
+        el[i].lo = ~order_key(sc);
+        el[i].tag = (uint32_t)e | (__float_as_uint(sc) == 0x80000000u ? 0x80000000u : 0u);
     }
     const int n = max(0, p.nvp[t]);
-    bitonic_sort_wave<V>(key, at, raw, lane);
+    bitonic_sort_wave<V>(el, lane);
+
+    // drop repeated ids (the previous element is slot i - 1, or the previous
+    // lane's last slot) and hand the survivors to the select's layout
+    const uint32_t prev_lane_last = (uint32_t)__shfl_up((int)el[V - 1].hi, 1);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const uint32_t prev = i > 0 ? el[i - 1].hi : (lane > 0 ? prev_lane_last : 0xFFFFFFFFu);
+        const bool kept = el[i].hi != 0x7FFFFFFFu && el[i].hi != prev;
+        const uint32_t bits = (el[i].tag & 0x80000000u) ? 0x80000000u : key_to_bits(~el[i].lo);
+        sid[V * lane + i] = kept ? el[i].hi : 0xFFFFFFFFu;
+        sraw[V * lane + i] = bits;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     float sv[V];
     int iv[V];
@@ -247,21 +266,11 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
     int n_forced = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int id = (int)(key[i] >> 32);
-        // the previous element (64i + lane - 1) is lane - 1's slot i, or lane
-        // 63's slot i - 1
-        const int up_id = __shfl_up(id, 1);
-        int prev = up_id;
-        if (i > 0) {
-            const int last = __shfl((int)(key[i - 1] >> 32), 63);
-            prev = lane == 0 ? last : up_id;
-        } else if (lane == 0) {
-            prev = -1;
-        }
-        const bool kept = id != 0x7FFFFFFF && id != prev;
-        sv[i] = __uint_as_float(raw[i]);
-        iv[i] = id;
-        const bool forced = kept && is_forced(id, n, p.init_blocks, p.local_blocks);
+        const uint32_t id = sid[i * 64 + lane];
+        const bool kept = id != 0xFFFFFFFFu;
+        sv[i] = __uint_as_float(sraw[i * 64 + lane]);
+        iv[i] = (int)id;
+        const bool forced = kept && is_forced((int)id, n, p.init_blocks, p.local_blocks);
         u[i] = kept && !forced ? order_key(sv[i]) : 0u;
         fbits |= (uint64_t)forced << i;
         n_forced += __popcll(__ballot(forced));
