@@ -133,159 +133,234 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 }
 
-// Inverse of order_key, up to the sign of zero (order_key maps -0 to +0).
-__device__ __forceinline__ uint32_t key_to_bits(uint32_t k)
-{
-    return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-}
-
-// Sort element of the duplicate-aware merge: hi = id (0x7FFFFFFF for an
-// empty slot), lo = ~order_key(score), tag = position in the concatenated
-// rows (low 16 bits) | 0x80000000 if the score is -0. Ordered by
-// (hi, lo, position): ascending id, then score descending, then earliest.
-struct SortEl {
-    uint32_t hi, lo, tag;
-};
-
-__device__ __forceinline__ bool sort_before(const SortEl& a, const SortEl& b)
-{
-    if (a.hi != b.hi)
-        return a.hi < b.hi;
-    if (a.lo != b.lo)
-        return a.lo < b.lo;
-    return (a.tag & 0xFFFFu) < (b.tag & 0xFFFFu);
-}
-
-// Sorts the wave's 64V elements by sort_before. Element e = V * lane + i sits
-// in slot i of `lane` (lane-major), so stages whose partner is fewer than V
-// elements away swap registers within a lane and only the stages with
-// partners V or more apart read the partner lane (three shuffles per
-// element). The network is fully unrolled, so every register index is a
-// compile-time constant.
+// Keeps the best K of the elements with key u != 0, ranked by key
+// descending and then by lower id (ids are distinct among the candidates):
+// take[i] is set for the kept ones. The K-th largest key thr comes from a
+// bitwise descent; if more keys equal thr than are still needed, a second
+// descent over their ids finds the lowest ones.
 template <int V>
-__device__ __forceinline__ void bitonic_sort_wave(SortEl (&el)[V], int lane)
+__device__ __forceinline__ void take_best(const uint32_t (&u)[V], const int (&id)[V], int K,
+                                          bool (&take)[V])
 {
-    constexpr int kN = 64 * V;
 #pragma unroll
-    for (int k = 2; k <= kN; k <<= 1) {
+    for (int i = 0; i < V; ++i)
+        take[i] = false;
+    if (K <= 0)
+        return;
+    uint32_t prefix = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = prefix | (1u << bit);
+        int cnt = 0;
 #pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j < V) {
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                    const int i2 = i ^ j;
-                    if (i2 > i) {
-                        const bool up = ((V * lane + i) & k) == 0;
-                        if (sort_before(el[i2], el[i]) == up) {
-                            const SortEl t = el[i];
-                            el[i] = el[i2];
-                            el[i2] = t;
-                        }
-                    }
-                }
-            } else {
-                const int lj = j / V;  // partner lane distance
-                const bool lower = (lane & lj) == 0;
-#pragma unroll
-                for (int i = 0; i < V; ++i) {
-                    const bool up = ((V * lane + i) & k) == 0;
-                    SortEl o;
-                    o.hi = (uint32_t)__shfl_xor((int)el[i].hi, lj);
-                    o.lo = (uint32_t)__shfl_xor((int)el[i].lo, lj);
-                    o.tag = (uint32_t)__shfl_xor((int)el[i].tag, lj);
-                    // the lower element keeps the min when up, the max otherwise
-                    const bool keep_min = lower == up;
-                    if (sort_before(o, el[i]) == keep_min)
-                        el[i] = o;
-                }
-            }
-        }
+        for (int i = 0; i < V; ++i)
+            cnt += __popcll(__ballot(u[i] >= trial));
+        if (cnt >= K)
+            prefix = trial;
     }
+    const uint32_t thr = prefix;
+    int gt = 0, tied = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        gt += __popcll(__ballot(u[i] > thr));
+        tied += __popcll(__ballot(u[i] == thr));
+    }
+    const int need = K - gt;  // >= 1 keys equal to thr are kept
+    int cut = 0x7FFFFFFF;      // keep tied keys with id <= cut
+    if (tied > need) {
+        // the largest c with fewer than `need` tied ids below it: the
+        // need-th smallest tied id is then c itself
+        int c = 0;
+        for (int bit = 30; bit >= 0; --bit) {
+            const int trial = c | (1 << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                cnt += __popcll(__ballot(u[i] == thr && id[i] < trial));
+            if (cnt < need)
+                c = trial;
+        }
+        cut = c;
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        take[i] = u[i] != 0u && (u[i] > thr || (u[i] == thr && id[i] <= cut));
+}
+
+template <int kSlots>
+__device__ __forceinline__ int slot_of(int id)
+{
+    static_assert((kSlots & (kSlots - 1)) == 0, "power of two");
+    constexpr int kBits = __builtin_ctz(kSlots);
+    return (int)(((uint32_t)id * 2654435761u) >> (32 - kBits));  // Fibonacci hashing
 }
 
 // Merge of partial rows in any order, an id possibly in several of them
 // (rows from ranks that each hold part of every page's rows): one wave per
-// (token, head). The row's R * 16 entries are sorted by (id ascending, score
-// descending, position) with a wave-wide bitonic network in registers, so
-// each id's entries are adjacent with its highest score first (the earliest
-// of equal ones, e.g. -0 and +0). The first entry of each id is kept (the
-// merge of row shards keeps an id's highest partial score: a block's max over
-// its rows is the max over the shards of their maxima). The kept entries go
-// through LDS into the select's element order (element i of lane l is sorted
-// position 64i + l, so element order is id order) and the usual selection
-// runs. Forced ids are recomputed over [0, n); one missing from the union is
-// counted.
+// (token, head), 64V >= R * 16 entries, element i of lane l is entry 64i + l
+// of the concatenated rows.
+//  * Each id's best entry (highest score, the earliest of equal ones such as
+//    -0 and +0) is found with an LDS hash table: a compare-and-swap claims
+//    the id's slot, and a 64-bit atomic max keeps (rank key, -position).
+//    The merge of row shards keeps an id's highest partial score: a block's
+//    max over its rows is the max over the shards of their maxima.
+//  * Forced ids are recomputed over [0, n) and kept; one missing from the
+//    union is counted. The other best entries compete by (score descending,
+//    id ascending) for 16 - |forced of [0, n)| slots: the keys at or above
+//    the K-th largest lane maximum (at most 64, else all of them) go through
+//    take_best.
+//  * The kept entries (at most 16) are written by ascending id: each finds
+//    its slot by counting the kept ids below its own.
 template <int V>
 __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
 {
-    __shared__ uint32_t sid[64 * V];
-    __shared__ uint32_t sraw[64 * V];
+    constexpr int kN = 64 * V;
+    constexpr int kSlots = 2 * kN;
+    __shared__ int slot_id[kSlots];
+    __shared__ unsigned long long slot_best[kSlots];
     __shared__ Candidate cand[64];
+    __shared__ float kept_score[kTop];
+    __shared__ int kept_id[kTop];
     const int lane = threadIdx.x;
     const int64_t th = blockIdx.x;  // t * 4 + h
     const int t = (int)(th / kHeads);
     const int total = p.num_ranges * kTop;
     const msa_top16_row* rows = p.partial + th * p.num_ranges;
-    SortEl el[V];
+
+    for (int s = lane; s < kSlots; s += 64) {
+        slot_id[s] = -1;
+        slot_best[s] = 0ull;
+    }
+    float sv[V];
+    int iv[V];
+    unsigned long long pk[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const int e = V * lane + i;
+        const int e = i * 64 + lane;
         const int ec = min(e, total - 1);
-        int id = rows[ec / kTop].id[ec % kTop];
-        float sc = rows[ec / kTop].score[ec % kTop];
-        if (e >= total || id < 0) {
-            id = 0x7FFFFFFF;  // sorts after every real id; dropped below
-            sc = -INFINITY;
-        }
-        el[i].hi = (uint32_t)id;
-        el[i].lo = ~order_key(sc);
-        el[i].tag = (uint32_t)e | (__float_as_uint(sc) == 0x80000000u ? 0x80000000u : 0u);
+        iv[i] = e < total ? rows[ec / kTop].id[ec % kTop] : -1;
+        sv[i] = rows[ec / kTop].score[ec % kTop];
+        pk[i] = ((unsigned long long)order_key(sv[i]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
     }
     const int n = max(0, p.nvp[t]);
-    bitonic_sort_wave<V>(el, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // drop repeated ids (the previous element is slot i - 1, or the previous
-    // lane's last slot) and hand the survivors to the select's layout
-    const uint32_t prev_lane_last = (uint32_t)__shfl_up((int)el[V - 1].hi, 1);
+    int hs[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const uint32_t prev = i > 0 ? el[i - 1].hi : (lane > 0 ? prev_lane_last : 0xFFFFFFFFu);
-        const bool kept = el[i].hi != 0x7FFFFFFFu && el[i].hi != prev;
-        const uint32_t bits = (el[i].tag & 0x80000000u) ? 0x80000000u : key_to_bits(~el[i].lo);
-        sid[V * lane + i] = kept ? el[i].hi : 0xFFFFFFFFu;
-        sraw[V * lane + i] = bits;
+        hs[i] = 0;
+        if (iv[i] >= 0) {
+            int h = slot_of<kSlots>(iv[i]);
+            while (true) {  // at most kN ids in 2 * kN slots: a free slot exists
+                int expected = -1;
+                __hip_atomic_compare_exchange_strong(&slot_id[h], &expected, iv[i],
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (expected == -1 || expected == iv[i])
+                    break;
+                h = (h + 1) & (kSlots - 1);
+            }
+            hs[i] = h;
+            __hip_atomic_fetch_max(&slot_best[h], pk[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    float sv[V];
-    int iv[V];
     uint32_t u[V];
-    uint64_t fbits = 0;
+    bool forced[V];
     int n_forced = 0;
+    uint32_t lane_max = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        const uint32_t id = sid[i * 64 + lane];
-        const bool kept = id != 0xFFFFFFFFu;
-        sv[i] = __uint_as_float(sraw[i * 64 + lane]);
-        iv[i] = (int)id;
-        const bool forced = kept && is_forced((int)id, n, p.init_blocks, p.local_blocks);
-        u[i] = kept && !forced ? order_key(sv[i]) : 0u;
-        fbits |= (uint64_t)forced << i;
-        n_forced += __popcll(__ballot(forced));
+        const bool best = iv[i] >= 0 && slot_best[hs[i]] == pk[i];
+        forced[i] = best && is_forced(iv[i], n, p.init_blocks, p.local_blocks);
+        u[i] = best && !forced[i] ? order_key(sv[i]) : 0u;
+        n_forced += __popcll(__ballot(forced[i]));
+        lane_max = max(lane_max, u[i]);
     }
     const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
     if (n_forced < expected_forced && lane == 0 && p.errors)
         atomicAdd(p.errors, 1);
+    const int K = min(kTop - expected_forced, count_keys<V>(u));
+
+    // threshold filter: every key of the best K is >= theta
+    uint32_t theta = 1u;
+    if (K > 0) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            if (__popcll(__ballot(lane_max >= trial)) >= K)
+                prefix = trial;
+        }
+        theta = max(prefix, 1u);
+    }
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool sel = K > 0 && u[i] >= theta;
+        const uint64_t mask = __ballot(sel);
+        const int slot = base + lanes_below(mask);
+        if (sel && slot < 64) {
+            Candidate c;
+            c.key = u[i];
+            c.score = sv[i];
+            c.id = iv[i];
+            cand[slot] = c;
+        }
+        base += __popcll(mask);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // the kept entries, compacted into kept_score / kept_id
+    int m = 0;
+    auto keep = [&](bool k, float score, int id) {
+        const uint64_t mask = __ballot(k);
+        if (k) {
+            const int slot = m + lanes_below(mask);
+            kept_score[slot] = score;
+            kept_id[slot] = id;
+        }
+        m += __popcll(mask);
+    };
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        keep(forced[i], sv[i], iv[i]);
+    if (base <= 64) {
+        Candidate mine = {0u, -INFINITY, -1};
+        if (lane < base)
+            mine = cand[lane];
+        const uint32_t u1[1] = {mine.key};
+        const int id1[1] = {mine.id};
+        bool take1[1];
+        take_best<1>(u1, id1, K, take1);
+        keep(take1[0], mine.score, mine.id);
+    } else {  // heavy ties at theta: rank every value
+        bool take[V];
+        take_best<V>(u, iv, K, take);
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            keep(take[i], sv[i], iv[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
     msa_top16_row* dst = p.out + th;
-    const int kept = select_row<V>(u, sv, fbits, kTop - expected_forced, count_keys<V>(u), lane,
-                                   cand, [&](int i) { return iv[i]; },
-                                   [&](float score, int id, int slot) {
-                                       dst->score[slot] = score;
-                                       dst->id[slot] = id;
-                                   });
-    pad_row(dst, kept, lane);
+    if (lane < m) {
+        const int my_id = kept_id[lane];
+        int rank = 0;
+        for (int j = 0; j < m; ++j)
+            rank += kept_id[j] < my_id ? 1 : 0;
+        dst->score[rank] = kept_score[lane];
+        dst->id[rank] = my_id;
+    }
+    pad_row(dst, m, lane);
 }
 
 // Select over R ranges and merge, one (token, head) row per workgroup: wave
