@@ -43,6 +43,61 @@ __device__ __forceinline__ int is_forced(int id, int n, int init_blocks, int loc
     return id >= 0 && id < n && (id < init_blocks || id >= n - local_blocks);
 }
 
+// Value of lane (this lane ^ j), j a power of two below 64, without LDS
+// addressing: DPP quad permutes for 1 and 2, swizzle (bitmask mode, within
+// each 32-lane half) for 4, 8 and 16, the permlane32 swap for 32.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane)
+{
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+    } else if constexpr (J == 32) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return lane < 32 ? sw[1] : sw[0];
+    } else {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
+    }
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t x, int lane)
+{
+    const uint32_t o = lane_xor<J>(x, lane);
+    const bool keep_min = ((lane & J) == 0) == ((lane & K) == 0);
+    return keep_min ? min(x, o) : max(x, o);
+}
+
+// Sorts one value per lane ascending across the wave (a 64-element bitonic
+// network of 21 exchange steps) and returns the K-th largest (lane 64 - K),
+// 1 <= K <= 64, in every lane.
+__device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t x, int K, int lane)
+{
+    x = bitonic_step<2, 1>(x, lane);
+    x = bitonic_step<4, 2>(x, lane);
+    x = bitonic_step<4, 1>(x, lane);
+    x = bitonic_step<8, 4>(x, lane);
+    x = bitonic_step<8, 2>(x, lane);
+    x = bitonic_step<8, 1>(x, lane);
+    x = bitonic_step<16, 8>(x, lane);
+    x = bitonic_step<16, 4>(x, lane);
+    x = bitonic_step<16, 2>(x, lane);
+    x = bitonic_step<16, 1>(x, lane);
+    x = bitonic_step<32, 16>(x, lane);
+    x = bitonic_step<32, 8>(x, lane);
+    x = bitonic_step<32, 4>(x, lane);
+    x = bitonic_step<32, 2>(x, lane);
+    x = bitonic_step<32, 1>(x, lane);
+    x = bitonic_step<64, 32>(x, lane);
+    x = bitonic_step<64, 16>(x, lane);
+    x = bitonic_step<64, 8>(x, lane);
+    x = bitonic_step<64, 4>(x, lane);
+    x = bitonic_step<64, 2>(x, lane);
+    x = bitonic_step<64, 1>(x, lane);
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 64 - K);
+}
+
 // Number of candidate keys (u != 0) in the wave.
 template <int V>
 __device__ __forceinline__ int count_keys(const uint32_t (&u)[V])
@@ -69,17 +124,21 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
     uint32_t thr = 0xFFFFFFFFu;
     int need = 0;
     if (K > 0) {
-        uint32_t prefix = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t trial = prefix | (1u << bit);
-            int cnt = 0;
+        if constexpr (V == 1) {
+            thr = kth_largest_of_lanes(u[0], K, __lane_id());  // the K-th largest key
+        } else {
+            uint32_t prefix = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t trial = prefix | (1u << bit);
+                int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < V; ++i)
-                cnt += __popcll(__ballot(u[i] >= trial));
-            if (cnt >= K)
-                prefix = trial;
+                for (int i = 0; i < V; ++i)
+                    cnt += __popcll(__ballot(u[i] >= trial));
+                if (cnt >= K)
+                    prefix = trial;
+            }
+            thr = prefix;  // the K-th largest key
         }
-        thr = prefix;  // the K-th largest key
         int gt = 0;
 #pragma unroll
         for (int i = 0; i < V; ++i)
@@ -130,15 +189,8 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
         lane_max = max(lane_max, u[i]);
     const int K = min(budget, n_cand);
     uint32_t theta = 1u;
-    if (K > 0) {
-        uint32_t prefix = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t trial = prefix | (1u << bit);
-            if (__popcll(__ballot(lane_max >= trial)) >= K)
-                prefix = trial;
-        }
-        theta = max(prefix, 1u);
-    }
+    if (K > 0)
+        theta = max(kth_largest_of_lanes(lane_max, K, lane), 1u);
     int base = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
