@@ -147,17 +147,22 @@ __device__ __forceinline__ void take_best(const uint32_t (&u)[V], const int (&id
         take[i] = false;
     if (K <= 0)
         return;
-    uint32_t prefix = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t trial = prefix | (1u << bit);
-        int cnt = 0;
+    uint32_t thr;
+    if constexpr (V == 1) {
+        thr = kth_largest_of_lanes(u[0], K, __lane_id());
+    } else {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = prefix | (1u << bit);
+            int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < V; ++i)
-            cnt += __popcll(__ballot(u[i] >= trial));
-        if (cnt >= K)
-            prefix = trial;
+            for (int i = 0; i < V; ++i)
+                cnt += __popcll(__ballot(u[i] >= trial));
+            if (cnt >= K)
+                prefix = trial;
+        }
+        thr = prefix;
     }
-    const uint32_t thr = prefix;
     int gt = 0, tied = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -289,15 +294,8 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
 
     // threshold filter: every key of the best K is >= theta
     uint32_t theta = 1u;
-    if (K > 0) {
-        uint32_t prefix = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t trial = prefix | (1u << bit);
-            if (__popcll(__ballot(lane_max >= trial)) >= K)
-                prefix = trial;
-        }
-        theta = max(prefix, 1u);
-    }
+    if (K > 0)
+        theta = max(kth_largest_of_lanes(lane_max, K, lane), 1u);
     int base = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {

@@ -225,6 +225,10 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
                           [&](int, int slot) { emit(mine.score, mine.id & ~kForcedFlag, slot); });
 }
 
+#ifndef MSA_SELECT_DIRECT_MAX_V
+#define MSA_SELECT_DIRECT_MAX_V 2
+#endif
+
 // Picks the search for V values per lane: direct for small V, filtered above.
 // n_cand is the number of candidate keys (u != 0).
 template <int V, class IdOf, class Emit>
@@ -232,7 +236,7 @@ __device__ __forceinline__ int select_row(const uint32_t (&u)[V], const float (&
                                           uint64_t fbits, int budget, int n_cand, int lane,
                                           Candidate* buf, IdOf&& id_of, Emit&& emit)
 {
-    if (V <= 2)
+    if (V <= MSA_SELECT_DIRECT_MAX_V)
         return wave_select<V>(u, fbits, budget, n_cand,
                               [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
     return wave_select_filtered<V>(u, sv, fbits, budget, n_cand, lane, buf, id_of, emit);
