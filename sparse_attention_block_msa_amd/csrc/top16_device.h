@@ -69,6 +69,70 @@ __device__ __forceinline__ uint32_t bitonic_step(uint32_t x, int lane)
     return keep_min ? min(x, o) : max(x, o);
 }
 
+__device__ __forceinline__ uint32_t lane_xor_any(uint32_t v, int j, int lane)
+{
+    switch (j) {  // j is a compile-time constant wherever this is unrolled
+    case 1:
+        return lane_xor<1>(v, lane);
+    case 2:
+        return lane_xor<2>(v, lane);
+    case 4:
+        return lane_xor<4>(v, lane);
+    case 8:
+        return lane_xor<8>(v, lane);
+    case 16:
+        return lane_xor<16>(v, lane);
+    default:
+        return lane_xor<32>(v, lane);
+    }
+}
+
+// K-th largest of the wave's 64V keys (element i of lane l is 64i + l),
+// 1 <= K <= 64V, in every lane: a bitonic network sorts them ascending,
+// partners 64 or more apart within a lane, nearer ones across lanes.
+template <int V>
+__device__ __forceinline__ uint32_t kth_largest_of_wave(const uint32_t (&u)[V], int K, int lane)
+{
+    constexpr int kN = 64 * V;
+    uint32_t x[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        x[i] = u[i];
+#pragma unroll
+    for (int k = 2; k <= kN; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j >= 64) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const int i2 = i ^ (j >> 6);
+                    if (i2 > i) {
+                        const bool up = ((i * 64) & k) == 0;
+                        const uint32_t lo = min(x[i], x[i2]), hi = max(x[i], x[i2]);
+                        x[i] = up ? lo : hi;
+                        x[i2] = up ? hi : lo;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const uint32_t o = lane_xor_any(x[i], j, lane);
+                    const int e = i * 64 + lane;
+                    const bool keep_min = ((e & j) == 0) == ((e & k) == 0);
+                    x[i] = keep_min ? min(x[i], o) : max(x[i], o);
+                }
+            }
+        }
+    }
+    const int e = kN - K;
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        if (e / 64 == i)
+            r = (uint32_t)__builtin_amdgcn_readlane((int)x[i], e % 64);
+    return r;
+}
+
 // Sorts one value per lane ascending across the wave (a 64-element bitonic
 // network of 21 exchange steps) and returns the K-th largest (lane 64 - K),
 // 1 <= K <= 64, in every lane.
@@ -126,6 +190,8 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
     if (K > 0) {
         if constexpr (V == 1) {
             thr = kth_largest_of_lanes(u[0], K, __lane_id());  // the K-th largest key
+        } else if constexpr (V == 2) {
+            thr = kth_largest_of_wave<2>(u, K, __lane_id());
         } else {
             uint32_t prefix = 0;
             for (int bit = 31; bit >= 0; --bit) {
