@@ -4,13 +4,16 @@ One step = the whole chain on one batch of the long-context workload
 (4 requests x 1,048,576 keys, page_size 256, decode_query_len 8,
 plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
 
-    msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
+    msa_score_decode -> msa_top16_select_merge (select over R=8 ranges and
+                        the merge in one launch; per-range rows also written)
 
-Two fused variants of the step are timed beside it: select and merge in one
-launch (msa_top16_select_merge, per-range rows also written;
-e2e.fused_select_merge), and the plane with the per-range rows in one launch
-followed by the merge (msa_score_select -> msa_top16_merge;
-e2e.score_select_then_merge). One rank's share of the same workload on a
+(for more than 16 ranges or ranges wider than 2048 columns, where the
+one-launch form does not apply, the step is the three-launch chain below).
+Two other forms of the same step are timed beside it: the three-launch
+chain msa_score_decode -> msa_top16_select -> msa_top16_merge
+(e2e.three_launch_chain; its per-kernel times are e2e.kernels_ms), and the
+plane with the per-range rows in one launch followed by the merge
+(msa_score_select -> msa_top16_merge; e2e.score_select_then_merge). One rank's share of the same workload on a
 cache split by rows over 2 or 4 ranks (msa_score_decode_sharded ->
 msa_top16_select_mapped, then the owner's msa_top16_merge_dedup) is
 reported under e2e.sharded_rank_share.
@@ -83,30 +86,42 @@ def load_traffic(launch_bytes: int):
             "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
 
 
-def cpu_baseline(w, dev_rows_unused=None):
-    """The oracle on the same workload, on this host's cores."""
-    import numpy as np
+CPU_BASELINE_MIN_S = 10.0  # repeat whole passes until this much CPU time is spent
+CPU_BASELINE_MAX_PASSES = 30
 
+
+def cpu_baseline(w):
+    """The oracle on the same workload, on this host's cores: whole passes
+    (score the full plane, then select and merge) repeated until about ten
+    seconds have been spent, so the rate is not one short sample."""
     import oracle
 
     orc = oracle.default()
-    t0 = time.perf_counter()
-    plane, _, _ = orc.score_decode(w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(),
-                                   w.seq_lens.numpy(), page_size=w.page_size,
-                                   decode_query_len=w.dql, cols=w.cols)
-    t1 = time.perf_counter()
-    ps, pi, _ = orc.top16_select(plane, w.num_valid_pages.numpy(), init_blocks=w.init_blocks,
-                                 local_blocks=w.local_blocks, num_ranges=w.num_ranges)
-    if w.num_ranges > 1:
-        orc.top16_merge(ps, pi, w.num_valid_pages.numpy(), init_blocks=w.init_blocks,
-                        local_blocks=w.local_blocks)
-    t2 = time.perf_counter()
+    nvp = w.num_valid_pages.numpy()
+    q, k, bt, sl = w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(), w.seq_lens.numpy()
+    score_s = select_s = 0.0
+    passes = 0
+    while passes < CPU_BASELINE_MAX_PASSES and score_s + select_s < CPU_BASELINE_MIN_S:
+        t0 = time.perf_counter()
+        plane, _, _ = orc.score_decode(q, k, bt, sl, page_size=w.page_size,
+                                       decode_query_len=w.dql, cols=w.cols)
+        t1 = time.perf_counter()
+        ps, pi, _ = orc.top16_select(plane, nvp, init_blocks=w.init_blocks,
+                                     local_blocks=w.local_blocks, num_ranges=w.num_ranges)
+        if w.num_ranges > 1:
+            orc.top16_merge(ps, pi, nvp, init_blocks=w.init_blocks, local_blocks=w.local_blocks)
+        t2 = time.perf_counter()
+        score_s += t1 - t0
+        select_s += t2 - t1
+        passes += 1
     keys = w.total_keys
-    return {"value": keys / (t2 - t0), "unit": "keys/s", "cores": orc.num_threads(),
+    total = score_s + select_s
+    return {"value": keys * passes / total, "unit": "keys/s", "cores": orc.num_threads(),
             "kind": "oracle",
-            "sample": f"the full workload once: {keys} keys scored ({t1 - t0:.1f} s), then "
-                      f"Top16 select over {w.num_ranges} ranges and merge ({t2 - t1:.2f} s)",
-            "seconds": round(t2 - t0, 2)}
+            "sample": f"{passes} whole passes over the workload ({keys} keys each): score "
+                      f"{score_s / passes:.2f} s, then Top16 select over {w.num_ranges} ranges "
+                      f"and merge {select_s / passes:.2f} s, per pass",
+            "seconds": round(total, 2)}
 
 
 def main():
@@ -165,11 +180,25 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    def step_fused():
+        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
+                             decode_query_len=w.dql, errors=errors, stream=stream)
+        msa.msa_top16_select_merge(plane, nvp, final, init_blocks=w.init_blocks,
+                                   local_blocks=w.local_blocks, num_ranges=R, partial=part,
+                                   errors=errors, stream=stream)
+
+    # select and merge in one launch where that form applies (at most 16
+    # ranges of at most 2048 columns)
+    fused_applies = 1 < R <= 16 and -(-w.cols // R) <= 2048
+    step_main = step_fused if fused_applies else step
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         if not args.no_flush:
             flush.sum()
-        step()
+        step_main()
+        if fused_applies:
+            step()
     torch.cuda.synchronize()
 
     # Timed region 1 (the headline): K steps, an event pair around each step
@@ -183,35 +212,25 @@ def main():
         if not args.no_flush:
             flush.sum()
         step_events[i][0].record(stream)
-        step()
+        step_main()
         step_events[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    # Timed region 1b: the same K steps with select and merge in one launch
-    # (msa_top16_select_merge, also writing the per-range rows), reported
-    # beside the headline.
-    def step_fused():
-        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
-                             decode_query_len=w.dql, errors=errors, stream=stream)
-        msa.msa_top16_select_merge(plane, nvp, final, init_blocks=w.init_blocks,
-                                   local_blocks=w.local_blocks, num_ranges=R, partial=part,
-                                   errors=errors, stream=stream)
-
-    fused_ms = None
-    if R <= 16 and -(-w.cols // R) <= 2048:
-        for _ in range(args.warmup):
-            step_fused()
-        fused_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # Timed region 1b: the same K steps as the three-launch chain (score,
+    # select, merge), reported beside the headline.
+    chain_ms = None
+    if fused_applies:
+        chain_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                         for _ in range(args.steps)]
         for i in range(args.steps):
             if not args.no_flush:
                 flush.sum()
-            fused_events[i][0].record(stream)
-            step_fused()
-            fused_events[i][1].record(stream)
+            chain_events[i][0].record(stream)
+            step()
+            chain_events[i][1].record(stream)
         torch.cuda.synchronize()
-        fused_ms = sum(ev[0].elapsed_time(ev[1]) for ev in fused_events) / args.steps
+        chain_ms = sum(ev[0].elapsed_time(ev[1]) for ev in chain_events) / args.steps
 
     # Timed region 1c: the same K steps with the plane and the range rows from
     # one launch (msa_score_select), then msa_top16_merge; reported beside the
@@ -305,7 +324,7 @@ def main():
                 "owner_merge_ms": merge_ms, "merged_rows_per_head": ws_n * R}
             del shard, splane, spart, all_rows, merged
 
-    # Timed region 2: the same K steps with an event between every kernel,
+    # Timed region 2: K three-launch steps with an event between every kernel,
     # for per-kernel durations (the events themselves lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps per kernel", file=sys.stderr, flush=True)
@@ -371,7 +390,10 @@ def main():
                    "ranges": R, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
                    "index_k_bytes": launch_bytes, "parallelism": "single-gpu",
                    "cache_flush_between_steps": not args.no_flush},
-        "e2e": {"hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
+        "e2e": {"step": ("msa_score_decode -> msa_top16_select_merge" if fused_applies else
+                         "msa_score_decode -> msa_top16_select" +
+                         (" -> msa_top16_merge" if R > 1 else "")),
+                "hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
                 "step_ms_p10": step_ms[len(step_ms) // 10],
                 "step_ms_p50": step_ms[len(step_ms) // 2],
                 "step_ms_p90": step_ms[(len(step_ms) * 9) // 10],
@@ -379,10 +401,10 @@ def main():
                                "top16_merge": mean(merge_ms)},
                 "score_decode_ms_back_to_back": score_b2b_ms,
                 "step_ms_with_kernel_events": mean([ev[0].elapsed_time(ev[3]) for ev in events]),
-                "fused_select_merge": None if fused_ms is None else {
-                    "ms_per_step": fused_ms, "keys_per_s": keys / (fused_ms * 1e-3),
-                    "hbm_gbps": launch_bytes / (fused_ms * 1e-3) / 1e9,
-                    "frac_of_peak": launch_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "three_launch_chain": None if chain_ms is None else {
+                    "ms_per_step": chain_ms, "keys_per_s": keys / (chain_ms * 1e-3),
+                    "hbm_gbps": launch_bytes / (chain_ms * 1e-3) / 1e9,
+                    "frac_of_peak": launch_bytes / (chain_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                 "score_select_then_merge": None if score_select_ms is None else {
                     "ms_per_step": score_select_ms,
                     "keys_per_s": keys / (score_select_ms * 1e-3),
