@@ -4,13 +4,15 @@ Select / merge (bit-exact): ties, signed zeros and -inf (the ranking
 treats -0 == +0, lower id wins), all-equal rows (more than 64 candidates at
 the threshold), empty and short rows, forced blocks covering everything,
 num_valid_pages outside [0, cols] (error counter, clamped), rows wide enough
-for the four-wave path, and up to the maximum number of ranges.
+for the four-wave path, and up to the maximum number of ranges. A plane of
+more than 2^31 elements (scorer and select).
 
 Scorer: empty and one-token requests, sequences shorter than the decode
 length, exact multiples of 128, page_size 256 with odd block counts, every
 decode_query_len, a plane exactly as wide as the written columns, a plane
-too narrow (error counter, clamped), and out-of-range block_table entries
-(error counter, block scored -inf).
+too narrow (error counter, clamped), out-of-range block_table entries
+(error counter, block scored -inf), 5000 requests, and pages past byte
+offset 2^32 of a larger-than-4-GiB cache.
 """
 from __future__ import annotations
 
@@ -30,6 +32,12 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
 TIE_POOL = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.5, 2.0], dtype=np.float32)
 
 
@@ -305,3 +313,75 @@ def test_scorer_large_batch():
     got, err = run_scorer(w, w.cols, extra=4)
     assert err == 0
     check_plane(w, got, w.cols + 4)
+
+
+def test_scorer_pages_beyond_4gib():
+    """An index-K cache larger than 4 GiB whose used pages (poison page
+    included) all sit above byte offset 2^32: 64-bit page addressing. The
+    plane matches the oracle run on the compact copy of the same pages."""
+    w = workloads.generate(batch=3, seq=("list", [3000, 700, 256]), page_size=256, dql=3,
+                           seed=77)
+    pages = w.index_k.shape[0]
+    base = (1 << 32) // (256 * 128) + 5  # first page whose bytes start past 4 GiB
+    say(f"[test] index-K of {(base + pages) * 256 * 128 / 2**30:.2f} GiB")
+    big = torch.empty((base + pages, 256, 128), dtype=torch.uint8, device=DEV)
+    big[base:] = w.index_k.to(DEV)
+    bt = (w.block_table + base).to(DEV)  # every slot, the poison page's too
+    cols = w.cols + 4
+    out = torch.full((w.num_tokens, 4, cols), int(CANARY_BITS), dtype=torch.int32,
+                     device=DEV).view(torch.float32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_score_decode(w.index_q.to(DEV), big, bt, w.seq_lens.to(DEV), out,
+                         page_size=256, decode_query_len=w.dql, errors=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = out.cpu().numpy()
+    del big
+    torch.cuda.empty_cache()
+    check_plane(w, got, cols)
+
+
+def test_plane_beyond_2g_elements():
+    """A plane of more than 2^31 float32 elements (8193 requests x 8 tokens x
+    4 heads x 8192 columns, 8.6 GB): 64-bit plane offsets in the scorer and
+    the select. The last requests' rows match the oracle (plane within the
+    score bound, select bit for bit on the GPU's plane)."""
+    batch, dql, cols = 8193, 8, 8192
+    w = workloads.generate(batch=batch, seq=("uniform", 1, 300), page_size=128, dql=dql,
+                           seed=78, cols=cols, table_width=4)
+    T = w.num_tokens
+    assert T * 4 * cols > 2**31
+    say(f"[test] plane of {T * 4 * cols * 4 / 1e9:.1f} GB")
+    plane = torch.full((T, 4, cols), int(CANARY_BITS), dtype=torch.int32,
+                       device=DEV).view(torch.float32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_score_decode(w.index_q.to(DEV), w.index_k.to(DEV), w.block_table.to(DEV),
+                         w.seq_lens.to(DEV), plane, page_size=128, decode_query_len=dql,
+                         errors=err)
+    rows = msa.new_rows(T, 4, 1, device=DEV)
+    rows.fill_(0x7BADBEEF)
+    nvp = w.num_valid_pages.to(DEV)
+    msa.msa_top16_select(plane, nvp, rows, init_blocks=1, local_blocks=2, num_ranges=1,
+                         errors=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    last = 3  # the last requests: their rows sit past element 2^31
+    t0 = (batch - last) * dql
+    got = plane[t0:].cpu().numpy()
+    got_rows = rows[t0:, :, 0].cpu()
+    del plane, rows
+    torch.cuda.empty_cache()
+    assert t0 * 4 * cols < 2**31 < T * 4 * cols  # the checked rows straddle element 2^31
+    sub = slice(batch - last, batch)
+    sl = w.seq_lens[sub].numpy()
+    ref, amax, _ = oracle.score_decode(w.index_q[t0:].numpy(), w.index_k.numpy(),
+                                       w.block_table[sub].numpy(), sl, page_size=128,
+                                       decode_query_len=dql, cols=cols, want_amax=True)
+    written = written_mask(sl, dql, cols)
+    n_bad, ratio = compare_plane(got, ref, amax, written)
+    assert n_bad == 0, (n_bad, ratio)
+    assert np.all(got.view(np.uint32)[~written] == CANARY_BITS)
+    nvp_sub = w.num_valid_pages[t0:].numpy()
+    rs, ri, _ = oracle.top16_select(got, nvp_sub, init_blocks=1, local_blocks=2, num_ranges=1)
+    assert_rows_equal(msa.row_scores(got_rows).numpy(), msa.row_ids(got_rows).numpy(),
+                      rs[:, :, 0], ri[:, :, 0], "select past element 2^31")
