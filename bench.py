@@ -5,7 +5,7 @@ One step = the whole chain on one batch of the long-context workload
 plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
 
     msa_score_decode -> msa_top16_select_merge (select over R=8 ranges and
-                        the merge in one launch; per-range rows also written)
+                        the merge in one launch; the range rows stay in LDS)
 
 (for more than 16 ranges or ranges wider than 2048 columns, where the
 one-launch form does not apply, the step is the three-launch chain below).
@@ -184,7 +184,7 @@ def main():
         msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
                              decode_query_len=w.dql, errors=errors, stream=stream)
         msa.msa_top16_select_merge(plane, nvp, final, init_blocks=w.init_blocks,
-                                   local_blocks=w.local_blocks, num_ranges=R, partial=part,
+                                   local_blocks=w.local_blocks, num_ranges=R,
                                    errors=errors, stream=stream)
 
     # select and merge in one launch where that form applies (at most 16

@@ -236,8 +236,9 @@ def test_end_to_end(n):
     torch.cuda.synchronize()
     assert int(errors.item()) == 0
     if 1 < R <= 16 and -(-w.cols // R) <= 2048:
-        # the one-launch select + merge, as the benchmark's step runs it, on
-        # the same plane: bit-identical merged rows and range rows
+        # the one-launch select + merge on the same plane: bit-identical
+        # merged rows and range rows, then merged rows alone as the
+        # benchmark's step runs it
         fused = msa.new_rows(T, 4, device=DEV)
         fused_part = msa.new_rows(T, 4, R, device=DEV)
         fused.fill_(0x7BADBEEF)
@@ -249,6 +250,12 @@ def test_end_to_end(n):
         assert int(errors.item()) == 0
         assert torch.equal(fused, final)
         assert torch.equal(fused_part, part)
+        fused.fill_(0x7BADBEEF)  # the benchmark's form: merged rows only
+        msa.msa_top16_select_merge(plane, case.nvp, fused, init_blocks=w.init_blocks,
+                                   local_blocks=w.local_blocks, num_ranges=R, errors=errors)
+        torch.cuda.synchronize()
+        assert int(errors.item()) == 0
+        assert torch.equal(fused, final)
     gplane = plane.cpu().numpy()
     fin = final.cpu()
     g_s, g_i = msa.row_scores(fin).numpy(), msa.row_ids(fin).numpy()
