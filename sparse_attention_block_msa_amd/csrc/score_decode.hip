@@ -407,13 +407,17 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, const ColumnG
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    static_assert(kUnit == 4 || (kUnit == 1 && !kDeviceScope), "unsupported store mode");
+    static_assert(kUnit == 4 || kUnit == 1, "unsupported store mode");
     if constexpr (kUnit == 1) {  // single-column stores: windows need not be 4-aligned
         const int ncol = c_end - c_begin;
         for (int i = lane; i < rows * ncol; i += 64) {
             const int rho = i / ncol;
             const int c = i - rho * ncol;
-            p.out[(row_base + rho) * p.cols + c_begin + c] = res[rho][c];
+            float* dst = p.out + (row_base + rho) * p.cols + c_begin + c;
+            if (kDeviceScope)  // written through to the device's coherence point
+                __hip_atomic_store(dst, res[rho][c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *dst = res[rho][c];
         }
     }
     if constexpr (kUnit == 4) {
@@ -423,10 +427,15 @@ __device__ __forceinline__ void score_window(const ScoreParams& p, const ColumnG
             const int q4 = i - rho * quads;
             const v4f v = *reinterpret_cast<const v4f*>(&res[rho][q4 * 4]);
             float* dst = p.out + (row_base + rho) * p.cols + c_begin + q4 * 4;
-            if (kDeviceScope) {  // written through to the device's coherence point
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (kDeviceScope) {
+                // Written through to the device's coherence point: the sc1
+                // policy, which an agent-scope atomic store of one dword
+                // also carries, on one 16-byte store (the four dwords need
+                // no atomicity together; readers wait for the producing
+                // wave's counter release first). Its completion is awaited
+                // with an explicit vmcnt(0) before that release.
+                asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(v)
+                             : "memory");
             } else {
                 *reinterpret_cast<v4f*>(dst) = v;
             }
@@ -617,7 +626,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // within the waves the device holds at once, so every wait ends; the clock
 // limit counts an error instead of spinning on if that fails, and a wave that
 // has timed out once counts its later unfinished waits without waiting.
-template <int NT, int kParts, int kWavesPerEU, int V>
+template <int NT, int kParts, int kWavesPerEU, int V, int kUnit>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_select_kernel(ScoreSelectParams q)
 {
@@ -629,7 +638,7 @@ void score_select_kernel(ScoreSelectParams q)
     const int R = q.num_ranges;
     const int w = q.width;
 
-    score_wave_range<NT, kParts, true, 4, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
+    score_wave_range<NT, kParts, true, kUnit, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (lane == 0) {
             for (int r = c_begin / w; r * w < c_end; ++r) {
@@ -716,11 +725,15 @@ const void* score_latency_kernel_fn()
         &score_decode_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, 1, false>);
 }
 
-template <int NT, int V>
+template <int NT, int V, bool kLatency>
 const void* score_select_kernel_fn()
 {
     constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
-    return reinterpret_cast<const void*>(&score_select_kernel<NT, kParts, kRegWaves, V>);
+    if constexpr (kLatency)  // one column per wave, a block per DMA round trip
+        return reinterpret_cast<const void*>(
+            &score_select_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, V, 1>);
+    else
+        return reinterpret_cast<const void*>(&score_select_kernel<NT, kParts, kRegWaves, V, 4>);
 }
 
 // Compute units of the current device (host query, cached per device; the
@@ -789,10 +802,13 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
     return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
 }
 
-// Values per lane of the fused kernel's select: spans up to 256, 1024 and
-// 2048 columns.
-#define MSA_FOR_EACH_SCORE_SELECT(X) X(1, 4) X(1, 16) X(1, 32) X(2, 4) X(2, 16) X(2, 32)
-constexpr int kScoreSelectInstances = 6;
+// Values per lane of the fused kernel's select (spans up to 256, 1024 and
+// 2048 columns), streaming or latency mode.
+#define MSA_FOR_EACH_SCORE_SELECT(X)                                                  \
+    X(1, 4, false) X(1, 16, false) X(1, 32, false) X(2, 4, false) X(2, 16, false)     \
+    X(2, 32, false) X(1, 4, true) X(1, 16, true) X(1, 32, true) X(2, 4, true)         \
+    X(2, 16, true) X(2, 32, true)
+constexpr int kScoreSelectInstances = 12;
 
 // Workgroups (one wave each) of instance `which` that one CU holds at once,
 // queried once per device: the query costs far more host time than a launch.
@@ -815,13 +831,17 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
 {
     const int nt = q.score.dql * kHeads <= 16 ? 1 : 2;
     const int v = q.width <= 256 ? 4 : q.width <= 1024 ? 16 : q.width <= kMaxFusedWidth ? 32 : 0;
+    // the scorer's rule: small batches score one column per wave
+    const int64_t max_cols = (int64_t)q.score.batch * q.score.cols;
+    const bool latency =
+        max_cols <= (int64_t)device_cus() * 4 * MSA_SCORE_LATENCY_WAVES_PER_SIMD;
     const void* fn = nullptr;
     int which = 0, index = 0;
-#define X(NT, V)                                \
-    if (nt == NT && v == V) {                   \
-        fn = score_select_kernel_fn<NT, V>();   \
-        which = index;                          \
-    }                                           \
+#define X(NT, V, L)                                  \
+    if (nt == NT && v == V && latency == L) {        \
+        fn = score_select_kernel_fn<NT, V, L>();     \
+        which = index;                               \
+    }                                                \
     ++index;
     MSA_FOR_EACH_SCORE_SELECT(X)
 #undef X
@@ -832,7 +852,7 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
     const int per_cu = resident_per_cu(fn, which);
     if (per_cu <= 0)
         return hipErrorInvalidConfiguration;
-    int64_t grid = score_grid(q.score);
+    int64_t grid = latency ? max_cols : score_grid(q.score);
     const int64_t resident = (int64_t)per_cu * device_cus();
     if (grid > resident)
         grid = resident;
@@ -856,9 +876,9 @@ hipError_t warmup_score_kernels()
         e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<1>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<2>());
-#define X(NT, V)          \
+#define X(NT, V, L)       \
     if (e == hipSuccess)  \
-        e = hipFuncGetAttributes(&attr, score_select_kernel_fn<NT, V>());
+        e = hipFuncGetAttributes(&attr, score_select_kernel_fn<NT, V, L>());
     MSA_FOR_EACH_SCORE_SELECT(X)
 #undef X
     return e;
