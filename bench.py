@@ -33,7 +33,10 @@ steps, fills included, with a synchronize on both sides.
 Prints one JSON line. `value` is scored keys/s, i.e. the sum of seq_len over
 the mean step time. `roofline` rates the scorer, the dominant kernel, against
 HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
-`cpu_baseline` times the oracle on the same workload.
+`roofline.stream_read_probe` times msa_stream_read_probe, a plain streaming
+read with no other work, over as many index-K bytes in the same way: the
+streaming ceiling the scorer's rate is read against. `cpu_baseline` times the oracle on the
+same workload.
 """
 from __future__ import annotations
 
@@ -350,6 +353,21 @@ def main():
     b2b[1].record(stream)
     torch.cuda.synchronize()
     score_b2b_ms = b2b[0].elapsed_time(b2b[1]) / args.steps
+    # Timed region 3b: the streaming-read probe (a plain read, no other work)
+    # over as many index-K bytes, timed the same way: the streaming ceiling
+    # the scorer's rate is read against.
+    probe_bytes = workloads.index_k_bytes(w)  # the first pages, in storage order
+    sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    msa.msa_stream_read_probe(k, sink, nbytes=probe_bytes, stream=stream)
+    if not args.no_flush:
+        flush.sum()
+    b2b_probe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b2b_probe[0].record(stream)
+    for _ in range(args.steps):
+        msa.msa_stream_read_probe(k, sink, nbytes=probe_bytes, stream=stream)
+    b2b_probe[1].record(stream)
+    torch.cuda.synchronize()
+    probe_ms = b2b_probe[0].elapsed_time(b2b_probe[1]) / args.steps
     if int(errors.item()) != 0:
         raise RuntimeError(f"device error counter = {int(errors.item())}")
     if args.calibrate_copy:
@@ -371,6 +389,7 @@ def main():
     e2e_gbps = launch_bytes / (ms_step * 1e-3) / 1e9
     score_mean = mean(score_ms)
     achieved = launch_bytes / (score_b2b_ms * 1e-3) / 1e9
+    probe_gbps = probe_bytes / (probe_ms * 1e-3) / 1e9
 
     out = {
         "metric": "index-K scored keys/s and achieved HBM GB/s (% of peak), score+Top16, 1 GPU",
@@ -418,7 +437,13 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "launch_ms": score_b2b_ms,
                      "launch_ms_source": "K scorer launches back to back between one event pair",
-                     "traffic": load_traffic(launch_bytes)},
+                     "traffic": load_traffic(launch_bytes),
+                     "stream_read_probe": {
+                         "what": "msa_stream_read_probe over as many index-K bytes, pages "
+                                 "in storage order: a plain streaming read with no other work",
+                         "launch_ms": probe_ms, "achieved": probe_gbps,
+                         "frac_of_peak": probe_gbps / HBM_PEAK_GBPS,
+                         "scorer_frac_of_probe": achieved / probe_gbps}},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

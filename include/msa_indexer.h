@@ -66,6 +66,7 @@ extern "C" {
 #define MSA_MAX_SELECT_COLS 12287 /* select scores: 0 < K < 12288                          */
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
 #define MSA_SCORE_SELECT_COUNTER_STRIDE 32 /* int32 per msa_score_select counter (128 B)  */
+#define MSA_STREAM_PROBE_SINK_WORDS 1024   /* uint32 words of msa_stream_read_probe's sink */
 
 /*
  * One Top16 row (128 bytes). score[i] is the score-plane value of block
@@ -315,6 +316,24 @@ int32_t msa_score_columns(int64_t max_seq_len);
  * Returns MSA_OK or MSA_ERR_LAUNCH.
  */
 int msa_warmup(void);
+
+/*
+ * Measurement aid, not a step of the indexer: no page defines it. It reads
+ * `bytes` of device memory at `src` once, with no other work (non-temporal
+ * 16-byte loads, a whole 16 KiB block in flight per wave, the fastest plain
+ * read shape measured on the device), so its rate is the streaming ceiling
+ * that msa_score_decode's rate can be read against. Benchmarks time it
+ * beside the scorer over as many index-K bytes.
+ *
+ * src   device, 16-byte aligned; bytes a positive multiple of 16384.
+ * sink  device uint32[MSA_STREAM_PROBE_SINK_WORDS]. The probe xors every
+ *       dword of the buffer into these words (each wave's share into one of
+ *       them), so a caller that zeroes them first can check that the xor of
+ *       all words is the xor of the buffer, i.e. that every byte was read.
+ * Returns MSA_OK, MSA_ERR_INVALID_ARG (null pointer, misaligned src, bad
+ * size; nothing launched) or MSA_ERR_LAUNCH.
+ */
+int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
  * Text of the last failed check or launch of the calling thread. The string

@@ -34,9 +34,11 @@ TOPK = 16
 COUNTER_STRIDE = 32  # int32 words per msa_score_select workspace counter (128 bytes)
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
+STREAM_PROBE_SINK_WORDS = 1024  # MSA_STREAM_PROBE_SINK_WORDS
+
 EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
-           "msa_score_columns", "msa_warmup", "msa_last_error")
+           "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe")
 
 
 class MsaError(RuntimeError):
@@ -84,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_score_columns.restype = i32
     lib.msa_warmup.argtypes = []
     lib.msa_warmup.restype = ctypes.c_int
+    lib.msa_stream_read_probe.argtypes = [P, i64, P, P]
+    lib.msa_stream_read_probe.restype = ctypes.c_int
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -155,6 +159,23 @@ def msa_score_columns(max_seq_len: int) -> int:
 def msa_warmup() -> None:
     """Loads every kernel into the current device's context."""
     _check(load().msa_warmup())
+
+
+def msa_stream_read_probe(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int | None = None,
+                          stream=None) -> None:
+    """Measurement aid: a plain streaming read of the first `nbytes` (default
+    all) of the contiguous device tensor `src`, xoring every dword into the
+    words of `sink` (int32 [>= 1024] on the device; the xor of its words is
+    the xor of the bytes read)."""
+    _dev(src, sink)
+    _need(src.is_contiguous(), "src: contiguous")
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    _need(0 < nbytes <= total, f"nbytes must be in (0, {total}]")
+    _need(sink.dtype == torch.int32 and sink.numel() >= STREAM_PROBE_SINK_WORDS and
+          sink.is_contiguous(), f"sink: contiguous int32 [>= {STREAM_PROBE_SINK_WORDS}]")
+    _check(load().msa_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(),
+                                        _stream_handle(stream)))
 
 
 def _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,

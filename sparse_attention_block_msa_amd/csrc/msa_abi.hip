@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include "msa_internal.h"
+#include "stream_probe.h"
 
 namespace {
 
@@ -351,6 +352,21 @@ int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols
     p.num_ranges = num_ranges;
     p.width = width;
     return launch_result(msa::launch_top16_select_merge(p, stream), fn);
+}
+
+int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream)
+{
+    static const char* fn = "msa_stream_read_probe";
+    g_last_error[0] = '\0';
+    MSA_CHECK(src && sink, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(src, 16), "%s: src must be 16-byte aligned", fn);
+    MSA_CHECK(bytes > 0 && bytes % msa::kProbeBlockBytes == 0,
+              "%s: bytes (%lld) must be a positive multiple of %lld", fn, (long long)bytes,
+              (long long)msa::kProbeBlockBytes);
+    return launch_result(msa::launch_stream_read_probe(static_cast<const uint8_t*>(src),
+                                                       bytes / msa::kProbeBlockBytes, sink,
+                                                       stream),
+                         fn);
 }
 
 int msa_warmup(void)

@@ -292,3 +292,25 @@ def _merge_dedup(lib, **kw):
 def test_merge_dedup_rejects(lib, kw, needle):
     assert _merge_dedup(lib, **kw) == msa.MSA_ERR_INVALID_ARG
     assert needle in lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(src=None), "null"),
+    (dict(sink=None), "null"),
+    (dict(src=FAKE + 4), "aligned"),
+    (dict(nbytes=0), "multiple"),
+    (dict(nbytes=-16384), "multiple"),
+    (dict(nbytes=16384 + 16), "multiple"),
+])
+def test_stream_read_probe_rejects(lib, kw, needle):
+    a = dict(src=FAKE, nbytes=1 << 20, sink=FAKE, stream=None)
+    a.update(kw)
+    assert lib.msa_stream_read_probe(a["src"], a["nbytes"], a["sink"],
+                                     a["stream"]) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def test_probe_sink_words_match_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MSA_STREAM_PROBE_SINK_WORDS (\d+)", text)
+    assert m and int(m.group(1)) == msa.STREAM_PROBE_SINK_WORDS

@@ -385,3 +385,17 @@ def test_plane_beyond_2g_elements():
     rs, ri, _ = oracle.top16_select(got, nvp_sub, init_blocks=1, local_blocks=2, num_ranges=1)
     assert_rows_equal(msa.row_scores(got_rows).numpy(), msa.row_ids(got_rows).numpy(),
                       rs[:, :, 0], ri[:, :, 0], "select past element 2^31")
+
+
+@pytest.mark.parametrize("blocks", [1, 7, 3000])
+def test_stream_read_probe_reads_every_byte(blocks):
+    """The streaming-read probe (the benchmark's ceiling for the scorer) reads
+    every byte once: its xor of all the buffer's dwords equals the host's,
+    for a partial last workgroup and a partial last wave."""
+    g = torch.Generator().manual_seed(blocks)
+    host = torch.randint(0, 256, (blocks * 16384,), dtype=torch.uint8, generator=g)
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=DEV)
+    msa.msa_stream_read_probe(host.to(DEV), sink)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
