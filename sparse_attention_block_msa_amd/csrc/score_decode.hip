@@ -280,10 +280,13 @@ struct ColumnGeometry {
     int pos_off;     // position of a column's first key minus c * col_stride
     int page_rows;   // key rows per stored page
     int col_rows;    // keys per column
-    int parts;       // 32-key DMA pieces per column
+    int parts;       // DMA pieces (128 / kParts keys each) per column
 };
 
-template <bool kSharded>
+// kParts: pieces per B128 block of the instance; a column of col_rows keys
+// takes col_rows / (128 / kParts) of them (the host picks an instance whose
+// piece divides the column).
+template <bool kSharded, int kParts>
 __device__ __forceinline__ ColumnGeometry column_geometry(const ScoreParams& p)
 {
     ColumnGeometry gm;
@@ -294,14 +297,14 @@ __device__ __forceinline__ ColumnGeometry column_geometry(const ScoreParams& p)
         gm.pos_off = p.rank * r;
         gm.page_rows = r;
         gm.col_rows = r;
-        gm.parts = r / 32;
+        gm.parts = r / (kBlockTokens / kParts);
     } else {
         gm.col_shift = p.page_size == 256 ? 1 : 0;
         gm.col_stride = kBlockTokens;
         gm.pos_off = 0;
         gm.page_rows = p.page_size;
         gm.col_rows = kBlockTokens;
-        gm.parts = 4;
+        gm.parts = kParts;
     }
     return gm;
 }
@@ -459,7 +462,7 @@ template <int NT, int kParts, bool kDeviceScope, int kUnit, bool kSharded, class
 __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* tile,
                                                  float (*res)[kChunk], SegmentDone&& segment_done)
 {
-    const ColumnGeometry gm = column_geometry<kSharded>(p);
+    const ColumnGeometry gm = column_geometry<kSharded, kParts>(p);
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -707,12 +710,18 @@ const void* score_kernel_fn()
     return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, false>);
 }
 
-// Row-sharded cache: one rank's share, streaming grid.
-template <int NT>
+// Row-sharded cache: one rank's share, streaming grid. A shard column of 64
+// or 128 rows is staged in 64-row pieces (kShardParts = 2), a 32-row one in
+// 32-row pieces.
+#ifndef MSA_SCORE_SHARD_WIDE_PARTS
+#define MSA_SCORE_SHARD_WIDE_PARTS 2
+#endif
+template <int NT, int kShardParts>
 const void* score_sharded_kernel_fn()
 {
     constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
-    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, true>);
+    return reinterpret_cast<const void*>(
+        &score_decode_kernel<NT, kShardParts, kRegWaves, 4, true>);
 }
 
 // Small batches: one column per work unit and a whole block per DMA round
@@ -789,7 +798,11 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
     void* args[] = {const_cast<ScoreParams*>(&p)};
     const bool small_q = p.dql * kHeads <= 16;
     if (p.world_size > 1) {
-        const void* fn = small_q ? score_sharded_kernel_fn<1>() : score_sharded_kernel_fn<2>();
+        const bool wide = (p.page_size / p.world_size) % (kBlockTokens / MSA_SCORE_SHARD_WIDE_PARTS) == 0;
+        const void* fn =
+            wide ? (small_q ? score_sharded_kernel_fn<1, MSA_SCORE_SHARD_WIDE_PARTS>()
+                            : score_sharded_kernel_fn<2, MSA_SCORE_SHARD_WIDE_PARTS>())
+                 : (small_q ? score_sharded_kernel_fn<1, 4>() : score_sharded_kernel_fn<2, 4>());
         return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
     }
     const int64_t max_cols = (int64_t)p.batch * p.cols;
@@ -869,9 +882,13 @@ hipError_t warmup_score_kernels()
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_kernel_fn<2>());
     if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1>());
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1, 4>());
     if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2>());
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2, 4>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1, MSA_SCORE_SHARD_WIDE_PARTS>());
+    if (e == hipSuccess)
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2, MSA_SCORE_SHARD_WIDE_PARTS>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<1>());
     if (e == hipSuccess)
