@@ -245,6 +245,25 @@ __device__ __forceinline__ int written_cols(int seq, int cols, bool& clamped,
     return clamped ? cols : (int)w;
 }
 
+// The wave's place in the work split. Workgroups are dispatched to the
+// device's XCDs round-robin (workgroup i to XCD i % kXcds), and each XCD has
+// its own L2 and its own share of the fabric to HBM. With a grid that is a
+// whole number of waves per XCD, slot = (i % kXcds) * (grid / kXcds) + i /
+// kXcds gives every XCD one contiguous eighth of the units, so the XCDs'
+// loads differ by at most one unit however uneven the per-wave shares are.
+#ifndef MSA_SCORE_XCD_SPLIT
+#define MSA_SCORE_XCD_SPLIT 1
+#endif
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int split_slot()
+{
+    const int i = blockIdx.x, grid = gridDim.x;
+    if (!MSA_SCORE_XCD_SPLIT || grid % kXcds != 0)
+        return i;
+    return (i % kXcds) * (grid / kXcds) + i / kXcds;
+}
+
 __device__ __forceinline__ int wave_sum(int v)
 {
 #pragma unroll
@@ -463,6 +482,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
                                                  float (*res)[kChunk], SegmentDone&& segment_done)
 {
     const ColumnGeometry gm = column_geometry<kSharded, kParts>(p);
+    const int slot = split_slot();
     const int lane = threadIdx.x;
     const int r16 = lane & 15;
     const int g = lane >> 4;
@@ -481,8 +501,8 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
                            : 0;
         const int incl = wave_inclusive_scan(gb, lane);
         const int64_t total = __shfl(incl, 63);
-        g_lo = total * (int64_t)blockIdx.x / gridDim.x;
-        g_hi = total * ((int64_t)blockIdx.x + 1) / gridDim.x;
+        g_lo = total * (int64_t)slot / gridDim.x;
+        g_hi = total * ((int64_t)slot + 1) / gridDim.x;
         if (g_lo >= g_hi)
             return;
         const int l = __ffsll((unsigned long long)__ballot(incl > g_lo)) - 1;
@@ -498,8 +518,8 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
                                : 0;
             total += wave_sum(gb);
         }
-        g_lo = total * (int64_t)blockIdx.x / gridDim.x;
-        g_hi = total * ((int64_t)blockIdx.x + 1) / gridDim.x;
+        g_lo = total * (int64_t)slot / gridDim.x;
+        g_hi = total * ((int64_t)slot + 1) / gridDim.x;
         if (g_lo >= g_hi)
             return;
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
