@@ -33,7 +33,9 @@ steps, fills included, with a synchronize on both sides.
 Prints one JSON line. `value` is scored keys/s, i.e. the sum of seq_len over
 the mean step time. `roofline` rates the scorer, the dominant kernel, against
 HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
-`roofline.stream_read_probe` times msa_stream_read_probe, a plain streaming
+`roofline.mfma` is the scorer's MFMA work and busy fraction from rocprofv3
+counters (committed under profiles/, valid while the scorer's source hash
+matches). `roofline.stream_read_probe` times msa_stream_read_probe, a plain streaming
 read with no other work, over as many index-K bytes in the same way: the
 streaming ceiling the scorer's rate is read against. `cpu_baseline` times the oracle on the
 same workload.
@@ -55,6 +57,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30           # read before each step; > 256 MB Infinity Cache
 COPY_BYTES = 512 << 20          # calibration copy: reads and writes this many bytes
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_score_decode_long_b4_s1m.json")
+MFMA_FILE = os.path.join(HERE, "profiles", "mfma_score_decode_long_b4_s1m.json")
 KERNEL_SOURCES = [os.path.join(HERE, "sparse_attention_block_msa_amd", "csrc", f)
                   for f in ("score_decode.hip", "msa_internal.h")]
 
@@ -87,6 +90,20 @@ def load_traffic(launch_bytes: int):
             "total_bytes": t["fetch_bytes"] + t["write_bytes"],
             "vs_algorithmic": round((t["fetch_bytes"] + t["write_bytes"]) / launch_bytes, 4),
             "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, HERE)}
+
+
+def load_mfma():
+    """The scorer's MFMA counters (flops, busy fraction) from the committed
+    summary, or None when it is missing or the kernel source changed."""
+    try:
+        with open(MFMA_FILE) as f:
+            m = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if m.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {"flops_per_launch": m["mfma_flops"], "mfma_busy_frac": m["mfma_util"],
+            "source": os.path.relpath(MFMA_FILE, HERE)}
 
 
 CPU_BASELINE_MIN_S = 10.0  # repeat whole passes until this much CPU time is spent
@@ -438,6 +455,7 @@ def main():
                      "launch_ms": score_b2b_ms,
                      "launch_ms_source": "K scorer launches back to back between one event pair",
                      "traffic": load_traffic(launch_bytes),
+                     "mfma": load_mfma(),
                      "stream_read_probe": {
                          "what": "msa_stream_read_probe over as many index-K bytes, pages "
                                  "in storage order: a plain streaming read with no other work",
