@@ -11,7 +11,10 @@ request), page size, decode_query_len, number of column ranges (up to 16, or
 * msa_top16_select_merge (where the one-launch form applies): bit for bit the
   two-launch rows, with and without the range rows;
 * msa_score_select then msa_top16_merge: bit for bit the plane and rows of
-  the separate launches.
+  the separate launches;
+* the row-sharded chain over world size 2 or 4 (every rank's
+  msa_score_decode_sharded and msa_top16_select_mapped, then
+  msa_top16_merge_dedup of all ranks' rows): bit for bit the merged rows.
 """
 from __future__ import annotations
 
@@ -22,7 +25,7 @@ import torch
 import oracle
 import sparse_attention_block_msa_amd as msa
 import workloads
-from oracle_pins import CANARY_BITS
+from oracle_pins import CANARY_BITS, shard_index_map
 from parity import assert_rows_equal, compare_plane, written_mask
 
 pytestmark = pytest.mark.gpu
@@ -66,12 +69,13 @@ def draw_case(seed):
     R = int(rng.integers(1, min(17, w.cols + 1)))
     if seed % 6 == 3:  # more ranges than the one-launch forms take
         R = int(rng.integers(17, min(100, w.cols + 1)))
-    return w, R
+    ws = int(rng.choice([2, 4]))
+    return w, R, ws
 
 
 @pytest.mark.parametrize("seed", range(48))
 def test_random_chain(seed):
-    w, R = draw_case(seed)
+    w, R, ws = draw_case(seed)
     T, cols = w.num_tokens, w.cols
     say(f"[test] random case {seed}: batch {w.batch} page {w.page_size} dql {w.dql} "
         f"cols {cols} R {R} init {w.init_blocks} local {w.local_blocks}")
@@ -130,12 +134,12 @@ def test_random_chain(seed):
             if fpart is not None:
                 assert torch.equal(fpart, part)
 
-        ws = msa.score_select_workspace(w.batch, R, device=DEV)
+        counters = msa.score_select_workspace(w.batch, R, device=DEV)
         plane2 = torch.full((T, 4, cols), int(CANARY_BITS), dtype=torch.int32,
                             device=DEV).view(torch.float32)
         part2 = msa.new_rows(T, 4, R, device=DEV)
         part2.fill_(ROW_FILL)
-        msa.msa_score_select(q, k, bt, sl, plane2, nvp, part2, ws, page_size=w.page_size,
+        msa.msa_score_select(q, k, bt, sl, plane2, nvp, part2, counters, page_size=w.page_size,
                              decode_query_len=w.dql, num_ranges=R, errors=err, **kw)
         final2 = msa.new_rows(T, 4, device=DEV)
         final2.fill_(ROW_FILL)
@@ -145,4 +149,30 @@ def test_random_chain(seed):
         assert torch.equal(plane2.view(torch.int32), plane.view(torch.int32))
         assert torch.equal(part2, part)
         assert torch.equal(final2, final)
-        assert int(ws.count_nonzero()) == 0
+        assert int(counters.count_nonzero()) == 0
+
+    # the row-sharded chain: every rank's share, then the owner's merge
+    pages = -(-int(w.seq_lens.max()) // w.page_size)
+    scols = max(4, -(-pages // 4) * 4)
+    rs = min(R, scols)
+    if ws * rs <= 64:
+        rows = msa.new_rows(T, 4, ws * rs, device=DEV)
+        rows.fill_(ROW_FILL)
+        for rank in range(ws):
+            shard = workloads.shard_rows(w.index_k, rank, ws).to(DEV)
+            splane = torch.full((T, 4, scols), int(CANARY_BITS), dtype=torch.int32,
+                                device=DEV).view(torch.float32)
+            msa.msa_score_decode_sharded(q, shard, bt, sl, splane, page_size=w.page_size,
+                                         decode_query_len=w.dql, rank=rank, world_size=ws,
+                                         errors=err)
+            scale, offset = shard_index_map(w.page_size, rank, ws)
+            spart = msa.new_rows(T, 4, rs, device=DEV)
+            msa.msa_top16_select_mapped(splane, nvp, spart, num_ranges=rs, index_scale=scale,
+                                        index_offset=offset, errors=err, **kw)
+            rows[:, :, rank * rs:(rank + 1) * rs] = spart
+        merged = msa.new_rows(T, 4, device=DEV)
+        merged.fill_(ROW_FILL)
+        msa.msa_top16_merge_dedup(rows, nvp, merged, errors=err, **kw)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(merged, final), f"sharded chain ws {ws} case {seed}"
