@@ -2,18 +2,17 @@
 
 One step = the whole chain on one batch of the long-context workload
 (4 requests x 1,048,576 keys, page_size 256, decode_query_len 8,
-plane 32 x 4 x 8192, Top16 over 8 column ranges, then the merge):
+plane 32 x 4 x 8192, Top16 over 8 column ranges, the per-range lists merged
+by msa_top16_merge):
 
-    msa_score_decode -> msa_top16_select_merge (select over R=8 ranges and
-                        the merge in one launch; the range rows stay in LDS)
+    msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
 
-(for more than 16 ranges or ranges wider than 2048 columns, where the
-one-launch form does not apply, the step is the three-launch chain below).
-Two other forms of the same step are timed beside it: the three-launch
-chain msa_score_decode -> msa_top16_select -> msa_top16_merge
-(e2e.three_launch_chain; its per-kernel times are e2e.kernels_ms), and the
-plane with the per-range rows in one launch followed by the merge
-(msa_score_select -> msa_top16_merge; e2e.score_select_then_merge). One rank's share of the same workload on a
+Two other forms of the same step, with bit-identical rows, are timed beside
+it: select and merge in one launch (msa_score_decode ->
+msa_top16_select_merge, the range rows kept in LDS;
+e2e.one_launch_select_merge), and the plane with the per-range rows in one
+launch followed by the merge (msa_score_select -> msa_top16_merge;
+e2e.score_select_then_merge). One rank's share of the same workload on a
 cache split by rows over 2 or 4 ranks (msa_score_decode_sharded ->
 msa_top16_select_mapped, then the owner's msa_top16_merge_dedup) is
 reported under e2e.sharded_rank_share.
@@ -210,15 +209,14 @@ def main():
     # select and merge in one launch where that form applies (at most 16
     # ranges of at most 2048 columns)
     fused_applies = 1 < R <= 16 and -(-w.cols // R) <= 2048
-    step_main = step_fused if fused_applies else step
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         if not args.no_flush:
             flush.sum()
-        step_main()
+        step()
         if fused_applies:
-            step()
+            step_fused()
     torch.cuda.synchronize()
 
     # Timed region 1 (the headline): K steps, an event pair around each step
@@ -232,25 +230,25 @@ def main():
         if not args.no_flush:
             flush.sum()
         step_events[i][0].record(stream)
-        step_main()
+        step()
         step_events[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    # Timed region 1b: the same K steps as the three-launch chain (score,
-    # select, merge), reported beside the headline.
-    chain_ms = None
+    # Timed region 1b: the same K steps with select and merge in one launch
+    # (msa_top16_select_merge), reported beside the headline.
+    fused_ms = None
     if fused_applies:
-        chain_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fused_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                         for _ in range(args.steps)]
         for i in range(args.steps):
             if not args.no_flush:
                 flush.sum()
-            chain_events[i][0].record(stream)
-            step()
-            chain_events[i][1].record(stream)
+            fused_events[i][0].record(stream)
+            step_fused()
+            fused_events[i][1].record(stream)
         torch.cuda.synchronize()
-        chain_ms = sum(ev[0].elapsed_time(ev[1]) for ev in chain_events) / args.steps
+        fused_ms = sum(ev[0].elapsed_time(ev[1]) for ev in fused_events) / args.steps
 
     # Timed region 1c: the same K steps with the plane and the range rows from
     # one launch (msa_score_select), then msa_top16_merge; reported beside the
@@ -344,7 +342,7 @@ def main():
                 "owner_merge_ms": merge_ms, "merged_rows_per_head": ws_n * R}
             del shard, splane, spart, all_rows, merged
 
-    # Timed region 2: K three-launch steps with an event between every kernel,
+    # Timed region 2: K steps with an event between every kernel,
     # for per-kernel durations (the events themselves lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps per kernel", file=sys.stderr, flush=True)
@@ -426,9 +424,8 @@ def main():
                    "ranges": R, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
                    "index_k_bytes": launch_bytes, "parallelism": "single-gpu",
                    "cache_flush_between_steps": not args.no_flush},
-        "e2e": {"step": ("msa_score_decode -> msa_top16_select_merge" if fused_applies else
-                         "msa_score_decode -> msa_top16_select" +
-                         (" -> msa_top16_merge" if R > 1 else "")),
+        "e2e": {"step": "msa_score_decode -> msa_top16_select" +
+                        (" -> msa_top16_merge" if R > 1 else ""),
                 "hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
                 "step_ms_p10": step_ms[len(step_ms) // 10],
                 "step_ms_p50": step_ms[len(step_ms) // 2],
@@ -437,10 +434,10 @@ def main():
                                "top16_merge": mean(merge_ms)},
                 "score_decode_ms_back_to_back": score_b2b_ms,
                 "step_ms_with_kernel_events": mean([ev[0].elapsed_time(ev[3]) for ev in events]),
-                "three_launch_chain": None if chain_ms is None else {
-                    "ms_per_step": chain_ms, "keys_per_s": keys / (chain_ms * 1e-3),
-                    "hbm_gbps": launch_bytes / (chain_ms * 1e-3) / 1e9,
-                    "frac_of_peak": launch_bytes / (chain_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "one_launch_select_merge": None if fused_ms is None else {
+                    "ms_per_step": fused_ms, "keys_per_s": keys / (fused_ms * 1e-3),
+                    "hbm_gbps": launch_bytes / (fused_ms * 1e-3) / 1e9,
+                    "frac_of_peak": launch_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                 "score_select_then_merge": None if score_select_ms is None else {
                     "ms_per_step": score_select_ms,
                     "keys_per_s": keys / (score_select_ms * 1e-3),

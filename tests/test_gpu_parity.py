@@ -237,8 +237,8 @@ def test_end_to_end(n):
     assert int(errors.item()) == 0
     if 1 < R <= 16 and -(-w.cols // R) <= 2048:
         # the one-launch select + merge on the same plane: bit-identical
-        # merged rows and range rows, then merged rows alone as the
-        # benchmark's step runs it
+        # merged rows and range rows, then merged rows alone (the form the
+        # benchmark times beside its step)
         fused = msa.new_rows(T, 4, device=DEV)
         fused_part = msa.new_rows(T, 4, R, device=DEV)
         fused.fill_(0x7BADBEEF)
