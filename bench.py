@@ -404,6 +404,7 @@ def main():
     e2e_gbps = launch_bytes / (ms_step * 1e-3) / 1e9
     score_mean = mean(score_ms)
     achieved = launch_bytes / (score_b2b_ms * 1e-3) / 1e9
+    traffic = load_traffic(launch_bytes)  # HBM bytes per launch, from the committed counters
     probe_gbps = probe_bytes / (probe_ms * 1e-3) / 1e9
 
     out = {
@@ -451,7 +452,8 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "launch_ms": score_b2b_ms,
                      "launch_ms_source": "K scorer launches back to back between one event pair",
-                     "traffic": load_traffic(launch_bytes),
+                     "traffic": None if traffic is None else traffic["total_bytes"],
+                     "traffic_detail": traffic,
                      "mfma": load_mfma(),
                      "stream_read_probe": {
                          "what": "msa_stream_read_probe over as many index-K bytes, pages "
