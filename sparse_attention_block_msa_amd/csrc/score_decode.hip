@@ -16,10 +16,13 @@
 //    of 4-column groups (score_wave_range). A wave converts the Q tile of the
 //    request it is in (4*dql <= 32 rows of 128 fp8 bytes) to bf16 once and
 //    keeps it in registers as the B operand of the MFMA. Small batches use
-//    single columns as the unit instead (latency mode).
+//    single columns as the unit instead (latency mode). Waves take their
+//    ranges in an XCD-aware order (split_slot), so each of the device's XCDs
+//    works on one contiguous eighth of the groups.
 //  * A B128 block is 128 keys x 128 bytes = 16 KiB, contiguous inside one
 //    page. It is staged through a per-wave 4 KiB LDS tile in four pieces of
-//    32 keys with global_load_lds_dwordx4 (latency mode: one 16 KiB piece):
+//    32 keys with global_load_lds_dwordx4 (latency mode: one 16 KiB piece;
+//    row-sharded columns of 64 or 128 rows: 64-row pieces):
 //    each DMA instruction moves 1 KiB of whole 128-byte rows (a fully
 //    contiguous, non-temporal read), and the per-lane source addresses are
 //    chosen so the tile lands XOR-swizzled, letting the MFMA-layout
