@@ -64,6 +64,8 @@ class Oracle:
         lib.oracle_top16_select_mapped.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -85,6 +87,10 @@ class Oracle:
         e = np.empty(n, dtype=np.float64)
         self.lib.oracle_dots(_ptr(q), _ptr(k), n, _ptr(f), _ptr(e))
         return f, e
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads later plane calls may use (takes effect at once)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def num_threads(self) -> int:
         """OpenMP threads the plane functions use."""

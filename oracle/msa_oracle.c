@@ -163,6 +163,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sets the threads later plane calls may use (OpenMP); n >= 1. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Score plane.                                                              */
 /* ------------------------------------------------------------------------ */
