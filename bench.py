@@ -443,6 +443,8 @@ def main():
         "e2e": {"step": "msa_score_decode -> msa_top16_select" +
                         (" -> msa_top16_merge" if R > 1 else ""),
                 "hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
+                # each key is scored against its request's 4 * dql query rows
+                "dot_products_per_s": value * 4 * w.dql,
                 "step_ms_p10": step_ms[len(step_ms) // 10],
                 "step_ms_p50": step_ms[len(step_ms) // 2],
                 "step_ms_p90": step_ms[(len(step_ms) * 9) // 10],
