@@ -399,3 +399,34 @@ def test_stream_read_probe_reads_every_byte(blocks):
     msa.msa_stream_read_probe(host.to(DEV), sink)
     torch.cuda.synchronize()
     assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
+
+
+def test_scorer_latency_mode_large_batch():
+    """300 short requests on a 4-column plane: batch x cols = 1200 puts the
+    scorer in its one-column-per-wave mode while the batch needs the
+    two-pass request search (more than 64 requests); the fused score+select
+    takes the same mode and must agree bit for bit."""
+    w = workloads.generate(batch=300, seq=("loguniform", 1, 512), page_size=128, dql=2,
+                           seed=93, cols=4)
+    assert w.batch * w.cols <= 2048
+    got, err = run_scorer(w, w.cols)
+    assert err == 0
+    check_plane(w, got, w.cols)
+    T = w.num_tokens
+    plane = torch.full((T, 4, w.cols), int(CANARY_BITS), dtype=torch.int32,
+                       device=DEV).view(torch.float32)
+    rows = msa.new_rows(T, 4, 2, device=DEV)
+    ws = msa.score_select_workspace(w.batch, 2, device=DEV)
+    e2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_score_select(w.index_q.to(DEV), w.index_k.to(DEV), w.block_table.to(DEV),
+                         w.seq_lens.to(DEV), plane, w.num_valid_pages.to(DEV), rows, ws,
+                         page_size=128, decode_query_len=2, init_blocks=1, local_blocks=1,
+                         num_ranges=2, errors=e2)
+    ref_rows = msa.new_rows(T, 4, 2, device=DEV)
+    msa.msa_top16_select(torch.from_numpy(got).to(DEV), w.num_valid_pages.to(DEV), ref_rows,
+                         init_blocks=1, local_blocks=1, num_ranges=2, errors=e2)
+    torch.cuda.synchronize()
+    assert int(e2.item()) == 0
+    assert np.array_equal(plane.cpu().numpy().view(np.uint32), got.view(np.uint32))
+    assert torch.equal(rows, ref_rows)
+    assert int(ws.count_nonzero()) == 0
