@@ -491,6 +491,55 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     const int g = lane >> 4;
     const int rows = p.dql * kHeads;
 
+    // Latency mode with one wave per (request, column) of the plane: the wave
+    // knows its column without the prefix pass over seq_lens, so its
+    // sequence length, Q tile and block-table entry load together.
+    if constexpr (kUnit == 1 && !kSharded) {
+        if ((int64_t)gridDim.x == (int64_t)p.batch * p.cols) {
+            const int b = (int)(blockIdx.x / p.cols);
+            const int c = (int)(blockIdx.x % p.cols);
+            const int64_t row_base = (int64_t)b * rows;
+            const int pidx = c >> gm.col_shift;
+            int entry = -1;
+            if (pidx < p.bt_stride)  // inside the table's row: safe to read early
+                entry = p.bt[(int64_t)b * p.bt_stride + pidx];
+            v8i qraw[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const int rho = n * 16 + r16;
+                qraw[n] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                if (rho < rows)
+                    qraw[n] = load_row_slice(p.q + (row_base + rho) * kDim, g);
+            }
+            const int seq = p.seq_lens[b];
+            bool clamped;
+            const int wcols = written_cols(seq, p.cols, clamped, gm.col_stride);
+            if (c >= wcols)
+                return;
+            if (clamped && c == 0 && lane == 0 && p.errors)
+                atomicAdd(p.errors, 1);
+            const int nblk = key_columns(seq, gm);
+            // the entry counts only for a column with keys, as the window
+            // loads would have read it
+            const bool bad = c < nblk && (pidx >= p.bt_stride || entry < 0 ||
+                                          (int64_t)entry >= p.num_pages);
+            WindowPages wp;
+            wp.page = bad ? 0 : entry;
+            wp.bad_mask = __ballot(bad && lane == 0);
+            Bf16Slice qb[NT];
+            int pos[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                pos[n] = seq - p.dql + ((n * 16 + r16) >> 2);
+                qb[n] = to_bf16(qraw[n]);
+            }
+            score_window<NT, kParts, kDeviceScope, kUnit>(p, gm, b, seq, nblk, c, c + 1, wp, qb,
+                                                          pos, tile, res, lane, r16, g);
+            segment_done(b, c, c + 1);
+            return;
+        }
+    }
+
     // Groups of all requests, this wave's range [g_lo, g_hi), the request b
     // holding g_lo and the groups before it (base). One pass over seq_lens
     // when the batch fits one wave, two otherwise.
