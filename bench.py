@@ -172,7 +172,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: the indexer runs on one GPU (got --gpus {args.gpus}); "
               "there is no multi-GPU path to measure", file=sys.stderr)
         sys.exit(2)
 
