@@ -386,7 +386,10 @@ def main():
     # Timed region 3b: the streaming-read probe (a plain read, no other work)
     # over as many index-K bytes, timed the same way: the streaming ceiling
     # the scorer's rate is read against.
-    probe_bytes = workloads.index_k_bytes(w)  # the first pages, in storage order
+    # as many bytes as the scorer's algorithmic read, in whole 16 KiB blocks
+    # from the start of the cache (pages in storage order)
+    probe_bytes = max(16384, workloads.index_k_bytes(w) // 16384 * 16384)
+    probe_bytes = min(probe_bytes, k.numel() // 16384 * 16384)
     sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
     msa.msa_stream_read_probe(k, sink, nbytes=probe_bytes, stream=stream)
     if not args.no_flush:
