@@ -105,6 +105,25 @@ def load_mfma():
             "source": os.path.relpath(MFMA_FILE, HERE)}
 
 
+def cpu_host() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs of the
+    machine (os.cpu_count) and those this process may run on (nproc)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "nproc": nproc}
+
+
 CPU_BASELINE_MIN_S = 10.0  # repeat whole passes until this much CPU time is spent
 CPU_BASELINE_MAX_PASSES = 30
 
@@ -149,13 +168,62 @@ def cpu_baseline(w):
     one = time.perf_counter() - t0
     orc.set_num_threads(cores)
     return {"value": keys * passes / total, "unit": "keys/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "host": cpu_host(),
             "sample": f"{passes} whole passes over the workload ({keys} keys each): score "
                       f"{score_s / passes:.2f} s, then Top16 select over {w.num_ranges} ranges "
                       f"and merge {select_s / passes:.2f} s, per pass",
             "seconds": round(total, 2),
             "single_thread": {"value": keys / one, "unit": "keys/s", "cores": 1,
                               "sample": "one whole pass over the workload", "seconds": round(one, 2)}}
+
+
+def mfma_accuracy(tiles: int = 2048, seed: int = 77) -> dict:
+    """Accumulation error of the three MFMA forms of msa_contraction_probe
+    on 128-dim fp8 dot products (tiles x 16 x 16 of them per distribution),
+    against exact float64 sums of torch-decoded codes (every finite e4m3fn
+    code is a multiple of 2^-9 below 2^9, so each sum is a multiple of 2^-18
+    below 2^43, which float64 holds exactly)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_block_msa_amd as msa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    forms = {"bf16 16x16x32 x4 (the scorer's form)": msa.PROBE_BF16,
+             "fp8 16x16x32 x4": msa.PROBE_FP8_16X16X32,
+             "f8f6f4 16x16x128 x1": msa.PROBE_F8F6F4_16X16X128}
+    g = torch.Generator().manual_seed(seed)
+    shape = (tiles, 16, 128)
+
+    def normal(scale):
+        return (torch.randn(shape, generator=g) * scale).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    def codes():
+        return workloads.FINITE_CODES[torch.randint(0, 254, shape, generator=g)]
+
+    dists = {"q, k ~ N(0,1) -> e4m3fn": (normal(1.0), normal(1.0)),
+             "q, k uniform over the 254 finite codes": (codes(), codes()),
+             "q ~ N(0,1), k ~ N(0,64) -> e4m3fn": (normal(1.0), normal(8.0))}
+    result = {"what": "max |err| / sum|q_i k_i| of 128-dim fp8 dot products, and how many "
+                      "exceed 1e-5", "dots_per_distribution": tiles * 256, "seed": seed,
+              "results": {}}
+    out = torch.empty((tiles, 16, 16), dtype=torch.float32, device=dev)
+    for dname, (q, k) in dists.items():
+        qd = q.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        kd = k.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        exact = np.einsum("tid,tjd->tij", qd, kd)
+        absum = np.einsum("tid,tjd->tij", np.abs(qd), np.abs(kd))
+        qg, kg = q.to(dev), k.to(dev)
+        row = {}
+        for fname, form in forms.items():
+            msa.msa_contraction_probe(qg, kg, out, form=form)
+            torch.cuda.synchronize()
+            rel = np.abs(out.cpu().numpy().astype(np.float64) - exact) / np.maximum(absum, 1e-300)
+            row[fname] = {"max_rel_err": float(rel.max()),
+                          "over_1e-5": int(np.count_nonzero(rel > 1e-5))}
+        result["results"][dname] = row
+    return result
 
 
 def main():
@@ -166,6 +234,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload number (1..5)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting read pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-accuracy", action="store_true",
+                    help="only measure the accumulation error of the fp8 and bf16 MFMA forms "
+                         "(msa_contraction_probe) and print it as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, copy a 512 MiB buffer once (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -175,6 +246,10 @@ def main():
         print(f"bench.py: the indexer runs on one GPU (got --gpus {args.gpus}); "
               "there is no multi-GPU path to measure", file=sys.stderr)
         sys.exit(2)
+
+    if args.mfma_accuracy:
+        print(json.dumps(mfma_accuracy()), flush=True)
+        return
 
     import torch
 

@@ -336,6 +336,28 @@ int msa_warmup(void);
 int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
+ * Measurement aid, not a step of the indexer: no page defines it. The pages
+ * give fp8 inputs and fp32 scores ("msa_icp_decode_index_score_sharded",
+ * index_q / index_k / score_out); this call measures how three gfx950 MFMA
+ * forms accumulate 128-dim fp8 dot products, which decides the form the
+ * scorer contracts in:
+ *   MSA_PROBE_BF16             the scorer's form: codes converted exactly to
+ *                              bf16, four v_mfma_f32_16x16x32_bf16 chained;
+ *   MSA_PROBE_FP8_16X16X32     four v_mfma_f32_16x16x32_fp8_fp8 chained;
+ *   MSA_PROBE_F8F6F4_16X16X128 one v_mfma_f32_16x16x128_f8f6f4 (e4m3, unscaled).
+ *
+ * q, k   device, e4m3fn bytes [tiles, 16, 128], contiguous, 16-byte aligned.
+ * out    device float32 [tiles, 16, 16]: out[t, i, j] = q[t, i, :] . k[t, j, :].
+ * Returns MSA_OK, MSA_ERR_INVALID_ARG (null or misaligned pointer, tiles outside
+ * [1, 2^31), unknown form; nothing launched) or MSA_ERR_LAUNCH.
+ */
+#define MSA_PROBE_BF16 0
+#define MSA_PROBE_FP8_16X16X32 1
+#define MSA_PROBE_F8F6F4_16X16X128 2
+int msa_contraction_probe(const uint8_t* q, const uint8_t* k, int64_t tiles, int32_t form,
+                          float* out, hipStream_t stream);
+
+/*
  * Text of the last failed check or launch of the calling thread. The string
  * is empty if there was none. It stays valid until the thread's next call
  * into the library.

@@ -38,7 +38,13 @@ STREAM_PROBE_SINK_WORDS = 1024  # MSA_STREAM_PROBE_SINK_WORDS
 
 EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
-           "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe")
+           "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe",
+           "msa_contraction_probe")
+
+# MFMA forms of msa_contraction_probe (MSA_PROBE_* in msa_indexer.h)
+PROBE_BF16 = 0
+PROBE_FP8_16X16X32 = 1
+PROBE_F8F6F4_16X16X128 = 2
 
 
 class MsaError(RuntimeError):
@@ -88,6 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_warmup.restype = ctypes.c_int
     lib.msa_stream_read_probe.argtypes = [P, i64, P, P]
     lib.msa_stream_read_probe.restype = ctypes.c_int
+    lib.msa_contraction_probe.argtypes = [P, P, i64, i32, P, P]
+    lib.msa_contraction_probe.restype = ctypes.c_int
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -176,6 +184,23 @@ def msa_stream_read_probe(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int 
           sink.is_contiguous(), f"sink: contiguous int32 [>= {STREAM_PROBE_SINK_WORDS}]")
     _check(load().msa_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(),
                                         _stream_handle(stream)))
+
+
+def msa_contraction_probe(q: torch.Tensor, k: torch.Tensor, out: torch.Tensor, *, form: int,
+                          stream=None) -> None:
+    """Measurement aid: out[t, i, j] = q[t, i, :] . k[t, j, :] for e4m3fn codes
+    q, k [tiles, 16, 128], through the MFMA form `form` (PROBE_*); out is
+    float32 [tiles, 16, 16]."""
+    q = _u8(q, "q")
+    k = _u8(k, "k")
+    _dev(q, k, out)
+    _need(q.dim() == 3 and q.shape[1:] == (16, HEAD_DIM) and q.is_contiguous(),
+          "q: contiguous [tiles, 16, 128]")
+    _need(k.shape == q.shape and k.is_contiguous(), "k: contiguous, shaped like q")
+    _need(out.dtype == torch.float32 and out.shape == (q.shape[0], 16, 16) and
+          out.is_contiguous(), "out: contiguous float32 [tiles, 16, 16]")
+    _check(load().msa_contraction_probe(q.data_ptr(), k.data_ptr(), q.shape[0], int(form),
+                                        out.data_ptr(), _stream_handle(stream)))
 
 
 def _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,

@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include "contraction_probe.h"
 #include "msa_internal.h"
 #include "stream_probe.h"
 
@@ -367,6 +368,22 @@ int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStr
                                                        bytes / msa::kProbeBlockBytes, sink,
                                                        stream),
                          fn);
+}
+
+int msa_contraction_probe(const uint8_t* q, const uint8_t* k, int64_t tiles, int32_t form,
+                          float* out, hipStream_t stream)
+{
+    static const char* fn = "msa_contraction_probe";
+    g_last_error[0] = '\0';
+    MSA_CHECK(q && k && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(q, 16) && aligned(k, 16) && aligned(out, 4),
+              "%s: q and k must be 16-byte aligned, out 4-byte aligned", fn);
+    MSA_CHECK(tiles >= 1 && tiles <= 0x7FFFFFFF, "%s: tiles (%lld) must be in [1, 2^31)", fn,
+              (long long)tiles);
+    MSA_CHECK(form == MSA_PROBE_BF16 || form == MSA_PROBE_FP8_16X16X32 ||
+                  form == MSA_PROBE_F8F6F4_16X16X128,
+              "%s: unknown form %d", fn, form);
+    return launch_result(msa::launch_contraction_probe(q, k, tiles, form, out, stream), fn);
 }
 
 int msa_warmup(void)

@@ -121,15 +121,25 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
                                        dst->id[slot] = id;
                                    });
     pad_row(dst, kept, lane);
+    // More than 16 kept entries: a forced id repeated in the input (rows
+    // that are not disjoint ranges); the row holds the first 16.
+    bool overflow = kept > kTop;
 
     int found_forced = n_forced;
     if (NW > 1) {
+        if (overflow && lane == 0 && p.errors)
+            atomicAdd(p.errors, 1);
+        overflow = false;
         __syncthreads();
-        if (wave == 0)
+        if (wave == 0) {
+            int kept_m = 0;
             found_forced = merge_lds_rows<NW>(part, n, p.init_blocks, p.local_blocks,
-                                              kTop - expected_forced, p.out + th, lane);
+                                              kTop - expected_forced, p.out + th, lane, &kept_m);
+            overflow = kept_m > kTop;
+        }
     }
-    if ((NW == 1 || wave == 0) && found_forced < expected_forced && lane == 0 && p.errors)
+    if ((NW == 1 || wave == 0) && (found_forced < expected_forced || overflow) && lane == 0 &&
+        p.errors)
         atomicAdd(p.errors, 1);
 }
 

@@ -178,7 +178,9 @@ __device__ __forceinline__ int count_keys(const uint32_t (&u)[V])
 // candidates (count_keys). Keeps all forced elements and the best
 // min(budget, n_cand) candidates, and calls emit(i, slot) for each kept
 // element, slots ascending in element order. Returns the number of kept
-// elements (uniform).
+// elements (uniform). Only slots below kTop are emitted: more than kTop kept
+// elements (forced entries repeated in malformed merge input) return a count
+// above kTop, which callers report, and never write past a row.
 template <int V, class Emit>
 __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbits, int budget,
                                            int n_cand, Emit&& emit)
@@ -220,8 +222,9 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
         const bool take = ((fbits >> i) & 1ull) ||
                           (K > 0 && (u[i] > thr || (tie && tie_base + lanes_below(tie_mask) < need)));
         const uint64_t take_mask = __ballot(take);
-        if (take)
-            emit(i, base + lanes_below(take_mask));
+        const int slot = base + lanes_below(take_mask);
+        if (take && slot < kTop)
+            emit(i, slot);
         base += __popcll(take_mask);
         tie_base += __popcll(tie_mask);
     }
@@ -229,12 +232,13 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
 }
 
 // Compaction buffer of one wave: up to 64 entries (key, raw score, id).
+// In wave_select_filtered's buffer a forced entry has key 0, every other
+// entry a key >= 1, so ids keep all 31 bits.
 struct Candidate {
     uint32_t key;
     float score;
-    int id;  // bit 30: forced
+    int id;
 };
-constexpr int kForcedFlag = 1 << 30;
 
 // Wave-level select, same contract as wave_select, for V > 1 values per lane.
 // Elements are (u[i], sv[i], id_of(i)). Every key of the best K is >= theta,
@@ -268,7 +272,7 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
             Candidate c;
             c.key = forced ? 0u : u[i];
             c.score = sv[i];
-            c.id = id_of(i) | (forced ? kForcedFlag : 0);
+            c.id = id_of(i);
             buf[slot] = c;
         }
         base += __popcll(mask);
@@ -286,9 +290,9 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint32_t u1[1] = {mine.key};
-    const uint64_t f1 = (lane < base && (mine.id & kForcedFlag)) ? 1ull : 0ull;
+    const uint64_t f1 = (lane < base && mine.key == 0u) ? 1ull : 0ull;
     return wave_select<1>(u1, f1, budget, n_cand,
-                          [&](int, int slot) { emit(mine.score, mine.id & ~kForcedFlag, slot); });
+                          [&](int, int slot) { emit(mine.score, mine.id, slot); });
 }
 
 #ifndef MSA_SELECT_DIRECT_MAX_V
@@ -319,11 +323,13 @@ __device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
 // Second level of a split row: the NW partial rows in LDS are merged by wave
 // 0 into `out`. Forced ids are recomputed from (n, init, local). The
 // candidate budget is `budget`, or 16 - (forced entries found) if budget < 0.
-// Returns the number of forced entries found (uniform in wave 0).
+// Returns the number of forced entries found (uniform in wave 0); *kept_out
+// receives the number of entries kept (above kTop only for repeated forced
+// ids in malformed input; then only the first kTop are written).
 template <int NW>
 __device__ __forceinline__ int merge_lds_rows(const msa_top16_row* part, int n, int init_blocks,
                                               int local_blocks, int budget, msa_top16_row* out,
-                                              int lane)
+                                              int lane, int* kept_out = nullptr)
 {
     static_assert(NW * kTop <= 64, "partial rows must fit one wave");
     uint32_t u[1] = {0u};
@@ -347,6 +353,8 @@ __device__ __forceinline__ int merge_lds_rows(const msa_top16_row* part, int n, 
         out->id[slot] = id;
     });
     pad_row(out, kept, lane);
+    if (kept_out)
+        *kept_out = kept;
     return n_forced;
 }
 

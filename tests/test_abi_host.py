@@ -314,3 +314,15 @@ def test_probe_sink_words_match_header():
     text = open(HEADER).read()
     m = re.search(r"#define MSA_STREAM_PROBE_SINK_WORDS (\d+)", text)
     assert m and int(m.group(1)) == msa.STREAM_PROBE_SINK_WORDS
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, FAKE, 4, 0, FAKE), "null"),
+    ((FAKE, FAKE + 8, 4, 0, FAKE), "aligned"),
+    ((FAKE, FAKE, 0, 0, FAKE), "tiles"),
+    ((FAKE, FAKE, 4, 3, FAKE), "form"),
+    ((FAKE, FAKE, 4, -1, FAKE), "form"),
+])
+def test_contraction_probe_rejects(lib, args, needle):
+    assert lib.msa_contraction_probe(*args, None) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()

@@ -20,7 +20,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_attention_block_msa_amd", "csrc")
-SOURCES = ["msa_abi.hip", "score_decode.hip", "top16.hip", "stream_probe.hip"]
+from sparse_attention_block_msa_amd.build import SOURCES  # noqa: E402  (the library's own list)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]

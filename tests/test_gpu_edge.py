@@ -125,6 +125,35 @@ def test_select_and_merge_edge(cols, R, init, local, kind):
     assert_rows_equal(ms, mi, ws[:, :, 0], wi[:, :, 0], f"merge cols={cols} R={R} {kind}")
 
 
+@pytest.mark.parametrize("R", [4, 100])
+def test_merge_repeated_rows_stays_in_its_row(R):
+    """Partial rows that repeat one select row R times (not disjoint column
+    ranges), so every forced id appears R times: the merge counts the
+    malformed input in `errors`, writes a row of at most 16 valid entries
+    and nothing past `out` (R = 100 takes the four-wave path)."""
+    rng = np.random.default_rng(900 + R)
+    T, cols, init, local = 3, 256, 4, 4
+    plane = plane_of(rng, T, cols, "normal")
+    nvp = np.array([cols, 100, 40], dtype=np.int32)
+    _, _, err, rows1, nvp_t = gpu_select(plane, nvp, init, local, 1)
+    assert err == 0
+    rows = rows1.repeat(1, 1, R, 1).contiguous()
+    guard = 4
+    buf = msa.new_rows(T * 4 + guard, device=DEV)
+    buf.fill_(0x7BADBEEF)
+    out = buf[:T * 4].view(T, 4, msa.ROW_WORDS)
+    errs = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_top16_merge(rows, nvp_t, out, init_blocks=init, local_blocks=local, errors=errs)
+    torch.cuda.synchronize()
+    b = buf.cpu()
+    assert torch.all(b[T * 4:] == 0x7BADBEEF), "merge wrote past its output rows"
+    assert int(errs.item()) >= T * 4, "malformed rows not counted"
+    ids = msa.row_ids(b[:T * 4]).numpy()
+    for r, row in enumerate(ids):
+        n = int(nvp[r // 4])
+        assert np.all((row == -1) | ((row >= 0) & (row < n))), f"row {r}: bad ids {row}"
+
+
 @pytest.mark.parametrize("R", [16, 100, 768])
 def test_merge_many_ranges(R):
     """Merge of up to 768 partial rows (12288 entries: the four-wave path)."""

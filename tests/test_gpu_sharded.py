@@ -127,6 +127,10 @@ TIE_POOL = np.array([-np.inf, -1.0, -0.0, 0.0, 0.5, 1.5, 2.0], dtype=np.float32)
     (64, 1, 1, 0, 1, 2), (64, 3, 2, 1, 4, 4), (300, 4, 2, 0, 2, 14), (1000, 1, 2, 1, 1, 4),
     (2047, 2, 2, 1, 16, 0), (4096, 8, 2, 0, 4, 4), (100, 5, 3, 2, 0, 0),
     (4096, 2, 2, 1, 4, 4), (12000, 3, 1, 0, 2, 2),  # ranges over 1024 columns: 4 waves
+    # global ids at and above 2^30 through the filtered (more than 128
+    # columns per range) and the four-wave paths
+    (1000, 1, 1, (1 << 30) + 5, 2, 2), (1000, 2, 2, (1 << 30) + 3, 1, 4),
+    (3000, 1, 1, (1 << 31) - 3011, 4, 4),
 ])
 @pytest.mark.parametrize("ties", [False, True])
 def test_select_mapped_bit_exact(cols, R, scale, offset, init, local, ties):

@@ -25,7 +25,10 @@ Recipe (the same for every configuration; ``seed = 1000 + config number``):
    missing mask shows up as a large score.
 5. Values: ``randn * scale`` cast with torch to float8_e4m3fn (round to
    nearest even), stored as raw uint8 codes. Outlier blocks (configuration 3)
-   are whole B128 blocks of keys multiplied by 8 before the cast.
+   are whole B128 blocks of keys multiplied by 8 before the cast. With
+   ``values="codes"`` every q and k byte is instead drawn uniformly from the
+   254 finite e4m3fn codes (subnormals through +-448 in one dot product: the
+   hardest case for fp32 accumulation).
 6. ``num_valid_pages[t] = floor(pos_t / 128) + 1`` with
    ``pos_t = seq_len - decode_query_len + j`` (for one query token per
    request this is ``ceil(seq_len / 128)``).
@@ -116,11 +119,22 @@ def _to_e4m3_codes(x: torch.Tensor) -> torch.Tensor:
     return codes
 
 
+FINITE_CODES = torch.tensor([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=torch.uint8)
+
+
+def _finite_codes(g: torch.Generator, shape) -> torch.Tensor:
+    """Codes drawn uniformly from the 254 finite e4m3fn codes."""
+    return FINITE_CODES[torch.randint(0, len(FINITE_CODES), shape, generator=g)]
+
+
 def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
              outlier_frac: float = 0.0, init: int = 1, local: int = 2, ranges: int = 1,
              pool=("exact", None), seed: int = 0, name: str = "custom", cols: int | None = None,
-             table_width: int | None = None, chunk_pages: int = 1024) -> Workload:
+             table_width: int | None = None, chunk_pages: int = 1024,
+             values: str = "normal") -> Workload:
     """Draws one workload following the module recipe."""
+    if values not in ("normal", "codes"):
+        raise ValueError(f"unknown value law {values!r}")
     g = torch.Generator().manual_seed(int(seed))
     seq_lens = _draw_seq_lens(g, batch, seq)
     if int(seq_lens.min()) < 0:
@@ -165,11 +179,17 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
                 n_outlier_blocks += 1
 
     T = batch * dql
-    index_q = _to_e4m3_codes(torch.randn((T, HEADS, DIM), generator=g) * scale)
+    if values == "codes":
+        index_q = _finite_codes(g, (T, HEADS, DIM))
+    else:
+        index_q = _to_e4m3_codes(torch.randn((T, HEADS, DIM), generator=g) * scale)
 
     index_k = torch.empty((num_pages, page_size, DIM), dtype=torch.uint8)
     for p0 in range(0, pool_size, chunk_pages):
         p1 = min(pool_size, p0 + chunk_pages)
+        if values == "codes":
+            index_k[p0:p1] = _finite_codes(g, (p1 - p0, page_size, DIM))
+            continue
         x = torch.randn((p1 - p0, page_size, DIM), generator=g) * scale
         if outlier_frac > 0:
             mult = torch.where(outlier[p0:p1], 8.0, 1.0)                 # [n, halves]
@@ -190,7 +210,7 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
                     dql=dql, cols=int(cols), init_blocks=init, local_blocks=local,
                     num_ranges=ranges, poison_page=poison,
                     meta=dict(seed=seed, pool=pool_size, outlier_blocks=n_outlier_blocks,
-                              scale=scale))
+                              scale=scale, values=values))
 
 
 def config(n: int, **overrides) -> Workload:
