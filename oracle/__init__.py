@@ -62,6 +62,9 @@ class Oracle:
         lib.oracle_score_decode_sharded.restype = i64
         lib.oracle_top16_select_mapped.argtypes = [P, i32, i32, P, i32, i32, i32, i32, i32, P]
         lib.oracle_top16_select_mapped.restype = i64
+        lib.oracle_score_prefill.argtypes = [P, P, i64, P, i64, P, P, i32, i32, P, i64, P, i32,
+                                             P]
+        lib.oracle_score_prefill.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -139,6 +142,41 @@ class Oracle:
             _ptr(q), _ptr(k), k.shape[0], _ptr(bt), bt.shape[1], _ptr(sl), page_size,
             decode_query_len, _ptr(r), _ptr(c), n, _ptr(s), _ptr(a))
         return s, a, int(bad)
+
+    def score_prefill(self, index_q, index_k, block_table, qo_indptr, seq_lens, *,
+                      page_size: int, cols: int, tokens=None, plane: np.ndarray | None = None,
+                      want_amax: bool = False):
+        """Prefill score plane: request b's query tokens are rows
+        [qo_indptr[b], qo_indptr[b+1]) of index_q [Tq, 4, 128], token j at
+        position seq_len[b] - q_len_b + j. Returns (plane [n, 4, cols],
+        amax|None, bad) for every token (n = Tq) or for the token rows in
+        `tokens` (in that order); unwritten columns keep `plane`'s values
+        (default NaN)."""
+        q = _c(index_q, np.uint8)
+        k = _c(index_k, np.uint8)
+        bt = _c(block_table, np.int32)
+        qo = _c(qo_indptr, np.int32)
+        sl = _c(seq_lens, np.int32)
+        batch = sl.shape[0]
+        assert qo.shape == (batch + 1,)
+        total = int(qo[-1])
+        assert q.size == total * HEADS * DIM
+        assert k.ndim == 3 and k.shape[1] == page_size and k.shape[2] == DIM
+        tk = None if tokens is None else _c(tokens, np.int64)
+        n = total if tk is None else tk.shape[0]
+        if plane is None:
+            plane = np.full((n, HEADS, cols), np.nan, dtype=np.float32)
+        else:
+            plane = np.array(plane, dtype=np.float32, order="C", copy=True)
+        assert plane.shape == (n, HEADS, cols)
+        amax = np.zeros((n, HEADS, cols), dtype=np.float64) if want_amax else None
+        bad = self.lib.oracle_score_prefill(
+            _ptr(q), _ptr(k), k.shape[0], _ptr(bt), bt.shape[1], _ptr(qo), _ptr(sl), batch,
+            page_size, None if tk is None else _ptr(tk), n, _ptr(plane), cols,
+            _ptr(amax) if want_amax else None)
+        if bad < 0:
+            raise ValueError("oracle_score_prefill: invalid arguments")
+        return plane, amax, int(bad)
 
     def written_columns_sharded(self, seq_len: int, page_size: int) -> int:
         return int(self.lib.oracle_written_columns_sharded(int(seq_len), int(page_size)))
@@ -290,3 +328,7 @@ def score_decode_sharded(*args, **kwargs):
 
 def top16_select_mapped(*args, **kwargs):
     return default().top16_select_mapped(*args, **kwargs)
+
+
+def score_prefill(*args, **kwargs):
+    return default().score_prefill(*args, **kwargs)

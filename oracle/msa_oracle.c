@@ -12,8 +12,9 @@
  *        (written columns), index_q (token positions), index_k, block_table,
  *        seq_lens, score_out (cols limits), page_size limits.
  *   [P2] "flashinfer.msa_ops.prepare_msa_icp_indexer": decode chain
- *        (score plane -> Top16 select -> owner merge); init_blocks/local_blocks
- *        (forced begin/end blocks, sum at most 16).
+ *        (score plane -> Top16 select -> owner merge); the prefill chain
+ *        (window plan -> per-chunk scoring and select -> merge);
+ *        init_blocks/local_blocks (forced begin/end blocks, sum at most 16).
  *   [P3] "flashinfer.msa_ops.msa_icp_topk_select_publish": description (the
  *        row format: sixteen unscaled scores with increasing block ids; all
  *        rows are written on each call, padding rows too); scores (K limit);
@@ -313,6 +314,75 @@ int64_t oracle_score_sampled(const uint8_t* index_q, const uint8_t* index_k, int
         score_out[i] = s;
         if (amax_out)
             amax_out[i] = a;
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Prefill score plane [P2 prefill chain; element definition of P1].         */
+/* ------------------------------------------------------------------------ */
+
+/* The prefill chain of [P2] scores a chunk of query tokens per request: the
+ * query tokens of request b are rows [qo_indptr[b], qo_indptr[b+1]) of
+ * index_q, q_len_b of them, and (as for decode tokens, [P1 index_q]) token j
+ * of the chunk sits at position seq_len[b] - q_len_b + j, its own key being
+ * the chunk's key at that position. Each element is the decode element:
+ * column c of a token's head row is the maximum over the block's keys
+ * p <= pos (p < seq_len) of the exact dot product, -inf if none, written for
+ * c < min(written_columns(seq_len[b]), cols). With q_len_b = decode_query_len
+ * for every request this is oracle_score_decode.
+ *
+ * tokens (nullable): the query-token rows to score, n_tokens of them; the
+ * output then holds those tokens' rows [n_tokens, 4, cols] in that order.
+ * With tokens == NULL every token of the chunk is scored (n_tokens ignored)
+ * into [qo_indptr[batch], 4, cols]. Columns a token does not write are left
+ * as they are. Returns the number of elements that met an out-of-range
+ * block_table entry, or -1 if a token row is outside [0, qo_indptr[batch]) or
+ * qo_indptr decreases. */
+int64_t oracle_score_prefill(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                             const int32_t* block_table, int64_t block_table_stride,
+                             const int32_t* qo_indptr, const int32_t* seq_lens, int32_t batch,
+                             int32_t page_size, const int64_t* tokens, int64_t n_tokens,
+                             float* score_out, int32_t cols, double* amax_out)
+{
+    ensure_table();
+    for (int32_t b = 0; b < batch; ++b)
+        if (qo_indptr[b + 1] < qo_indptr[b] || qo_indptr[0] != 0)
+            return -1;
+    int64_t total = qo_indptr[batch];
+    int64_t n_out = tokens ? n_tokens : total;
+    for (int64_t i = 0; tokens && i < n_out; ++i)
+        if (tokens[i] < 0 || tokens[i] >= total)
+            return -1;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+    for (int64_t i = 0; i < n_out; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        int64_t b = 0;
+        while (qo_indptr[b + 1] <= t)  /* the request whose chunk holds row t */
+            ++b;
+        int64_t q_len = qo_indptr[b + 1] - qo_indptr[b];
+        int64_t j = t - qo_indptr[b];
+        int64_t seq_len = seq_lens[b];
+        int64_t pos = seq_len - q_len + j;
+        int64_t written = oracle_written_columns(seq_len);
+        if (written > cols)
+            written = cols;
+        for (int h = 0; h < ORACLE_HEADS; ++h) {
+            const uint8_t* q_row = index_q + (t * ORACLE_HEADS + h) * ORACLE_DIM;
+            int64_t out_row = i * ORACLE_HEADS + h;
+            for (int64_t c = 0; c < written; ++c) {
+                float sc;
+                double a;
+                if (oracle_score_element(q_row, index_k, num_pages, page_size,
+                                         block_table + b * block_table_stride, seq_len, pos, c,
+                                         &sc, &a) != 0)
+                    ++bad;
+                score_out[out_row * cols + c] = sc;
+                if (amax_out)
+                    amax_out[out_row * cols + c] = a;
+            }
+        }
     }
     return bad;
 }

@@ -594,10 +594,137 @@ def pin_sharded_chain_exact(orc):
         assert np.array_equal(ms.view(np.uint32), ref_s[:, :, 0].view(np.uint32)), w.name
 
 
+# ----------------------------------------------------------------------------
+# prefill chunks ("prepare_msa_icp_indexer", the prefill chain)
+# ----------------------------------------------------------------------------
+
+def brute_force_plane_prefill(index_q, index_k, block_table, qo_indptr, seq_lens, page_size,
+                              cols):
+    """Prefill plane by whole-request matrices: the chunk's Q rows against all
+    the request's keys in position order (float64, exact), an explicit
+    position mask per query token, block max, one rounding to float32.
+    Unwritten entries are NaN, amax alongside."""
+    q = np.asarray(index_q, dtype=np.uint8)
+    k = np.asarray(index_k, dtype=np.uint8)
+    bt = np.asarray(block_table)
+    qo = np.asarray(qo_indptr, dtype=np.int64)
+    sl = np.asarray(seq_lens)
+    T = int(qo[-1])
+    out = np.full((T, 4, cols), np.nan, dtype=np.float32)
+    amax = np.zeros((T, 4, cols), dtype=np.float64)
+    for b in range(sl.shape[0]):
+        s, t0, t1 = int(sl[b]), int(qo[b]), int(qo[b + 1])
+        if s <= 0 or t1 == t0:
+            continue
+        p = np.arange(s)
+        kd = torch_decode(k[bt[b, p // page_size], p % page_size])       # [s, 128]
+        qd = torch_decode(q[t0:t1]).reshape((t1 - t0) * 4, 128)
+        S = qd @ kd.T
+        A = np.abs(qd) @ np.abs(kd).T
+        nblk = -(-s // 128)
+        ncols = min(-(-nblk // 4) * 4, cols)
+        qlen = t1 - t0
+        for r in range((t1 - t0) * 4):
+            j = r // 4
+            pos = s - qlen + j
+            for c in range(ncols):
+                sel = (p <= pos) & (p >= 128 * c) & (p < 128 * c + 128)
+                if sel.any():
+                    out[t0 + j, r % 4, c] = np.float32(S[r, sel].max())
+                    amax[t0 + j, r % 4, c] = A[r, sel].max()
+                else:
+                    out[t0 + j, r % 4, c] = NEG_INF
+    return out, amax
+
+
+def _tiny_prefill_workloads():
+    # short ragged chunks, one of a single token, one at the very start
+    yield workloads.generate(batch=3, seq=("list", [129, 300, 700]), q_lens=("list", [1, 17, 64]),
+                             page_size=128, dql=1, seed=31)
+    # chunks crossing block and page boundaries at P256, one chunk = whole request
+    yield workloads.generate(batch=3, seq=("list", [515, 1000, 130]),
+                             q_lens=("list", [257, 300, 130]), page_size=256, dql=1, seed=32,
+                             outlier_frac=0.05)
+    # an empty chunk and an empty request between non-empty ones, narrow plane
+    yield workloads.generate(batch=4, seq=("list", [640, 0, 383, 900]),
+                             q_lens=("list", [3, 0, 0, 40]), page_size=128, dql=1, seed=33,
+                             cols=12)
+
+
+def _prefill_args(w):
+    return (w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy(), w.qo_indptr.numpy(),
+            w.seq_lens.numpy())
+
+
+def pin_prefill_brute_force(orc):
+    """Prefill oracle plane == whole-request brute force, bit for bit, incl.
+    amax; a token subset returns those tokens' rows."""
+    for w in _tiny_prefill_workloads():
+        args = _prefill_args(w)
+        plane, amax, bad = orc.score_prefill(*args, page_size=w.page_size, cols=w.cols,
+                                             want_amax=True)
+        ref, ref_amax = brute_force_plane_prefill(*args, w.page_size, w.cols)
+        assert bad == 0
+        written = ~np.isnan(ref)
+        assert np.array_equal(np.isnan(plane), np.isnan(ref)), w.name
+        assert np.array_equal(plane[written], ref[written]), w.name
+        assert np.array_equal(amax[written], ref_amax[written]), w.name
+        toks = np.array([w.num_tokens - 1, 0, w.num_tokens // 2], dtype=np.int64)
+        sub, sub_a, bad2 = orc.score_prefill(*args, page_size=w.page_size, cols=w.cols,
+                                             tokens=toks, want_amax=True)
+        assert bad2 == 0
+        assert np.array_equal(sub, ref[toks], equal_nan=True), w.name
+        assert np.array_equal(sub_a[~np.isnan(sub)], ref_amax[toks][~np.isnan(sub)]), w.name
+
+
+def pin_prefill_closed_form(orc):
+    """q = 1.0 at dim 0, key p carries code min(p % 128, 126) at dim 0: each
+    block's maximum is the value of its last visible key, for every token of
+    a chunk of 300 tokens (the inclusive causal bound per token)."""
+    ps, s, qlen = 256, 700, 300
+    npg = -(-s // ps)
+    k = np.zeros((npg + 1, ps, 128), dtype=np.uint8)
+    k[:, :, 0] = np.minimum(np.arange(ps) % 128, 126).astype(np.uint8)[None, :]
+    bt = np.full((1, 4), npg, dtype=np.int32)
+    bt[0, :npg] = np.random.default_rng(4).permutation(npg)
+    q = np.zeros((qlen, 4, 128), dtype=np.uint8)
+    q[:, :, 0] = 0x38  # 1.0
+    cols = 8
+    plane, _, bad = orc.score_prefill(q, k, bt, np.array([0, qlen], np.int32),
+                                      np.array([s], np.int32), page_size=ps, cols=cols)
+    assert bad == 0
+    val = torch_decode(np.arange(256, dtype=np.uint8))
+    nblk = -(-s // 128)
+    for j in range(qlen):
+        pos = s - qlen + j
+        for c in range(cols):
+            if c >= nblk or pos < 128 * c:
+                want = -np.inf
+            else:
+                want = val[min(min(pos, 128 * c + 127) % 128, 126)]
+            assert np.all(plane[j, :, c] == np.float32(want)), (j, c, plane[j, :, c], want)
+
+
+def pin_prefill_uniform_chunks_are_decode(orc):
+    """With every chunk decode_query_len tokens long the prefill plane is the
+    decode plane (the decode plane is pinned by its own brute force)."""
+    for w in _tiny_workloads():
+        B = w.batch
+        qo = (np.arange(B + 1) * w.dql).astype(np.int32)
+        args = (w.index_q.numpy(), w.index_k.numpy(), w.block_table.numpy())
+        dec, _, b1 = orc.score_decode(*args, w.seq_lens.numpy(), page_size=w.page_size,
+                                      decode_query_len=w.dql, cols=w.cols)
+        pre, _, b2 = orc.score_prefill(*args, qo, w.seq_lens.numpy(), page_size=w.page_size,
+                                       cols=w.cols)
+        assert b1 == b2 == 0
+        assert np.array_equal(dec, pre, equal_nan=True), w.name
+
+
 ALL_PINS = [
     pin_e4m3_table, pin_dots_vs_float64, pin_code_pairs, pin_plane_brute_force,
     pin_plane_closed_form, pin_written_range, pin_column_counts_golden, pin_select_brute_force,
     pin_select_invariants, pin_merge_split_equivalence, pin_merge_missing_forced,
     pin_sharded_plane_brute_force, pin_sharded_rows_partition, pin_mapped_select,
-    pin_sharded_chain_exact,
+    pin_sharded_chain_exact, pin_prefill_brute_force, pin_prefill_closed_form,
+    pin_prefill_uniform_chunks_are_decode,
 ]

@@ -45,6 +45,12 @@ MUTATIONS = [
      "int64_t pages = (seq_len + ORACLE_BLOCK - 1) / ORACLE_BLOCK;"),
     ("mapped_offset_dropped", "int64_t id = (int64_t)index_scale * c + index_offset;",
      "int64_t id = (int64_t)index_scale * c;"),
+    # prefill chunks
+    ("prefill_position_from_chunk_start", "int64_t pos = seq_len - q_len + j;",
+     "int64_t pos = seq_len - q_len + j - 1;"),
+    ("prefill_request_lookup", "while (qo_indptr[b + 1] <= t)", "while (qo_indptr[b + 1] < t)"),
+    ("prefill_head_row", "index_q + (t * ORACLE_HEADS + h) * ORACLE_DIM",
+     "index_q + (t * ORACLE_HEADS) * ORACLE_DIM"),
     ("mapped_forced_on_columns",
      "entry e = {srow[c], (int32_t)id};\n                    if (is_forced(id, n,",
      "entry e = {srow[c], (int32_t)id};\n                    if (is_forced(c, n,"),

@@ -84,6 +84,17 @@ DRIVER = textwrap.dedent("""
                     scale, offset = (1, 0) if page_size == 128 else (2, rank * 2 // ws)
                     o.top16_select_mapped(sp, nvp, init_blocks=1, local_blocks=2, num_ranges=2,
                                           index_scale=scale, index_offset=offset)
+            # prefill chunks: empty, single-token, whole-request and ragged chunks
+            qlens = np.minimum(np.array([0, 1, 1, 127, 5, 129, 300, 999], dtype=np.int64), seqs)
+            qo = np.zeros(B + 1, dtype=np.int32)
+            qo[1:] = np.cumsum(qlens)
+            qp = codes((int(qo[-1]), 4, 128))
+            for table in (bt, bad):
+                for c in (cols, 4):
+                    o.score_prefill(qp, k, table, qo, seqs, page_size=page_size, cols=c,
+                                    want_amax=True)
+            o.score_prefill(qp, k, bt, qo, seqs, page_size=page_size, cols=cols,
+                            tokens=np.array([int(qo[-1]) - 1, 0, 3], dtype=np.int64))
     print("sanitized oracle ok")
 """)
 

@@ -34,6 +34,13 @@ Recipe (the same for every configuration; ``seed = 1000 + config number``):
    request this is ``ceil(seq_len / 128)``).
 7. ``cols`` = the smallest multiple of four that covers the longest
    request's B128 blocks (the score plane's width).
+
+Prefill workloads (``q_lens`` given) score a chunk of query tokens per
+request instead of decode_query_len tokens: request b's chunk holds
+``q_len_b`` tokens (drawn right after the sequence lengths, clipped to
+seq_len_b), rows ``[qo_indptr[b], qo_indptr[b+1])`` of index_q, token j at
+position ``seq_len_b - q_len_b + j``; ``num_valid_pages`` follows step 6 for
+every token. The rest of the recipe is unchanged.
 """
 from __future__ import annotations
 
@@ -83,6 +90,7 @@ class Workload:
     num_ranges: int
     poison_page: int
     meta: dict = field(default_factory=dict)
+    qo_indptr: torch.Tensor | None = None  # int32 [B + 1] for prefill chunks, else None
 
     @property
     def batch(self) -> int:
@@ -90,7 +98,25 @@ class Workload:
 
     @property
     def num_tokens(self) -> int:
+        if self.qo_indptr is not None:
+            return int(self.qo_indptr[-1])
         return self.batch * self.dql
+
+    @property
+    def q_lens(self) -> torch.Tensor:
+        """Query tokens per request (decode_query_len each for decode)."""
+        if self.qo_indptr is not None:
+            return (self.qo_indptr[1:] - self.qo_indptr[:-1]).to(torch.int32)
+        return torch.full((self.batch,), self.dql, dtype=torch.int32)
+
+    @property
+    def positions(self) -> torch.Tensor:
+        """int64 [T]: the position of every query token."""
+        ql = self.q_lens.to(torch.int64)
+        sl = self.seq_lens.to(torch.int64)
+        first = torch.repeat_interleave(sl - ql, ql)
+        start = torch.repeat_interleave(torch.cumsum(ql, 0) - ql, ql)
+        return first + torch.arange(int(ql.sum())) - start
 
     @property
     def total_keys(self) -> int:
@@ -131,14 +157,20 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
              outlier_frac: float = 0.0, init: int = 1, local: int = 2, ranges: int = 1,
              pool=("exact", None), seed: int = 0, name: str = "custom", cols: int | None = None,
              table_width: int | None = None, chunk_pages: int = 1024,
-             values: str = "normal") -> Workload:
-    """Draws one workload following the module recipe."""
+             values: str = "normal", q_lens=None) -> Workload:
+    """Draws one workload following the module recipe (a prefill workload
+    when q_lens, a sequence-length law for the chunks, is given)."""
     if values not in ("normal", "codes"):
         raise ValueError(f"unknown value law {values!r}")
     g = torch.Generator().manual_seed(int(seed))
     seq_lens = _draw_seq_lens(g, batch, seq)
     if int(seq_lens.min()) < 0:
         raise ValueError("negative sequence length")
+    qo_indptr = None
+    if q_lens is not None:
+        ql = torch.minimum(_draw_seq_lens(g, batch, q_lens), seq_lens)
+        qo_indptr = torch.zeros(batch + 1, dtype=torch.int32)
+        qo_indptr[1:] = torch.cumsum(ql, 0).to(torch.int32)
     pages_per_req = [(int(s) + page_size - 1) // page_size for s in seq_lens]
     need = sum(pages_per_req)
     pool_size = need if pool[0] == "exact" or pool[1] is None else int(pool[1])
@@ -178,7 +210,7 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
                 outlier[p, (blk * BLOCK % page_size) // BLOCK] = True
                 n_outlier_blocks += 1
 
-    T = batch * dql
+    T = batch * dql if qo_indptr is None else int(qo_indptr[-1])
     if values == "codes":
         index_q = _finite_codes(g, (T, HEADS, DIM))
     else:
@@ -201,8 +233,13 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
         if npg and s % page_size:
             index_k[int(block_table[b, npg - 1]), s % page_size:] = POISON_CODE
 
-    j = torch.arange(dql, dtype=torch.int64)
-    pos = (seq_lens[:, None] - dql + j[None, :]).reshape(-1)
+    if qo_indptr is None:
+        j = torch.arange(dql, dtype=torch.int64)
+        pos = (seq_lens[:, None] - dql + j[None, :]).reshape(-1)
+    else:
+        ql = (qo_indptr[1:] - qo_indptr[:-1]).to(torch.int64)
+        start = torch.repeat_interleave(qo_indptr[:-1].to(torch.int64), ql)
+        pos = torch.repeat_interleave(seq_lens - ql, ql) + torch.arange(T) - start
     nvp = torch.where(pos >= 0, pos // BLOCK + 1, torch.zeros_like(pos)).to(torch.int32)
 
     return Workload(name=name, index_q=index_q, index_k=index_k, block_table=block_table,
@@ -210,7 +247,8 @@ def generate(*, batch: int, seq, page_size: int, dql: int, scale: float = 1.0,
                     dql=dql, cols=int(cols), init_blocks=init, local_blocks=local,
                     num_ranges=ranges, poison_page=poison,
                     meta=dict(seed=seed, pool=pool_size, outlier_blocks=n_outlier_blocks,
-                              scale=scale, values=values))
+                              scale=scale, values=values),
+                    qo_indptr=qo_indptr)
 
 
 def config(n: int, **overrides) -> Workload:
