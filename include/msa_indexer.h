@@ -67,6 +67,10 @@ extern "C" {
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
 #define MSA_SCORE_SELECT_COUNTER_STRIDE 32 /* int32 per msa_score_select counter (128 B)  */
 #define MSA_STREAM_PROBE_SINK_WORDS 1024   /* uint32 words of msa_stream_read_probe's sink */
+#define MSA_PREFILL_WINDOW_TOKENS 64       /* query tokens per prefill window              */
+#define MSA_PREFILL_PLAN_HEADER_WORDS 8    /* int32 words before a prefill plan's items    */
+#define MSA_PREFILL_ITEM_WORDS 8           /* int32 words per prefill plan item            */
+#define MSA_PREFILL_MAX_BATCH 8192         /* requests one prefill plan takes              */
 
 /*
  * One Top16 row (128 bytes). score[i] is the score-plane value of block
@@ -298,6 +302,94 @@ int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols
                            const int32_t* num_valid_pages, int32_t init_blocks,
                            int32_t local_blocks, int32_t num_ranges, msa_top16_row* partial,
                            msa_top16_row* out, int32_t* errors, hipStream_t stream);
+
+/*
+ * The prefill chain: window plan -> local scoring and Top16 select -> merge.
+ * Source: "prepare_msa_icp_indexer", prefill bullet (prefill_window_plan once
+ * per query window and step; prefill_local per query chunk into the score
+ * scratch and the carrier rows; the exchange; prefill_merge of the received
+ * rows). The pages give the chain's shape, not its rule (the select page
+ * defers its parameters to msa_icp_topk_select_prefill(), which is not among
+ * them). This library reads it as the decode chain with a chunk of query
+ * tokens per request:
+ *   - request b's chunk is rows [qo_indptr[b], qo_indptr[b+1]) of index_q
+ *     ([num_tokens, 4, 128] e4m3fn), token j at position
+ *     seq_len_b - q_len_b + j (q_len_b = qo_indptr[b+1] - qo_indptr[b]), as a
+ *     decode token sits at seq_len - decode_query_len + j;
+ *   - the score scratch is a plane [num_tokens, 4, cols] with msa_score_decode's
+ *     element and written columns (block max over keys at or before the
+ *     token's position, -inf for a block with none, columns
+ *     c < min(roundup4(ceil(seq_len_b / 128)), cols), the rest untouched);
+ *   - the carrier rows are msa_top16_select's rows of that plane over R column
+ *     ranges, and the merge is msa_top16_merge (on one GPU the carrier is the
+ *     received set: there is no exchange).
+ *
+ * A window is at most MSA_PREFILL_WINDOW_TOKENS consecutive tokens of one
+ * chunk. The plan lists the windows' work items (a window and a range of its
+ * visible columns); it is built once per step on the device and serves every
+ * layer of that step.
+ */
+
+/*
+ * int32 words of a prefill plan able to hold any step of at most num_tokens
+ * query tokens over batch requests on a plane of cols columns (host only):
+ * MSA_PREFILL_PLAN_HEADER_WORDS + MSA_PREFILL_ITEM_WORDS * capacity. Returns
+ * MSA_ERR_INVALID_ARG for num_tokens < 1, batch outside
+ * [1, MSA_PREFILL_MAX_BATCH] or cols outside (0, 8192].
+ */
+int64_t msa_prefill_plan_words(int64_t num_tokens, int32_t batch, int32_t cols);
+
+/*
+ * Builds the plan of one prefill step (one workgroup, on `stream`).
+ * qo_indptr   device int32 [batch + 1]: chunk boundaries, qo_indptr[0] = 0,
+ *             non-decreasing, qo_indptr[batch] <= num_tokens.
+ * seq_lens    device int32 [batch]: keys of each request, its chunk's own keys
+ *             included. A request with seq_len <= 0 or an empty chunk writes
+ *             nothing.
+ * batch       1 <= batch <= MSA_PREFILL_MAX_BATCH.
+ * num_tokens  rows of index_q and of the score scratch (>= 1).
+ * cols        plane width, 0 < cols <= 8192, cols % 4 == 0.
+ * plan        device int32 [plan_words], caller-owned; plan_words from
+ *             msa_prefill_plan_words (at least header + one item).
+ * Device-side problems are counted in `errors`: a malformed chunk (skipped),
+ * a request whose columns the plane cuts short (clamped), items past the
+ * plan's capacity (dropped).
+ */
+int msa_prefill_window_plan(const int32_t* qo_indptr, const int32_t* seq_lens, int32_t batch,
+                            int32_t num_tokens, int32_t cols, int32_t* plan, int64_t plan_words,
+                            int32_t* errors, hipStream_t stream);
+
+/*
+ * Scores one prefill step and selects its Top16 rows.
+ * index_q, index_k, num_pages, block_table, block_table_stride, page_size
+ *             as for msa_score_decode, index_q holding num_tokens query rows.
+ * batch       rows of block_table (>= 1); a plan item of a request at or past
+ *             it is counted in `errors` and skipped.
+ * plan        the step's plan, made for the same num_tokens and cols (a plan
+ *             made for others is counted in `errors` and nothing is written).
+ * score_scratch  device float32 [num_tokens, 4, cols], 16-byte aligned: the
+ *             plane (written columns as above; other columns untouched).
+ * num_valid_pages, init_blocks, local_blocks, num_ranges
+ *             as for msa_top16_select on that plane (num_valid_pages [num_tokens]).
+ * carrier     device [num_tokens, 4, R] rows: msa_top16_select's rows of the plane.
+ * Block-table entries outside [0, num_pages) or past the row stride are counted
+ * in `errors` and their blocks score -inf.
+ */
+int msa_prefill_local(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                      const int32_t* block_table, int64_t block_table_stride, int32_t batch,
+                      int32_t page_size,
+                      const int32_t* plan, int64_t plan_words, float* score_scratch,
+                      int32_t num_tokens, int32_t cols, const int32_t* num_valid_pages,
+                      int32_t init_blocks, int32_t local_blocks, int32_t num_ranges,
+                      msa_top16_row* carrier, int32_t* errors, hipStream_t stream);
+
+/*
+ * Merges each (token, head)'s R carrier rows into one row: msa_top16_merge
+ * over num_tokens tokens. received [num_tokens, 4, R], output [num_tokens, 4].
+ */
+int msa_prefill_merge(const msa_top16_row* received, int32_t num_tokens, int32_t num_ranges,
+                      const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                      msa_top16_row* output, int32_t* errors, hipStream_t stream);
 
 /*
  * Score-plane width for requests of up to max_seq_len tokens:

@@ -39,7 +39,12 @@ STREAM_PROBE_SINK_WORDS = 1024  # MSA_STREAM_PROBE_SINK_WORDS
 EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
            "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe",
-           "msa_contraction_probe")
+           "msa_contraction_probe", "msa_prefill_plan_words", "msa_prefill_window_plan",
+           "msa_prefill_local", "msa_prefill_merge")
+
+PREFILL_WINDOW_TOKENS = 64  # MSA_PREFILL_WINDOW_TOKENS
+PREFILL_PLAN_HEADER_WORDS = 8
+PREFILL_ITEM_WORDS = 8
 
 # MFMA forms of msa_contraction_probe (MSA_PROBE_* in msa_indexer.h)
 PROBE_BF16 = 0
@@ -94,6 +99,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_warmup.restype = ctypes.c_int
     lib.msa_stream_read_probe.argtypes = [P, i64, P, P]
     lib.msa_stream_read_probe.restype = ctypes.c_int
+    lib.msa_prefill_plan_words.argtypes = [i64, i32, i32]
+    lib.msa_prefill_plan_words.restype = i64
+    lib.msa_prefill_window_plan.argtypes = [P, P, i32, i32, i32, P, i64, P, P]
+    lib.msa_prefill_window_plan.restype = ctypes.c_int
+    lib.msa_prefill_local.argtypes = [P, P, i64, P, i64, i32, i32, P, i64, P, i32, i32, P, i32,
+                                      i32, i32, P, P, P]
+    lib.msa_prefill_local.restype = ctypes.c_int
+    lib.msa_prefill_merge.argtypes = [P, i32, i32, P, i32, i32, P, P, P]
+    lib.msa_prefill_merge.restype = ctypes.c_int
     lib.msa_contraction_probe.argtypes = [P, P, i64, i32, P, P]
     lib.msa_contraction_probe.restype = ctypes.c_int
     lib.msa_last_error.argtypes = []
@@ -391,3 +405,93 @@ def msa_top16_select_merge(scores: torch.Tensor, num_valid_pages: torch.Tensor, 
         scores.data_ptr(), T, cols, num_valid_pages.data_ptr(), init_blocks, local_blocks,
         num_ranges, partial.data_ptr() if partial is not None else None, out.data_ptr(),
         _errors_ptr(errors), _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------------------
+# prefill chain ("prepare_msa_icp_indexer", prefill bullet)
+# ---------------------------------------------------------------------------
+
+def msa_prefill_plan_words(num_tokens: int, batch: int, cols: int) -> int:
+    """int32 words of a plan that holds any prefill step of at most
+    num_tokens query tokens over batch requests on a plane of cols columns."""
+    n = load().msa_prefill_plan_words(int(num_tokens), int(batch), int(cols))
+    _check(min(int(n), 0))
+    return int(n)
+
+
+def new_prefill_plan(num_tokens: int, batch: int, cols: int, device="cuda") -> torch.Tensor:
+    """An int32 plan buffer sized by msa_prefill_plan_words."""
+    return torch.empty(msa_prefill_plan_words(num_tokens, batch, cols), dtype=torch.int32,
+                       device=device)
+
+
+def msa_prefill_window_plan(qo_indptr: torch.Tensor, seq_lens: torch.Tensor,
+                            plan: torch.Tensor, *, num_tokens: int, cols: int,
+                            errors: torch.Tensor | None = None, stream=None) -> None:
+    """Builds the plan of one prefill step: request b's chunk is rows
+    [qo_indptr[b], qo_indptr[b+1]) of index_q ([num_tokens, 4, 128])."""
+    _dev(qo_indptr, seq_lens, plan)
+    B = seq_lens.numel()
+    _need(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens: int32 [B]")
+    _need(qo_indptr.dtype == torch.int32 and qo_indptr.shape == (B + 1,) and
+          qo_indptr.is_contiguous(), f"qo_indptr: contiguous int32 [{B + 1}]")
+    _need(plan.dtype == torch.int32 and plan.dim() == 1 and plan.is_contiguous(),
+          "plan: contiguous int32 [words]")
+    _check(load().msa_prefill_window_plan(qo_indptr.data_ptr(), seq_lens.data_ptr(), B,
+                                          int(num_tokens), int(cols), plan.data_ptr(),
+                                          plan.numel(), _errors_ptr(errors),
+                                          _stream_handle(stream)))
+
+
+def msa_prefill_local(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
+                      plan: torch.Tensor, score_scratch: torch.Tensor,
+                      num_valid_pages: torch.Tensor, carrier: torch.Tensor, *, page_size: int,
+                      init_blocks: int, local_blocks: int, num_ranges: int = 1,
+                      errors: torch.Tensor | None = None, stream=None) -> None:
+    """Scores one prefill step into score_scratch [Tq, 4, cols] and writes
+    its Top16 carrier rows [Tq, 4, R, 32]."""
+    q = _u8(index_q, "index_q")
+    k = _u8(index_k, "index_k")
+    _dev(q, k, block_table, plan, score_scratch, num_valid_pages, carrier)
+    _need(q.dim() == 3 and q.shape[1:] == (NUM_HEADS, HEAD_DIM) and q.is_contiguous(),
+          "index_q: contiguous [Tq, 4, 128]")
+    Tq = q.shape[0]
+    _need(k.dim() == 3 and k.shape[1] == page_size and k.shape[2] == HEAD_DIM and
+          k.is_contiguous(), f"index_k: contiguous [pages, {page_size}, 128]")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
+          block_table.is_contiguous(), "block_table: contiguous int32 [B, width]")
+    _need(plan.dtype == torch.int32 and plan.dim() == 1 and plan.is_contiguous(),
+          "plan: contiguous int32 [words]")
+    _need(score_scratch.dtype == torch.float32 and score_scratch.dim() == 3 and
+          score_scratch.shape[:2] == (Tq, NUM_HEADS) and score_scratch.is_contiguous(),
+          f"score_scratch: contiguous float32 [{Tq}, 4, cols]")
+    cols = score_scratch.shape[2]
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (Tq,),
+          f"num_valid_pages: int32 [{Tq}]")
+    _need(carrier.dtype == torch.int32 and carrier.shape == (Tq, NUM_HEADS, num_ranges, ROW_WORDS)
+          and carrier.is_contiguous(), f"carrier: contiguous int32 [{Tq}, 4, {num_ranges}, 32]")
+    _check(load().msa_prefill_local(q.data_ptr(), k.data_ptr(), k.shape[0],
+                                    block_table.data_ptr(), block_table.shape[1],
+                                    block_table.shape[0], page_size,
+                                    plan.data_ptr(), plan.numel(), score_scratch.data_ptr(), Tq,
+                                    cols, num_valid_pages.data_ptr(), init_blocks, local_blocks,
+                                    num_ranges, carrier.data_ptr(), _errors_ptr(errors),
+                                    _stream_handle(stream)))
+
+
+def msa_prefill_merge(received: torch.Tensor, num_valid_pages: torch.Tensor,
+                      output: torch.Tensor, *, init_blocks: int, local_blocks: int,
+                      errors: torch.Tensor | None = None, stream=None) -> None:
+    """Merges the carrier rows [Tq, 4, R, 32] into output rows [Tq, 4, 32]."""
+    _dev(received, num_valid_pages, output)
+    _need(received.dtype == torch.int32 and received.dim() == 4 and
+          received.shape[1] == NUM_HEADS and received.shape[3] == ROW_WORDS and
+          received.is_contiguous(), "received: contiguous int32 [Tq, 4, R, 32]")
+    Tq, _, R, _ = received.shape
+    _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (Tq,),
+          "num_valid_pages: int32 [Tq]")
+    _need(output.dtype == torch.int32 and output.shape == (Tq, NUM_HEADS, ROW_WORDS) and
+          output.is_contiguous(), f"output: contiguous int32 [{Tq}, 4, 32]")
+    _check(load().msa_prefill_merge(received.data_ptr(), Tq, R, num_valid_pages.data_ptr(),
+                                    init_blocks, local_blocks, output.data_ptr(),
+                                    _errors_ptr(errors), _stream_handle(stream)))

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libmsa_indexer.so")
-SOURCES = ["msa_abi.hip", "score_decode.hip", "top16.hip", "stream_probe.hip",
+SOURCES = ["msa_abi.hip", "score_decode.hip", "top16.hip", "prefill.hip", "stream_probe.hip",
            "contraction_probe.hip"]
 
 HIPCC_FLAGS = [

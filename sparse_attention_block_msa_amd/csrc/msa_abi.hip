@@ -370,6 +370,145 @@ int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStr
                          fn);
 }
 
+int64_t msa_prefill_plan_words(int64_t num_tokens, int32_t batch, int32_t cols)
+{
+    static const char* fn = "msa_prefill_plan_words";
+    g_last_error[0] = '\0';
+    MSA_CHECK(num_tokens >= 1 && num_tokens <= 0x7FFFFFFF,
+              "%s: num_tokens (%lld) must be in [1, 2^31)", fn, (long long)num_tokens);
+    MSA_CHECK(batch >= 1 && batch <= MSA_PREFILL_MAX_BATCH, "%s: batch (%d) must be in [1, %d]",
+              fn, batch, MSA_PREFILL_MAX_BATCH);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS, "%s: cols (%d) must be in (0, %d]", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    // windows <= num_tokens / 64 + batch; items per window <= ceil(cols / item columns)
+    const int64_t windows = num_tokens / MSA_PREFILL_WINDOW_TOKENS + batch;
+    const int64_t per_window = (cols + msa::kPrefillItemCols - 1) / msa::kPrefillItemCols;
+    return MSA_PREFILL_PLAN_HEADER_WORDS + MSA_PREFILL_ITEM_WORDS * windows * per_window;
+}
+
+int msa_prefill_window_plan(const int32_t* qo_indptr, const int32_t* seq_lens, int32_t batch,
+                            int32_t num_tokens, int32_t cols, int32_t* plan, int64_t plan_words,
+                            int32_t* errors, hipStream_t stream)
+{
+    static const char* fn = "msa_prefill_window_plan";
+    g_last_error[0] = '\0';
+    MSA_CHECK(qo_indptr && seq_lens && plan, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(qo_indptr, 4) && aligned(seq_lens, 4) && aligned(plan, 4) &&
+                  aligned(errors, 4),
+              "%s: int32 arrays must be 4-byte aligned", fn);
+    MSA_CHECK(batch >= 1 && batch <= MSA_PREFILL_MAX_BATCH, "%s: batch (%d) must be in [1, %d]",
+              fn, batch, MSA_PREFILL_MAX_BATCH);
+    MSA_CHECK(num_tokens >= 1, "%s: num_tokens (%d) must be >= 1", fn, num_tokens);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(plan_words >= MSA_PREFILL_PLAN_HEADER_WORDS + MSA_PREFILL_ITEM_WORDS,
+              "%s: plan_words (%lld) must hold the header and one item", fn,
+              (long long)plan_words);
+    msa::PrefillPlanParams p;
+    p.qo_indptr = qo_indptr;
+    p.seq_lens = seq_lens;
+    p.plan = plan;
+    p.capacity = (plan_words - MSA_PREFILL_PLAN_HEADER_WORDS) / MSA_PREFILL_ITEM_WORDS;
+    if (p.capacity > 0x7FFFFFF8)
+        p.capacity = 0x7FFFFFF8;
+    p.errors = errors;
+    p.batch = batch;
+    p.num_tokens = num_tokens;
+    p.cols = cols;
+    return launch_result(msa::launch_prefill_plan(p, stream), fn);
+}
+
+int msa_prefill_local(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                      const int32_t* block_table, int64_t block_table_stride, int32_t batch,
+                      int32_t page_size,
+                      const int32_t* plan, int64_t plan_words, float* score_scratch,
+                      int32_t num_tokens, int32_t cols, const int32_t* num_valid_pages,
+                      int32_t init_blocks, int32_t local_blocks, int32_t num_ranges,
+                      msa_top16_row* carrier, int32_t* errors, hipStream_t stream)
+{
+    static const char* fn = "msa_prefill_local";
+    g_last_error[0] = '\0';
+    MSA_CHECK(index_q && index_k && block_table && plan && score_scratch && num_valid_pages &&
+                  carrier,
+              "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(index_q, 16) && aligned(index_k, 16) && aligned(score_scratch, 16),
+              "%s: index_q, index_k and score_scratch must be 16-byte aligned", fn);
+    MSA_CHECK(aligned(block_table, 4) && aligned(plan, 4) && aligned(num_valid_pages, 4) &&
+                  aligned(carrier, 4) && aligned(errors, 4),
+              "%s: int32 arrays must be 4-byte aligned", fn);
+    MSA_CHECK(page_size == 128 || page_size == 256, "%s: page_size (%d) must be 128 or 256", fn,
+              page_size);
+    MSA_CHECK(num_pages >= 1, "%s: num_pages (%lld) must be >= 1", fn, (long long)num_pages);
+    MSA_CHECK(block_table_stride >= 1, "%s: block_table_stride (%lld) must be >= 1", fn,
+              (long long)block_table_stride);
+    MSA_CHECK(batch >= 1, "%s: batch (%d) must be >= 1", fn, batch);
+    MSA_CHECK(num_tokens >= 1 && (int64_t)num_tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
+              "%s: num_tokens (%d) must be >= 1 and tokens*4*ranges < 2^31", fn, num_tokens);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    MSA_CHECK(plan_words >= MSA_PREFILL_PLAN_HEADER_WORDS + MSA_PREFILL_ITEM_WORDS,
+              "%s: plan_words (%lld) must hold the header and one item", fn,
+              (long long)plan_words);
+    int rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+    int64_t capacity = (plan_words - MSA_PREFILL_PLAN_HEADER_WORDS) / MSA_PREFILL_ITEM_WORDS;
+    if (capacity > 0x7FFFFFF8)
+        capacity = 0x7FFFFFF8;
+
+    msa::PrefillScoreParams sp;
+    sp.q = index_q;
+    sp.k = index_k;
+    sp.num_pages = num_pages;
+    sp.bt = block_table;
+    sp.bt_stride = block_table_stride;
+    sp.bt_rows = batch;
+    sp.plan = plan;
+    sp.capacity = capacity;
+    sp.out = score_scratch;
+    sp.errors = errors;
+    sp.page_size = page_size;
+    sp.cols = cols;
+    sp.num_tokens = num_tokens;
+    rc = launch_result(msa::launch_prefill_score(sp, capacity, stream), fn);
+    if (rc != MSA_OK)
+        return rc;
+
+    msa::SelectParams p;
+    p.scores = score_scratch;
+    p.nvp = num_valid_pages;
+    p.out = carrier;
+    p.errors = errors;
+    p.num_tokens = num_tokens;
+    p.cols = cols;
+    p.init_blocks = init_blocks;
+    p.local_blocks = local_blocks;
+    p.num_ranges = num_ranges;
+    p.width = (cols + num_ranges - 1) / num_ranges;
+    p.index_scale = 1;
+    p.index_offset = 0;
+    return launch_result(msa::launch_top16_select(p, stream), fn);
+}
+
+int msa_prefill_merge(const msa_top16_row* received, int32_t num_tokens, int32_t num_ranges,
+                      const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                      msa_top16_row* output, int32_t* errors, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    msa::MergeParams p;
+    const int rc = merge_impl("msa_prefill_merge", received, num_tokens, num_ranges,
+                              MSA_MAX_RANGES, num_valid_pages, init_blocks, local_blocks, output,
+                              errors, &p);
+    if (rc != MSA_OK)
+        return rc;
+    return launch_result(msa::launch_top16_merge(p, stream), "msa_prefill_merge");
+}
+
 int msa_contraction_probe(const uint8_t* q, const uint8_t* k, int64_t tiles, int32_t form,
                           float* out, hipStream_t stream)
 {
@@ -392,6 +531,8 @@ int msa_warmup(void)
     hipError_t e = msa::warmup_score_kernels();
     if (e == hipSuccess)
         e = msa::warmup_top16_kernels();
+    if (e == hipSuccess)
+        e = msa::warmup_prefill_kernels();
     return launch_result(e, "msa_warmup");
 }
 

@@ -95,7 +95,42 @@ struct ScoreSelectParams {
     int64_t spin_ticks;      // set by the launcher
 };
 
+// Prefill chain: columns per work item (an item's pages are held one per
+// lane), and the most requests one plan takes (its LDS prefix array).
+constexpr int kPrefillItemCols = 32;
+constexpr int kMaxPrefillBatch = 8192;
+
+struct PrefillPlanParams {
+    const int32_t* qo_indptr;  // [batch + 1]
+    const int32_t* seq_lens;   // [batch]
+    int32_t* plan;             // header + capacity items
+    int64_t capacity;          // items the plan holds
+    int32_t* errors;           // nullable
+    int32_t batch;
+    int32_t num_tokens;        // rows of index_q / of the plane
+    int32_t cols;              // plane width
+};
+
+struct PrefillScoreParams {
+    const uint8_t* q;        // [num_tokens, 4, 128] e4m3fn
+    const uint8_t* k;        // [num_pages, page_size, 128] e4m3fn
+    int64_t num_pages;
+    const int32_t* bt;       // [bt_rows, bt_stride]
+    int64_t bt_stride;
+    int32_t bt_rows;
+    const int32_t* plan;     // from the plan kernel
+    int64_t capacity;        // items the plan holds
+    float* out;              // [num_tokens, 4, cols]
+    int32_t* errors;         // nullable
+    int32_t page_size;
+    int32_t cols;
+    int32_t num_tokens;
+};
+
 hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream);
+hipError_t launch_prefill_plan(const PrefillPlanParams& p, hipStream_t stream);
+hipError_t launch_prefill_score(const PrefillScoreParams& p, int64_t capacity,
+                                hipStream_t stream);
 hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream);
 hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream);
 hipError_t launch_top16_select(const SelectParams& p, hipStream_t stream);
@@ -105,5 +140,6 @@ hipError_t launch_top16_merge_dedup(const MergeParams& p, hipStream_t stream);
 // Loads the kernels of each file into the current device's context.
 hipError_t warmup_score_kernels();
 hipError_t warmup_top16_kernels();
+hipError_t warmup_prefill_kernels();
 
 }  // namespace msa

@@ -326,3 +326,59 @@ def test_probe_sink_words_match_header():
 def test_contraction_probe_rejects(lib, args, needle):
     assert lib.msa_contraction_probe(*args, None) == msa.MSA_ERR_INVALID_ARG
     assert needle in lib.msa_last_error().decode()
+
+
+def _plan(lib, **kw):
+    a = dict(qo=FAKE, sl=FAKE, batch=2, T=100, cols=32, plan=FAKE, words=1000, errors=None)
+    a.update(kw)
+    return lib.msa_prefill_window_plan(a["qo"], a["sl"], a["batch"], a["T"], a["cols"], a["plan"],
+                                       a["words"], a["errors"], None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(qo=None), "null"), (dict(plan=None), "null"), (dict(plan=FAKE + 2), "aligned"),
+    (dict(batch=0), "batch"), (dict(batch=8193), "batch"), (dict(T=0), "num_tokens"),
+    (dict(cols=30), "cols"), (dict(cols=8196), "cols"), (dict(words=15), "plan_words"),
+])
+def test_prefill_plan_rejects(lib, kw, needle):
+    assert _plan(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def _local(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, pages=10, bt=FAKE, stride=4, batch=2, ps=128, plan=FAKE, words=100,
+             out=FAKE, T=50, cols=32, nvp=FAKE, init=1, local=2, R=1, carrier=FAKE, errors=None)
+    a.update(kw)
+    return lib.msa_prefill_local(a["q"], a["k"], a["pages"], a["bt"], a["stride"], a["batch"],
+                                 a["ps"], a["plan"], a["words"], a["out"], a["T"], a["cols"],
+                                 a["nvp"], a["init"], a["local"], a["R"], a["carrier"],
+                                 a["errors"], None)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(q=None), "null"), (dict(carrier=None), "null"), (dict(out=FAKE + 4), "aligned"),
+    (dict(ps=64), "page_size"), (dict(pages=0), "num_pages"), (dict(stride=0), "stride"),
+    (dict(batch=0), "batch"), (dict(T=0), "num_tokens"), (dict(cols=6), "cols"),
+    (dict(R=0), "num_ranges"), (dict(R=33), "num_ranges"), (dict(words=8), "plan_words"),
+    (dict(init=10, local=7), "exceeds"),
+])
+def test_prefill_local_rejects(lib, kw, needle):
+    assert _local(lib, **kw) == msa.MSA_ERR_INVALID_ARG
+    assert needle in lib.msa_last_error().decode()
+
+
+def test_prefill_merge_rejects(lib):
+    assert lib.msa_prefill_merge(None, 4, 2, FAKE, 1, 2, FAKE, None, None) == \
+        msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_prefill_merge(FAKE, 4, 769, FAKE, 1, 2, FAKE, None, None) == \
+        msa.MSA_ERR_INVALID_ARG
+
+
+def test_prefill_plan_words():
+    # (ceil(T / 64) + batch) windows at most, ceil(cols / 32) items each
+    assert msa.msa_prefill_plan_words(8192, 1, 512) == 8 + 8 * (128 + 1) * 16
+    assert msa.msa_prefill_plan_words(1, 1, 4) == 8 + 8
+    with pytest.raises(msa.MsaError):
+        msa.msa_prefill_plan_words(0, 1, 4)
+    with pytest.raises(msa.MsaError):
+        msa.msa_prefill_plan_words(10, 1, 8200)
