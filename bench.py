@@ -343,16 +343,15 @@ def main():
     # Timed region 1c: the same K steps with the plane and the range rows from
     # one launch (msa_score_select), then msa_top16_merge; reported beside the
     # headline.
-    ws = msa.score_select_workspace(w.batch, R, device=dev)
+    ws = msa.score_select_workspace(w.batch, w.dql, w.cols, R, pool=True, device=dev)
 
     def step_score_select():
-        msa.msa_score_select(q, k, bt, sl, plane, nvp, part, ws, page_size=w.page_size,
+        # plane in the workspace's pool (scores unused), range rows and their
+        # merge from the same launch
+        msa.msa_score_select(q, k, bt, sl, None, nvp, part, ws, page_size=w.page_size,
                              decode_query_len=w.dql, init_blocks=w.init_blocks,
-                             local_blocks=w.local_blocks, num_ranges=R, errors=errors,
-                             stream=stream)
-        if R > 1:
-            msa.msa_top16_merge(part, nvp, final, init_blocks=w.init_blocks,
-                                local_blocks=w.local_blocks, errors=errors, stream=stream)
+                             local_blocks=w.local_blocks, num_ranges=R, cols=w.cols,
+                             merged=final if R <= 64 else None, errors=errors, stream=stream)
 
     score_select_ms = None
     if -(-w.cols // R) <= 2048:

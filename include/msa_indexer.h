@@ -65,7 +65,6 @@ extern "C" {
 #define MSA_MAX_SCORE_COLS 8192  /* score_out: 0 < cols <= 8192, cols % 4 == 0             */
 #define MSA_MAX_SELECT_COLS 12287 /* select scores: 0 < K < 12288                          */
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
-#define MSA_SCORE_SELECT_COUNTER_STRIDE 32 /* int32 per msa_score_select counter (128 B)  */
 #define MSA_STREAM_PROBE_SINK_WORDS 1024   /* uint32 words of msa_stream_read_probe's sink */
 #define MSA_PREFILL_WINDOW_TOKENS 64       /* query tokens per prefill window              */
 #define MSA_PREFILL_PLAN_HEADER_WORDS 8    /* int32 words before a prefill plan's items    */
@@ -153,40 +152,54 @@ int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shar
                              hipStream_t stream);
 
 /*
- * Steps 1 and 2 in one launch: the score plane, and Top16 select per (token,
- * head, column range) on it.
+ * int32 words of msa_score_select's workspace for these sizes (host only):
+ * counters, a ready queue and per-range counters, per-(token, head) merge
+ * tickets, and, with with_pool != 0 (score_out == NULL), the pool plane of
+ * batch * decode_query_len * 4 * cols floats. Returns MSA_ERR_INVALID_ARG for
+ * sizes msa_score_select would reject.
+ */
+int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len, int32_t cols,
+                                         int32_t num_ranges, int32_t with_pool);
+
+/*
+ * Steps 1 and 2 in one launch (and step 3 when `merged` is given): the score
+ * plane, Top16 select per (token, head, column range), and the merge of each
+ * (token, head)'s range rows.
  * Source: "prepare_msa_icp_indexer", decode: the chain score plane -> Top16
  * select -> merge, whose first two steps a fused scorer
- * (msa_icp_decode_score_publish) can replace, given caller-owned pool storage.
- * Here the fused launch keeps both steps' outputs, those of msa_score_decode
- * and msa_top16_select, and publishes nothing.
+ * (msa_icp_decode_score_publish) can replace with caller-owned pool storage,
+ * its scores then unused. Here the rows stay on this GPU (no publish).
  *
- * Arguments are those of msa_score_decode, then:
+ * Arguments are those of msa_score_decode, except that score_out may be NULL:
+ * the scores then go to the pool in the workspace and are not returned. Then:
  * num_valid_pages  device int32 [batch * decode_query_len], as for msa_top16_select.
+ *                  With score_out NULL, values above the request's written columns
+ *                  are counted in `errors` and clamped to them (the pool holds no other).
  * init_blocks, local_blocks  >= 0, sum <= 16.
- * num_ranges       R, 1 <= R <= min(cols, 768), with ceil(cols / R) <= 2048. Larger
- *                  spans use the two separate calls.
+ * num_ranges       R, 1 <= R <= min(cols, 768), with ceil(cols / R) <= 2048 (and
+ *                  R <= 64 with a merged output). Larger spans use the separate calls.
  * out              device [batch * decode_query_len, 4, R] rows.
- * workspace        device int32 [batch * R * MSA_SCORE_SELECT_COUNTER_STRIDE] (one
- *                  counter per 128-byte line), caller-owned. It must hold zeros when
- *                  the call is made, and the launch leaves it holding zeros. Launches
- *                  that share a workspace must not overlap. If `errors` counted a wait
- *                  timeout (below), re-zero the workspace before the next call.
+ * merged           device [batch * decode_query_len, 4] rows, or NULL.
+ * workspace        device int32 [workspace_words], 16-byte aligned, caller-owned,
+ *                  workspace_words >= msa_score_select_workspace_words(...). It must
+ *                  hold zeros (past the pool) when the call is made; the launch leaves
+ *                  them zero. Launches that share a workspace must not overlap.
  *
- * score_out receives exactly what msa_score_decode writes, and out exactly what
- * msa_top16_select(score_out, ..., num_ranges) then writes. The waves that score the
- * plane also run the select jobs. A job waits until every column of its range that
- * this launch writes has been stored. That wait is only for scoring work, and the
- * launch is sized so every wave is resident at once. A wait still open after
- * 2 seconds (possible only if other work holds the device's compute units) is
- * counted in `errors`, and the job then reads the plane as it stands.
+ * score_out (when given) receives exactly what msa_score_decode writes, out
+ * exactly what msa_top16_select(plane, ..., num_ranges) then writes, and merged
+ * exactly what msa_top16_merge of out writes. The waves that score the plane
+ * also run the select jobs: the wave that stores a range's last column queues
+ * the range, and a job is only taken once its range is queued. A wave waits
+ * for queued work only while every wave of the launch has started, so no
+ * wait depends on waves that other work keeps from running; every wait ends.
  */
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
                      const int32_t* block_table, int64_t block_table_stride,
                      const int32_t* seq_lens, int32_t batch, int32_t page_size,
                      int32_t decode_query_len, float* score_out, int32_t cols,
                      const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
-                     int32_t num_ranges, msa_top16_row* out, int32_t* workspace, int32_t* errors,
+                     int32_t num_ranges, msa_top16_row* out, msa_top16_row* merged,
+                     int32_t* workspace, int64_t workspace_words, int32_t* errors,
                      hipStream_t stream);
 
 /*

@@ -31,7 +31,6 @@ NUM_HEADS = 4
 HEAD_DIM = 128
 BLOCK_TOKENS = 128
 TOPK = 16
-COUNTER_STRIDE = 32  # int32 words per msa_score_select workspace counter (128 bytes)
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
 STREAM_PROBE_SINK_WORDS = 1024  # MSA_STREAM_PROBE_SINK_WORDS
@@ -40,7 +39,7 @@ EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
            "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe",
            "msa_contraction_probe", "msa_prefill_plan_words", "msa_prefill_window_plan",
-           "msa_prefill_local", "msa_prefill_merge")
+           "msa_prefill_local", "msa_prefill_merge", "msa_score_select_workspace_words")
 
 PREFILL_WINDOW_TOKENS = 64  # MSA_PREFILL_WINDOW_TOKENS
 PREFILL_PLAN_HEADER_WORDS = 8
@@ -78,7 +77,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_score_decode.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, P]
     lib.msa_score_decode.restype = ctypes.c_int
     lib.msa_score_select.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, i32, i32,
-                                     i32, P, P, P, P]
+                                     i32, P, P, P, i64, P, P]
+    lib.msa_score_select_workspace_words.argtypes = [i32, i32, i32, i32, i32]
+    lib.msa_score_select_workspace_words.restype = i64
     lib.msa_score_select.restype = ctypes.c_int
     lib.msa_score_decode_sharded.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32, i32, P,
                                              i32, P, P]
@@ -268,39 +269,74 @@ def msa_score_decode_sharded(index_q: torch.Tensor, index_k_shard: torch.Tensor,
                                            _errors_ptr(errors), _stream_handle(stream)))
 
 
-def score_select_workspace(batch: int, num_ranges: int, device="cuda") -> torch.Tensor:
-    """A zeroed int32 workspace [batch * num_ranges * 32] for msa_score_select
-    (one counter per 128-byte line). The launch leaves it zeroed, so one
-    workspace serves every later call of that size or smaller on the same
-    stream."""
-    return torch.zeros(batch * num_ranges * COUNTER_STRIDE, dtype=torch.int32, device=device)
+def msa_score_select_workspace_words(batch: int, decode_query_len: int, cols: int,
+                                     num_ranges: int, pool: bool = False) -> int:
+    """int32 words of msa_score_select's workspace (with the pool plane when
+    pool is set, i.e. for calls without a score plane)."""
+    n = load().msa_score_select_workspace_words(int(batch), int(decode_query_len), int(cols),
+                                                int(num_ranges), 1 if pool else 0)
+    _check(min(int(n), 0))
+    return int(n)
+
+
+def score_select_workspace(batch: int, decode_query_len: int, cols: int, num_ranges: int,
+                           pool: bool = False, device="cuda") -> torch.Tensor:
+    """A zeroed int32 workspace for msa_score_select. Each launch leaves it
+    zeroed, so one workspace serves every later call of these sizes or
+    smaller on the same stream."""
+    return torch.zeros(msa_score_select_workspace_words(batch, decode_query_len, cols,
+                                                        num_ranges, pool),
+                       dtype=torch.int32, device=device)
 
 
 def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
-                     seq_lens: torch.Tensor, score_out: torch.Tensor,
+                     seq_lens: torch.Tensor, score_out: torch.Tensor | None,
                      num_valid_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
                      *, page_size: int, decode_query_len: int, init_blocks: int,
-                     local_blocks: int, num_ranges: int = 1,
-                     errors: torch.Tensor | None = None, stream=None) -> None:
-    """Score plane and per-range Top16 rows in one launch: score_out as
-    msa_score_decode writes it, `out` [T, 4, R, 32] as msa_top16_select then
-    writes it. `workspace` is int32 [>= batch * R * 32], zero on entry (see
-    score_select_workspace)."""
-    args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
-                       decode_query_len)
+                     local_blocks: int, num_ranges: int = 1, cols: int | None = None,
+                     merged: torch.Tensor | None = None, errors: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """Score plane (or, with score_out None, the workspace's pool of `cols`
+    columns), per-range Top16 rows `out` [T, 4, R, 32] and optionally their
+    merge `merged` [T, 4, 32], in one launch. `workspace` is a zeroed int32
+    tensor (see score_select_workspace)."""
+    q = _u8(index_q, "index_q")
+    k = _u8(index_k, "index_k")
     B = seq_lens.numel()
     T = B * decode_query_len
-    _dev(score_out, num_valid_pages, out, workspace)
+    if score_out is not None:
+        args = _score_args(index_q, index_k, block_table, seq_lens, score_out, page_size,
+                           decode_query_len)
+    else:
+        _need(cols is not None, "cols: needed when score_out is None")
+        _dev(q, k, block_table, seq_lens)
+        _need(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1, "seq_lens: int32 [B]")
+        _need(q.shape == (T, NUM_HEADS, HEAD_DIM) and q.is_contiguous(),
+              f"index_q: expected contiguous [{T}, 4, 128], got {tuple(q.shape)}")
+        _need(k.dim() == 3 and k.shape[1] == page_size and k.shape[2] == HEAD_DIM and
+              k.is_contiguous(), f"index_k: expected contiguous [pages, {page_size}, 128]")
+        _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
+              block_table.shape[0] == B and block_table.is_contiguous(),
+              "block_table: contiguous int32 [B, width]")
+        args = (q.data_ptr(), k.data_ptr(), k.shape[0], block_table.data_ptr(),
+                block_table.shape[1], seq_lens.data_ptr(), B, page_size, decode_query_len,
+                None, int(cols))
+    _dev(q, num_valid_pages, out, workspace)
     _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
           "num_valid_pages: int32 [T]")
     _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
           out.is_contiguous(), f"out: contiguous int32 [{T}, 4, {num_ranges}, 32]")
-    _need(workspace.dtype == torch.int32 and workspace.is_contiguous() and
-          workspace.numel() >= B * num_ranges * COUNTER_STRIDE,
-          f"workspace: contiguous int32 with >= {B * num_ranges * COUNTER_STRIDE} elements")
+    if merged is not None:
+        _dev(out, merged)
+        _need(merged.dtype == torch.int32 and merged.shape == (T, NUM_HEADS, ROW_WORDS) and
+              merged.is_contiguous(), f"merged: contiguous int32 [{T}, 4, 32]")
+    _need(workspace.dtype == torch.int32 and workspace.dim() == 1 and workspace.is_contiguous(),
+          "workspace: contiguous int32 [words]")
     _check(load().msa_score_select(*args, num_valid_pages.data_ptr(), init_blocks, local_blocks,
-                                   num_ranges, out.data_ptr(), workspace.data_ptr(),
-                                   _errors_ptr(errors), _stream_handle(stream)))
+                                   num_ranges, out.data_ptr(),
+                                   merged.data_ptr() if merged is not None else None,
+                                   workspace.data_ptr(), workspace.numel(), _errors_ptr(errors),
+                                   _stream_handle(stream)))
 
 
 def msa_top16_select(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,

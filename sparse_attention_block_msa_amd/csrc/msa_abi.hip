@@ -222,28 +222,72 @@ int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shar
     return launch_result(msa::launch_score_decode(p, stream), fn);
 }
 
+int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len, int32_t cols,
+                                         int32_t num_ranges, int32_t with_pool)
+{
+    static const char* fn = "msa_score_select_workspace_words";
+    g_last_error[0] = '\0';
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    const int64_t rows = (int64_t)batch * decode_query_len * MSA_NUM_HEADS;
+    int64_t words = msa::kFusedHeaderWords + 2 * (int64_t)batch * num_ranges + rows;
+    if (with_pool)
+        words = (words + 3) / 4 * 4 + rows * cols;  // the pool starts 16-byte aligned
+    return words;
+}
+
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
                      const int32_t* block_table, int64_t block_table_stride,
                      const int32_t* seq_lens, int32_t batch, int32_t page_size,
                      int32_t decode_query_len, float* score_out, int32_t cols,
                      const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
-                     int32_t num_ranges, msa_top16_row* out, int32_t* workspace, int32_t* errors,
+                     int32_t num_ranges, msa_top16_row* out, msa_top16_row* merged,
+                     int32_t* workspace, int64_t workspace_words, int32_t* errors,
                      hipStream_t stream)
 {
     g_last_error[0] = '\0';
     const char* fn = "msa_score_select";
-    msa::ScoreSelectParams q;
-    int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
-                          seq_lens, batch, page_size, decode_query_len, score_out, cols, errors,
-                          &q.score);
-    if (rc != MSA_OK)
-        return rc;
-    MSA_CHECK(num_valid_pages && out && workspace, "%s: null pointer argument", fn);
-    MSA_CHECK(aligned(num_valid_pages, 4) && aligned(out, 4) && aligned(workspace, 4),
-              "%s: arrays must be 4-byte aligned", fn);
+    MSA_CHECK(workspace && aligned(workspace, 16), "%s: workspace must be non-null and 16-byte "
+              "aligned", fn);
+    const bool pool = score_out == nullptr;
     MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
               "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
               MSA_MAX_RANGES);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    const int64_t need =
+        msa_score_select_workspace_words(batch, decode_query_len, cols, num_ranges, pool ? 1 : 0);
+    g_last_error[0] = '\0';
+    MSA_CHECK(workspace_words >= need, "%s: workspace_words (%lld) must be >= %lld", fn,
+              (long long)workspace_words, (long long)need);
+    float* plane = score_out;
+    if (pool) {
+        const int64_t off = (msa::kFusedHeaderWords + 2 * (int64_t)batch * num_ranges +
+                             (int64_t)batch * decode_query_len * MSA_NUM_HEADS + 3) / 4 * 4;
+        plane = reinterpret_cast<float*>(workspace + off);
+    }
+    msa::ScoreSelectParams q;
+    int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
+                          seq_lens, batch, page_size, decode_query_len, plane, cols, errors,
+                          &q.score);
+    if (rc != MSA_OK)
+        return rc;
+    MSA_CHECK(num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(num_valid_pages, 4) && aligned(out, 4) && aligned(merged, 4),
+              "%s: arrays must be 4-byte aligned", fn);
     const int64_t tokens = (int64_t)batch * decode_query_len;
     MSA_CHECK(tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
               "%s: tokens*4*num_ranges must be < 2^31", fn);
@@ -251,17 +295,21 @@ int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num
     MSA_CHECK(width <= msa::kMaxFusedWidth,
               "%s: ceil(cols / num_ranges) = %d exceeds %d; use msa_score_decode + "
               "msa_top16_select", fn, width, msa::kMaxFusedWidth);
+    MSA_CHECK(merged == nullptr || num_ranges <= msa::kMaxFusedMergeRanges,
+              "%s: a merged output needs num_ranges <= %d (got %d); use msa_top16_merge", fn,
+              msa::kMaxFusedMergeRanges, num_ranges);
     rc = check_forced(fn, init_blocks, local_blocks);
     if (rc != MSA_OK)
         return rc;
     q.nvp = num_valid_pages;
     q.out = out;
-    q.counters = workspace;
+    q.merged = merged;
+    q.workspace = workspace;
     q.init_blocks = init_blocks;
     q.local_blocks = local_blocks;
     q.num_ranges = num_ranges;
     q.width = width;
-    q.spin_ticks = 0;
+    q.pool = pool ? 1 : 0;
     return launch_result(msa::launch_score_select(q, stream), fn);
 }
 

@@ -80,24 +80,31 @@ struct SelectMergeParams {
     int32_t width;           // ceil(cols / R)
 };
 
-// Scorer plus per-range select in one launch (same ranges as SelectParams).
-// One completion counter per (request, range), each on its own 128-byte line.
-constexpr int kCounterStride = MSA_SCORE_SELECT_COUNTER_STRIDE;
+// Scorer plus per-range select (and merge) in one launch (same ranges as
+// SelectParams). Workspace: kFusedHeaderWords words of counters, then
+// 2 * batch * R words (ready queue, range counters), then T * 4 merge
+// tickets, then (pool mode) a 16-byte aligned plane of T * 4 * cols floats.
+constexpr int kFusedHeaderWords = 128;
+constexpr int kMaxFusedMergeRanges = 64;
 struct ScoreSelectParams {
-    ScoreParams score;
+    ScoreParams score;       // score.out: the caller's plane, or the pool
     const int32_t* nvp;      // [batch*dql]
-    msa_top16_row* out;      // [batch*dql, 4, R]
-    int32_t* counters;       // [batch * R * kCounterStride]; zero on entry and on exit
+    msa_top16_row* out;      // [batch*dql, 4, R] range rows
+    msa_top16_row* merged;   // [batch*dql, 4] or null
+    int32_t* workspace;      // zero on entry and on exit
     int32_t init_blocks;
     int32_t local_blocks;
     int32_t num_ranges;
     int32_t width;           // ceil(cols / R) <= kMaxFusedWidth
-    int64_t spin_ticks;      // set by the launcher
+    int32_t pool;            // 1: score.out points into the workspace
 };
 
 // Prefill chain: columns per work item (an item's pages are held one per
 // lane), and the most requests one plan takes (its LDS prefix array).
-constexpr int kPrefillItemCols = 32;
+#ifndef MSA_PREFILL_ITEM_COLS
+#define MSA_PREFILL_ITEM_COLS 32
+#endif
+constexpr int kPrefillItemCols = MSA_PREFILL_ITEM_COLS;
 constexpr int kMaxPrefillBatch = 8192;
 
 struct PrefillPlanParams {

@@ -47,7 +47,7 @@ namespace {
 using namespace keytile;
 
 #ifndef MSA_PREFILL_WAVES_PER_EU
-#define MSA_PREFILL_WAVES_PER_EU 4  // register cap: workgroups of 4 waves, 4 waves per SIMD
+#define MSA_PREFILL_WAVES_PER_EU 2  // register cap: 128 query rows of operands per wave
 #endif
 
 constexpr int kWindow = MSA_PREFILL_WINDOW_TOKENS;
@@ -181,54 +181,106 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillPlanP
     }
 }
 
+// Launch shape of the chunk scorer: kWaves waves of kWaveTiles 16-row query
+// tiles each cover the window's 64 tokens x 4 heads. With 8 tiles (128 rows)
+// per wave every converted key operand feeds 8 MFMAs, and two waves per
+// SIMD hold the 128 query operand registers each.
+#ifndef MSA_PREFILL_WAVE_TILES
+#define MSA_PREFILL_WAVE_TILES 8
+#endif
+constexpr int kWaveTiles = MSA_PREFILL_WAVE_TILES;
+constexpr int kWaveRows = 16 * kWaveTiles;
+constexpr int kWaves = kWindow * kHeads / kWaveRows;
+constexpr int kWaveKeyRows = kBlockTokens / kWaves;  // key rows each wave stages per block
+static_assert(kWaves * kWaveRows == kWindow * kHeads && kWaveKeyRows % 8 == 0, "bad shape");
+
 // One column of one item for one wave: the block in `tile` against the
-// wave's 64 query rows. On return lane l holds the block max of wave row l
-// (row 16n + r of query tile n sits in lane 16n + r). kMask: key k of the
-// block is visible to the row of wave token u only if k <= lim0 + u.
+// wave's kWaveRows query rows. On return mx[n] holds, in every lane, the
+// block max of wave row 16n + lane % 16. kMask: key k of the block is
+// visible to wave row 16n + r only if k <= lim0 + (16n + r) / 4 (the row's
+// token offset from the wave's first token).
 template <bool kMask>
-__device__ __forceinline__ float prefill_block(const uint8_t* tile, const Bf16Slice (&qb)[4],
-                                               int r16, int g, int lim0)
+__device__ __forceinline__ void prefill_block(const uint8_t* tile,
+                                              const Bf16Slice (&qb)[kWaveTiles], int r16, int g,
+                                              int lim0, float (&mx)[kWaveTiles])
 {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    float mx[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < kWaveTiles; ++n)
         mx[n] = -INFINITY;
-#pragma unroll 2
     for (int kt = 0; kt < 8; ++kt) {
         const Bf16Slice kb = to_bf16(read_row_slice(tile, kt * 16 + r16, g));
+        // step-major over the query tiles: consecutive MFMAs never depend on
+        // each other, and a tile's result is read kWaveTiles MFMAs after its
+        // last step was issued
+        v4f a[kWaveTiles];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            v4f a = zero;
+        for (int n = 0; n < kWaveTiles; ++n)
+            a[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.op[0], qb[n].op[0], zero, 0, 0, 0);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.op[s], qb[n].op[s], a, 0, 0, 0);
+        for (int s = 1; s < 4; ++s) {
+#pragma unroll
+            for (int n = 0; n < kWaveTiles; ++n)
+                a[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.op[s], qb[n].op[s], a[n], 0, 0,
+                                                               0);
+        }
+#pragma unroll
+        for (int n = 0; n < kWaveTiles; ++n) {
+            v4f x = a[n];
             if (kMask) {
-                // lane: keys kt*16 + 4g .. +3 for query row 16n + r16 (token 4n + r16/4)
+                // lane: keys kt*16 + 4g .. +3 for query row 16n + r16
                 const int lim = lim0 + 4 * n + (r16 >> 2) - (kt * 16 + 4 * g);
-                a.x = 0 <= lim ? a.x : -INFINITY;
-                a.y = 1 <= lim ? a.y : -INFINITY;
-                a.z = 2 <= lim ? a.z : -INFINITY;
-                a.w = 3 <= lim ? a.w : -INFINITY;
+                x.x = 0 <= lim ? x.x : -INFINITY;
+                x.y = 1 <= lim ? x.y : -INFINITY;
+                x.z = 2 <= lim ? x.z : -INFINITY;
+                x.w = 3 <= lim ? x.w : -INFINITY;
             }
-            mx[n] = fmaxf(mx[n], max4(a));
+            mx[n] = fmaxf(fmaxf(fmaxf(fmaxf(mx[n], x.x), x.y), x.z), x.w);
         }
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kWaveTiles; ++n) {
         mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 16));
         mx[n] = fmaxf(mx[n], __shfl_xor(mx[n], 32));
     }
-    return g == 0 ? mx[0] : g == 1 ? mx[1] : g == 2 ? mx[2] : mx[3];
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSA_PREFILL_WAVES_PER_EU)))
+// s_waitcnt immediates (gfx9 encoding): at most n vector-memory operations
+// of the wave outstanding (expcnt and lgkmcnt at their maxima), and every LDS
+// access of the wave returned (vmcnt and expcnt at their maxima).
+constexpr int wait_vmcnt(int n)
+{
+    return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+constexpr int kStageLoads = kWaveKeyRows / 8;  // DMA instructions per wave per block
+
+// This wave's kWaveKeyRows rows of a block, from `src_rows` into LDS at
+// `dst_rows` with the swizzle of stage_piece. Issued as inline assembly, so
+// the compiler, which cannot tell the two tiles apart, adds no DMA waits of
+// its own before LDS reads; the caller waits with explicit vmcnt counts.
+// Default cache policy: the windows of a request re-read the same blocks.
+__device__ __forceinline__ void stage_rows_async(const uint8_t* src_rows, uint8_t* dst_rows,
+                                                 int lane)
+{
+#pragma unroll
+    for (int t = 0; t < kStageLoads; ++t) {
+        const int row = 8 * t + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr)(dst_rows + t * 1024);
+        const uint8_t* src = src_rows + row * kDim + chunk * 16;
+        asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+    }
+}
+
+__global__ __launch_bounds__(kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(MSA_PREFILL_WAVES_PER_EU)))
 void prefill_score_kernel(PrefillScoreParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kBlockTokens * kDim];
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kBlockTokens * kDim];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;
     const int g = lane >> 4;
 
@@ -257,14 +309,15 @@ void prefill_score_kernel(PrefillScoreParams p)
     }
 
     const int col_shift = p.page_size == 256 ? 1 : 0;
-    const int64_t row_base = (int64_t)token0 * kHeads + wave * 64;  // first plane row of the wave
-    const int wave_tokens = ntok - 16 * wave;                          // may be <= 0
+    constexpr int kWaveTokens = kWaveRows / kHeads;
+    const int64_t row_base = (int64_t)token0 * kHeads + wave * kWaveRows;  // wave's first row
+    const int wave_tokens = ntok - kWaveTokens * wave;                      // may be <= 0
 
     // the wave's query rows as bf16 B operands (rows of tokens past the
     // window's end are zero and never stored)
-    Bf16Slice qb[4];
+    Bf16Slice qb[kWaveTiles];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kWaveTiles; ++n) {
         v8i raw = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         if (4 * n + (r16 >> 2) < wave_tokens)
             raw = load_row_slice(p.q + (row_base + 16 * n + r16) * kDim, g);
@@ -293,43 +346,67 @@ void prefill_score_kernel(PrefillScoreParams p)
     if (bad_mask != 0 && tid == 0 && p.errors)
         atomicAdd(p.errors, (int)__popcll(bad_mask));
 
-    const bool row_valid = wave_tokens > 0 && (lane >> 2) < wave_tokens;
-    float* out_row = p.out + (row_base + lane) * p.cols;
-    const int wave_pos0 = pos0 + 16 * wave;  // position of the wave's first token
+    // Lane l stores wave rows 16n + l % 16 for the tiles n with n % 4 == l / 16.
+    float* out_rows = p.out + (row_base + lane) * p.cols;
+    const int wave_pos0 = pos0 + kWaveTokens * wave;  // position of the wave's first token
+
+    // Two tiles: column i + 1's DMA is in flight while column i is
+    // contracted. A column with a bad entry stages page 0 (never read), so
+    // every column issues the same DMA instructions.
+    auto rows_of = [&](int c) -> const uint8_t* {
+        const int pi = (c >> col_shift) - pg0;
+        const int page = ((bad_mask >> pi) & 1ull) ? 0 : __builtin_amdgcn_readlane(entry, pi);
+        return p.k + ((int64_t)page * p.page_size + (c & ((1 << col_shift) - 1)) * kBlockTokens +
+                      wave * kWaveKeyRows) * kDim;
+    };
+    if (ncols > 0)
+        stage_rows_async(rows_of(col0), tiles[0] + wave * kWaveKeyRows * kDim, lane);
     for (int i = 0; i < ncols; ++i) {
         const int c = col0 + i;
+        const uint8_t* cur = tiles[i & 1];
+        if (i + 1 < ncols) {
+            stage_rows_async(rows_of(c + 1), tiles[(i + 1) & 1] + wave * kWaveKeyRows * kDim,
+                             lane);
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(kStageLoads));  // column i of this wave landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+        }
+        __builtin_amdgcn_s_barrier();  // and every other wave's
         const int pi = (c >> col_shift) - pg0;
-        float v = -INFINITY;
-        if (!((bad_mask >> pi) & 1ull)) {  // uniform over the workgroup
-            const int page = __builtin_amdgcn_readlane(entry, pi);
-            const uint8_t* blk =
-                p.k + ((int64_t)page * p.page_size + (c & ((1 << col_shift) - 1)) * kBlockTokens) *
-                          kDim;
-            stage_piece<32, 0>(blk + wave * 32 * kDim, tile + wave * 32 * kDim, lane);
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA has landed
-            __syncthreads();                // and every other wave's
-            if (wave_tokens > 0) {
+        if (wave_tokens > 0) {
+            float mx[kWaveTiles];
+            if ((bad_mask >> pi) & 1ull) {
+#pragma unroll
+                for (int n = 0; n < kWaveTiles; ++n)
+                    mx[n] = -INFINITY;
+            } else {
                 const int key0 = c * kBlockTokens;
                 if (key0 + (kBlockTokens - 1) > wave_pos0)
-                    v = prefill_block<true>(tile, qb, r16, g, wave_pos0 - key0);
+                    prefill_block<true>(cur, qb, r16, g, wave_pos0 - key0, mx);
                 else
-                    v = prefill_block<false>(tile, qb, r16, g, 0);
+                    prefill_block<false>(cur, qb, r16, g, 0, mx);
             }
-            __syncthreads();  // the tile's reads are done before the next DMA
+#pragma unroll
+            for (int n = 0; n < kWaveTiles; n += 4) {
+                const float v = g == 0 ? mx[n] : g == 1 ? mx[n + 1] : g == 2 ? mx[n + 2] : mx[n + 3];
+                // wave row 16n + lane: token offset (16n + lane) / 4
+                if (4 * n + (lane >> 2) < wave_tokens)
+                    out_rows[(int64_t)16 * n * p.cols + c] = v;
+            }
         }
-        if (row_valid)
-            out_row[c] = v;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // this wave's reads of `cur` returned
+        __builtin_amdgcn_s_barrier();               // every wave's: `cur` may be refilled
     }
 
     // columns no token of the window can see
     const int f0 = col0 + ncols;
     if (fill_end > f0) {
         const int nf = fill_end - f0;
-        const int64_t total = (int64_t)ntok * kHeads * nf;
+        const int total = ntok * kHeads * nf;  // <= 256 rows x 8192 columns
         float* base = p.out + (int64_t)token0 * kHeads * p.cols;
-        for (int64_t e = tid; e < total; e += 256) {
-            const int64_t row = e / nf;
-            base[row * p.cols + f0 + (e - row * nf)] = -INFINITY;
+        for (int e = tid; e < total; e += kWaves * 64) {
+            const int row = e / nf;
+            base[(int64_t)row * p.cols + f0 + (e - row * nf)] = -INFINITY;
         }
     }
 }
@@ -350,7 +427,7 @@ hipError_t launch_prefill_score(const PrefillScoreParams& p, int64_t capacity,
     const int64_t grid = (capacity + kXcds - 1) / kXcds * kXcds;
     void* args[] = {const_cast<PrefillScoreParams*>(&p)};
     return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_score_kernel),
-                           dim3((unsigned)grid), dim3(256), args, 0, stream);
+                           dim3((unsigned)grid), dim3(kWaves * 64), args, 0, stream);
 }
 
 hipError_t warmup_prefill_kernels()

@@ -578,53 +578,165 @@ void score_decode_kernel(ScoreParams p)
     score_wave_range<NT, kParts, false, kUnit, kSharded>(p, tile, res, [](int, int, int) {});
 }
 
-// Waits until the produced-column count in the low 16 bits of *ctr reaches
-// `expected`, for at most spin_ticks of the device's constant-rate clock.
-// Returns false on timeout. The plane values it waits for are read afterwards
-// with agent-scope atomic loads, so no cache invalidation is needed; the
-// workgroup-scope fence keeps those loads after the wait.
-__device__ __forceinline__ bool wait_for_columns(const int32_t* ctr, int expected,
-                                                 int64_t spin_ticks)
-{
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    bool ok = true;
-    while ((__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) <
-           expected) {
-        if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > spin_ticks) {
-            ok = false;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return ok;
-}
-
 // s_waitcnt immediate (gfx9 encoding) that waits for every outstanding
 // vector-memory operation of the wave, stores included: vmcnt(0), with
 // expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Score plane and per-range Top16 rows in one launch. Every wave first scores
-// its columns as score_decode_kernel does, but stores the plane with
-// agent-scope atomic stores (written through to the device's coherence
-// point). After each request segment it waits for those stores to complete
-// and adds the segment's column count, per column range, to the range's
-// counter (one per 128-byte line: counters sharing a line made the polling
-// below throttle the whole launch). It then runs select jobs j = blockIdx.x,
-// blockIdx.x + gridDim.x, ... over the (token, head, range) rows, in the row
-// order of the select kernel. A job waits until every column of its range
-// that this launch writes has been counted, reads the row with agent-scope
-// atomic loads and selects exactly as the select kernel does, then adds
-// 1 << 16 to the counter as a consumer mark. The last of the range's 4*dql
-// consumers resets the counter to zero, so the counters are zero again when
-// the launch ends. The protocol is the agent-scope release/acquire pair
-// without its whole-cache write-back and invalidation, which only non-atomic
-// accesses need (with them, the launch took three times as long). The wait is
-// only for scoring work, which waits on nothing, and the host keeps the grid
-// within the waves the device holds at once, so every wait ends; the clock
-// limit counts an error instead of spinning on if that fails, and a wave that
-// has timed out once counts its later unfinished waits without waiting.
+// Polls of any wait in score_select_kernel before it gives up and counts an
+// error. Every wait there ends by the launch's protocol (below); this bound
+// only keeps a defect from hanging the device.
+constexpr uint32_t kMaxPolls = 1u << 20;
+
+// Workspace of score_select_kernel (int32 words): four counters on their own
+// 128-byte lines, then the ready queue (a range id + 1 per completed range, in
+// completion order), the per-range column counters, the per-(token, head)
+// merge tickets, and, when the caller passes no plane, the pool plane.
+struct FusedWs {
+    int32_t* started;   // waves that have begun
+    int32_t* finished;  // waves that are done; the last one clears the workspace
+    int32_t* ready;     // completed ranges (the queue's length)
+    int32_t* claimed;   // select jobs taken
+    int32_t* queue;     // [batch * R]
+    int32_t* ctr;       // [batch * R] columns stored per range
+    int32_t* ticket;    // [T * 4] range rows written per (token, head)
+};
+
+__device__ __forceinline__ FusedWs fused_ws(const ScoreSelectParams& q)
+{
+    FusedWs f;
+    f.started = q.workspace;
+    f.finished = q.workspace + 32;
+    f.ready = q.workspace + 64;
+    f.claimed = q.workspace + 96;
+    f.queue = q.workspace + kFusedHeaderWords;
+    f.ctr = f.queue + (int64_t)q.score.batch * q.num_ranges;
+    f.ticket = f.ctr + (int64_t)q.score.batch * q.num_ranges;
+    return f;
+}
+
+// Wave-uniform agent-scope atomics, issued by lane 0.
+__device__ __forceinline__ int lane0_load(const int32_t* a)
+{
+    int v = 0;
+    if (__lane_id() == 0)
+        v = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int lane0_add(int32_t* a, int n)
+{
+    int v = 0;
+    if (__lane_id() == 0)
+        v = __hip_atomic_fetch_add(a, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ bool lane0_cas(int32_t* a, int expected, int desired)
+{
+    int ok = 0;
+    if (__lane_id() == 0)
+        ok = __hip_atomic_compare_exchange_strong(a, &expected, desired, __ATOMIC_RELAXED,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 ? 1
+                 : 0;
+    return __builtin_amdgcn_readfirstlane(ok) != 0;
+}
+
+__device__ __forceinline__ void lane0_store(int32_t* a, int v)
+{
+    if (__lane_id() == 0)
+        __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Columns of range r that request b writes (its row's expected count).
+__device__ __forceinline__ int range_columns(const ScoreSelectParams& q, int b, int r)
+{
+    bool clamped;
+    const int wb = written_cols(q.score.seq_lens[b], q.score.cols, clamped);
+    const int lo = r * q.width;
+    return max(0, min(min(lo + q.width, q.score.cols), wb) - lo);
+}
+
+// Appends range rr to the ready queue (its select jobs become claimable).
+__device__ __forceinline__ void publish_range(const FusedWs& f, int64_t rr)
+{
+    const int slot = lane0_add(f.ready, 1);
+    lane0_store(f.queue + slot, (int)rr + 1);
+}
+
+// Merge of row th's R range rows (written through by other waves, read with
+// agent-scope loads) into merged[th], exactly as msa_top16_merge does with
+// n = max(0, num_valid_pages) (a forced id missing from the rows, possible
+// only for num_valid_pages past the plane, is counted); VM values per lane
+// cover R * 16 <= 64 * VM entries.
+template <int VM>
+__device__ __forceinline__ void fused_merge(const ScoreSelectParams& q, int64_t th, int n,
+                                            int lane, topk::Candidate* buf)
+{
+    using namespace topk;
+    const int total = q.num_ranges * kTop;
+    const int32_t* rows = reinterpret_cast<const int32_t*>(q.out + th * q.num_ranges);
+    float mv[VM];
+    int iv[VM];
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const int e = min(i * 64 + lane, total - 1);
+        const int32_t* row = rows + (e / kTop) * 2 * kTop;
+        mv[i] = __int_as_float(
+            __hip_atomic_load(row + e % kTop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        iv[i] = __hip_atomic_load(row + kTop + e % kTop, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint32_t um[VM];
+    uint64_t fm = 0;
+    int n_forced = 0;
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const bool valid = i * 64 + lane < total && iv[i] >= 0;
+        const bool forced = valid && is_forced(iv[i], n, q.init_blocks, q.local_blocks);
+        um[i] = valid && !forced ? order_key(mv[i]) : 0u;
+        fm |= (uint64_t)forced << i;
+        n_forced += __popcll(__ballot(forced));
+    }
+    const int expected_forced = forced_count(n, q.init_blocks, q.local_blocks);
+    msa_top16_row* dst = q.merged + th;
+    const int kept = select_row<VM>(um, mv, fm, kTop - expected_forced, count_keys<VM>(um), lane,
+                                    buf, [&](int i) { return iv[i]; },
+                                    [&](float score, int id, int slot) {
+                                        dst->score[slot] = score;
+                                        dst->id[slot] = id;
+                                    });
+    pad_row(dst, kept, lane);
+    if ((n_forced < expected_forced || kept > kTop) && lane == 0 && q.score.errors)
+        atomicAdd(q.score.errors, 1);
+}
+
+// Score plane (or pool) and per-range Top16 rows, and optionally their merge,
+// in one launch ("flashinfer.msa_ops.prepare_msa_icp_indexer", decode: a fused
+// scorer can replace the score and select steps, with caller-owned pool
+// storage). Protocol, with no wait on a wave that may not have started:
+//  1. Every wave counts itself in `started`, then scores its columns as
+//     score_decode_kernel does, storing them written through to the device's
+//     coherence point (sc1). After each request segment it waits for those
+//     stores and adds the segment's columns to each range's counter; the wave
+//     whose add completes a range appends it to the ready queue. Ranges with
+//     no written column are appended by workgroup 0 at the start.
+//  2. Select jobs ((range, row of the range) pairs, numbered in queue order)
+//     are claimed one at a time by compare-and-swap on `claimed`, only below
+//     the number of ready jobs. A wave that finds none ready keeps polling
+//     only while every wave of the grid has started (then every range still
+//     open belongs to running waves, which finish their scoring without
+//     waiting); otherwise it leaves, and the waves that complete the
+//     remaining ranges claim their jobs themselves. A job selects its row of
+//     the range exactly as top16_select_kernel does (agent-scope loads of the
+//     plane) and writes the range row written through.
+//  3. With a merged output, the job then adds 1 to its (token, head) ticket;
+//     the job that brings it to R merges the R rows as msa_top16_merge does
+//     and clears the ticket.
+//  4. Every wave counts itself in `finished` last; the wave that completes
+//     the count clears the counters, the queue and the range counters, so the
+//     workspace holds zeros again for the next launch.
 template <int NT, int kParts, int kWavesPerEU, int V, int kUnit>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_select_kernel(ScoreSelectParams q)
@@ -632,55 +744,142 @@ void score_select_kernel(ScoreSelectParams q)
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];
     __shared__ topk::Candidate cand[64];
+    __shared__ msa_top16_row row_buf;
     const ScoreParams& p = q.score;
     const int lane = threadIdx.x;
     const int R = q.num_ranges;
     const int w = q.width;
+    const FusedWs f = fused_ws(q);
+    const int rows_per_range = p.dql * kHeads;
+    const int64_t n_ranges = (int64_t)p.batch * R;
+    const int64_t total_jobs = n_ranges * rows_per_range;
+    const int grid = (int)gridDim.x;
 
-    score_wave_range<NT, kParts, true, kUnit, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        if (lane == 0) {
-            for (int r = c_begin / w; r * w < c_end; ++r) {
-                const int n = min(c_end, (r + 1) * w) - max(c_begin, r * w);
-                atomicAdd(q.counters + ((int64_t)b * R + r) * kCounterStride, n);
+    lane0_add(f.started, 1);
+    if (blockIdx.x == 0) {  // ranges with no written column are ready at once
+        for (int64_t rr = lane; rr < n_ranges; rr += 64) {
+            if (range_columns(q, (int)(rr / R), (int)(rr % R)) == 0) {
+                const int slot =
+                    __hip_atomic_fetch_add(f.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(f.queue + slot, (int)rr + 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
+        }
+    }
+
+    // 1. scoring
+    score_wave_range<NT, kParts, true, kUnit, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the segment's stores are complete
+        for (int r = c_begin / w; r * w < c_end; ++r) {
+            const int n = min(c_end, (r + 1) * w) - max(c_begin, r * w);
+            const int64_t rr = (int64_t)b * R + r;
+            const int old = lane0_add(f.ctr + rr, n);
+            if (old + n == range_columns(q, b, r))
+                publish_range(f, rr);
         }
     });
 
-    const int rows = p.dql * kHeads;
-    const int64_t jobs = (int64_t)p.batch * rows * R;
-    bool patient = true;  // after one timed-out wait this wave waits no more
-    for (int64_t job = blockIdx.x; job < jobs; job += gridDim.x) {
-        const int r = (int)(job % R);
-        const int64_t th = job / R;  // t * 4 + h
-        const int t = (int)(th / kHeads);
-        const int b = t / p.dql;
-        int n = q.nvp[t];
-        if (n < 0 || n > p.cols) {
-            if (r == 0 && (th % kHeads) == 0 && lane == 0 && p.errors)
-                atomicAdd(p.errors, 1);
-            n = n < 0 ? 0 : p.cols;
+    // 2. and 3. select jobs, then merges
+    uint32_t polls = 0;
+    bool gave_up = false;
+    while (true) {
+        const int c = lane0_load(f.claimed);
+        if ((int64_t)c >= total_jobs)
+            break;
+        const int64_t ready_jobs = (int64_t)lane0_load(f.ready) * rows_per_range;
+        if ((int64_t)c < ready_jobs) {
+            if (!lane0_cas(f.claimed, c, c + 1))
+                continue;  // another wave took job c
+            polls = 0;
+            const int slot = c / rows_per_range;
+            const int row = c - slot * rows_per_range;
+            int rr1;
+            while ((rr1 = lane0_load(f.queue + slot)) == 0) {  // its publisher is writing it
+                if (++polls > kMaxPolls) {
+                    gave_up = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (gave_up)
+                break;
+            const int64_t rr = rr1 - 1;
+            const int b = (int)(rr / R);
+            const int r = (int)(rr - (int64_t)b * R);
+            const int t = b * p.dql + row / kHeads;
+            const int64_t th = (int64_t)t * kHeads + row % kHeads;
+            // valid ids [0, n): num_valid_pages, clamped to the plane (and,
+            // for the pool, to the columns this launch writes)
+            bool clamped;
+            const int limit = q.pool ? written_cols(p.seq_lens[b], p.cols, clamped) : p.cols;
+            int n = q.nvp[t];
+            if (n < 0 || n > limit) {
+                if (r == 0 && (row % kHeads) == 0 && lane == 0 && p.errors)
+                    atomicAdd(p.errors, 1);
+                n = n < 0 ? 0 : limit;
+            }
+            const int lo = r * w;
+            const int hi = min(lo + w, p.cols);
+            float sv[V];
+            topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
+            topk::select_loaded<V>(sv, lo, hi, topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
+                                   &row_buf, lane, cand);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // the range row, written through (a merging wave reads it)
+            int32_t* dst = reinterpret_cast<int32_t*>(q.out + th * R + r);
+            if (lane < 2 * kTop)
+                __hip_atomic_store(dst + lane, reinterpret_cast<const int32_t*>(&row_buf)[lane],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (q.merged != nullptr) {
+                if (R == 1) {
+                    if (lane < 2 * kTop)
+                        reinterpret_cast<int32_t*>(q.merged + th)[lane] =
+                            reinterpret_cast<const int32_t*>(&row_buf)[lane];
+                } else {
+                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row is stored
+                    if (lane0_add(f.ticket + th, 1) == R - 1) {
+                        const int nm = max(0, q.nvp[t]);  // as msa_top16_merge reads it
+                        if (R <= 4)
+                            fused_merge<1>(q, th, nm, lane, cand);
+                        else if (R <= 8)
+                            fused_merge<2>(q, th, nm, lane, cand);
+                        else if (R <= 16)
+                            fused_merge<4>(q, th, nm, lane, cand);
+                        else
+                            fused_merge<16>(q, th, nm, lane, cand);
+                        lane0_store(f.ticket + th, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            continue;
         }
-        const int lo = r * w;
-        const int hi = min(lo + w, p.cols);
-        bool clamped;
-        const int wb = written_cols(p.seq_lens[b], p.cols, clamped);
-        const int expected = max(0, min(hi, wb) - lo);
-        int32_t* ctr = q.counters + ((int64_t)b * R + r) * kCounterStride;
-        if (expected > 0 && !(patient && wait_for_columns(ctr, expected, q.spin_ticks))) {
-            patient = false;
-            if (lane == 0 && p.errors)
-                atomicAdd(p.errors, 1);
+        // nothing ready: wait only while every wave of the grid is running or done
+        if (lane0_load(f.started) < grid)
+            break;
+        if (++polls > kMaxPolls) {
+            gave_up = true;
+            break;
         }
-        float sv[V];
-        topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
-        topk::select_loaded<V>(sv, lo, hi,
-                               topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
-                               q.out + job, lane, cand);
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (gave_up && lane == 0 && p.errors)
+        atomicAdd(p.errors, 1);
+
+    // 4. the last wave out clears the workspace
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (lane0_add(f.finished, 1) == grid - 1) {
+        for (int64_t i = lane; i < 2 * n_ranges; i += 64)
+            f.queue[i] = 0;  // queue and range counters
         if (lane == 0) {
-            const int old = atomicAdd(ctr, 1 << 16);
-            if ((old >> 16) == rows - 1)
-                atomicExch(ctr, 0);
+            *f.started = 0;
+            *f.ready = 0;
+            *f.claimed = 0;
+            *f.finished = 0;
         }
     }
 }
@@ -759,25 +958,6 @@ int device_cus()
     return n;
 }
 
-// Ticks of the device's constant-rate clock (s_memrealtime) in 2 seconds.
-int64_t spin_ticks_2s()
-{
-    static std::atomic<int64_t> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 200000000;  // 100 MHz
-    int64_t ticks = cached[dev].load(std::memory_order_relaxed);
-    if (ticks == 0) {
-        int khz = 0;
-        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
-            khz <= 0)
-            khz = 100000;
-        ticks = (int64_t)khz * 2000;
-        cached[dev].store(ticks, std::memory_order_relaxed);
-    }
-    return ticks;
-}
-
 // Scorer grid: one wave per workgroup, a whole number of waves per SIMD, no
 // more waves than 4-column groups can exist.
 int64_t score_grid(const ScoreParams& p)
@@ -817,24 +997,6 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
     X(1, 4, false) X(1, 16, false) X(1, 32, false) X(2, 4, false) X(2, 16, false)     \
     X(2, 32, false) X(1, 4, true) X(1, 16, true) X(1, 32, true) X(2, 4, true)         \
     X(2, 16, true) X(2, 32, true)
-constexpr int kScoreSelectInstances = 12;
-
-// Workgroups (one wave each) of instance `which` that one CU holds at once,
-// queried once per device: the query costs far more host time than a launch.
-int resident_per_cu(const void* fn, int which)
-{
-    static std::atomic<int> cached[64][kScoreSelectInstances];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 0;
-    int per_cu = cached[dev][which].load(std::memory_order_relaxed);
-    if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0) != hipSuccess)
-            return 0;
-        cached[dev][which].store(per_cu, std::memory_order_relaxed);
-    }
-    return per_cu;
-}
 
 hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
 {
@@ -845,29 +1007,15 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
     const bool latency =
         max_cols <= (int64_t)device_cus() * 4 * MSA_SCORE_LATENCY_WAVES_PER_SIMD;
     const void* fn = nullptr;
-    int which = 0, index = 0;
 #define X(NT, V, L)                                  \
-    if (nt == NT && v == V && latency == L) {        \
-        fn = score_select_kernel_fn<NT, V, L>();     \
-        which = index;                               \
-    }                                                \
-    ++index;
+    if (nt == NT && v == V && latency == L)          \
+        fn = score_select_kernel_fn<NT, V, L>();
     MSA_FOR_EACH_SCORE_SELECT(X)
 #undef X
     if (fn == nullptr)
         return hipErrorInvalidValue;
-    // Every wave must be resident at once (select jobs wait on other waves'
-    // scoring), so the grid is capped at what the device holds.
-    const int per_cu = resident_per_cu(fn, which);
-    if (per_cu <= 0)
-        return hipErrorInvalidConfiguration;
-    int64_t grid = latency ? max_cols : score_grid(q.score);
-    const int64_t resident = (int64_t)per_cu * device_cus();
-    if (grid > resident)
-        grid = resident;
-    ScoreSelectParams qq = q;
-    qq.spin_ticks = spin_ticks_2s();
-    void* args[] = {&qq};
+    const int64_t grid = latency ? max_cols : score_grid(q.score);
+    void* args[] = {const_cast<ScoreSelectParams*>(&q)};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), args, 0, stream);
 }
 

@@ -435,6 +435,180 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
     pad_row(dst, kept_m, lane);
 }
 
+// Whole-row Top16 in one pass, for msa_top16_select_merge without per-range
+// rows: the merge of a row's split lists equals the select of the whole row,
+// so one selection over the row gives the same rows.
+//  * Wave w loads span [64Vw, 64V(w+1)) of the row and takes theta_w, the
+//    K-th largest of its 64 lane maxima (K = 16 - |forced ids of the row|).
+//    A span with at least K candidates has at least K keys >= theta_w, so
+//    theta = the largest such theta_w is at most the row's K-th largest key:
+//    every key of the best K, ties at the K-th included, is >= theta.
+//  * Each wave compacts its forced entries and its keys >= theta into its own
+//    LDS segment (at most 64), in element (= id) order. When the segments hold
+//    at most 128 entries together, wave 0 selects among them with one or two
+//    values per lane, the segments read in wave order (ascending ids).
+//    Otherwise (heavy ties, or spans too short to bound the row) every wave
+//    selects its span as msa_top16_select does and wave 0 merges the NW rows
+//    (exact by the same argument).
+template <int V, int NW>
+__global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergeParams p)
+{
+    constexpr int VM = NW * kTop / 64 > 0 ? NW * kTop / 64 : 1;  // merge values per lane
+    __shared__ Candidate seg[NW][64];
+    __shared__ int seg_count[NW];
+    __shared__ uint32_t theta_w[NW];
+    __shared__ msa_top16_row part[NW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t th = blockIdx.x;  // t * 4 + h
+    const int t = (int)(th / kHeads);
+    const int span_lo = wave * 64 * V;
+    float sv[V];
+    load_span<V>(p.scores + th * p.cols, p.cols, span_lo, lane, sv);
+
+    int n = p.nvp[t];
+    if (n < 0 || n > p.cols) {
+        if ((th % kHeads) == 0 && threadIdx.x == 0 && p.errors)
+            atomicAdd(p.errors, 1);
+        n = n < 0 ? 0 : p.cols;
+    }
+    const ColumnIds ci = column_ids(n, p.init_blocks, p.local_blocks, 1, 0);
+    const int K = kTop - forced_count(n, p.init_blocks, p.local_blocks);
+
+    // keys of the span, as select_loaded forms them
+    const int valid_hi = min(min(p.cols, ci.valid_end), span_lo + V * 64);
+    const int n_valid = max(0, valid_hi - span_lo);
+    const int n_init = max(0, min(valid_hi, ci.init_end) - span_lo);
+    const int n_local = max(0, valid_hi - max(span_lo, ci.local_begin));
+    const int n_both = max(0, min(valid_hi, ci.init_end) - max(span_lo, ci.local_begin));
+    const int n_cand = n_valid - (n_init + n_local - n_both);
+    uint32_t u[V];
+    uint64_t fbits = 0;
+    uint32_t lane_max = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int c = span_lo + i * 64 + lane;
+        const bool valid = c < valid_hi;
+        const bool forced = valid && (c < ci.init_end || c >= ci.local_begin);
+        u[i] = valid && !forced ? order_key(sv[i]) : 0u;
+        fbits |= (uint64_t)forced << i;
+        lane_max = max(lane_max, u[i]);
+    }
+    uint32_t tw = 0;  // 0: this span does not bound the row
+    if (K > 0 && n_cand >= K)
+        tw = max(kth_largest_of_lanes(lane_max, K, lane), 1u);
+    if (lane == 0)
+        theta_w[wave] = tw;
+    __syncthreads();
+    uint32_t theta = 1u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        theta = max(theta, theta_w[w]);
+
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const bool forced = (fbits >> i) & 1ull;
+        const bool sel = forced || (K > 0 && u[i] >= theta);
+        const uint64_t mask = __ballot(sel);
+        const int slot = base + lanes_below(mask);
+        if (sel && slot < 64) {
+            Candidate c;
+            c.key = forced ? 0u : u[i];  // candidates have keys >= theta >= 1
+            c.score = sv[i];
+            c.id = span_lo + i * 64 + lane;
+            seg[wave][slot] = c;
+        }
+        base += __popcll(mask);
+    }
+    if (lane == 0)
+        seg_count[wave] = base;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        total += min(seg_count[w], 129);  // a segment past 64 forces the fallback
+    bool fits = total <= 128;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        fits = fits && seg_count[w] <= 64;
+    msa_top16_row* dst = p.out + th;
+    if (fits) {
+        if (wave != 0)
+            return;
+        // element e of the concatenated segments (wave order: ascending ids)
+        auto gather = [&](int e) {
+            Candidate c = {0u, -INFINITY, -1};
+            int before = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cnt = seg_count[w];
+                if (e >= before && e < before + cnt)
+                    c = seg[w][e - before];
+                before += cnt;
+            }
+            return c;
+        };
+        if (total <= 64) {
+            const Candidate mine = gather(lane);
+            const bool have = lane < total;
+            const uint32_t u1[1] = {have ? mine.key : 0u};
+            const uint64_t f1 = (have && mine.key == 0u) ? 1ull : 0ull;
+            const int kept = wave_select<1>(u1, f1, K, count_keys<1>(u1), [&](int, int slot) {
+                dst->score[slot] = mine.score;
+                dst->id[slot] = mine.id;
+            });
+            pad_row(dst, kept, lane);
+        } else {
+            const Candidate mine[2] = {gather(lane), gather(64 + lane)};
+            uint32_t u2[2];
+            uint64_t f2 = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bool have = 64 * i + lane < total;
+                u2[i] = have ? mine[i].key : 0u;
+                f2 |= (uint64_t)(have && mine[i].key == 0u) << i;
+            }
+            const int kept = wave_select<2>(u2, f2, K, count_keys<2>(u2), [&](int i, int slot) {
+                dst->score[slot] = mine[i].score;
+                dst->id[slot] = mine[i].id;
+            });
+            pad_row(dst, kept, lane);
+        }
+        return;
+    }
+
+    // fallback: select every span, then merge the NW rows
+    select_loaded<V>(sv, span_lo, p.cols, ci, &part[wave], lane, seg[wave]);
+    __syncthreads();
+    if (wave != 0)
+        return;
+    float mv[VM];
+    int iv[VM];
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const int e = min(i * 64 + lane, NW * kTop - 1);
+        mv[i] = part[e / kTop].score[e % kTop];
+        iv[i] = part[e / kTop].id[e % kTop];
+    }
+    uint32_t um[VM];
+    uint64_t fm = 0;
+#pragma unroll
+    for (int i = 0; i < VM; ++i) {
+        const bool valid = i * 64 + lane < NW * kTop && iv[i] >= 0;
+        const bool forced = valid && is_forced(iv[i], n, p.init_blocks, p.local_blocks);
+        um[i] = valid && !forced ? order_key(mv[i]) : 0u;
+        fm |= (uint64_t)forced << i;
+    }
+    const int kept_m = select_row<VM>(um, mv, fm, K, count_keys<VM>(um), lane, seg[0],
+                                      [&](int i) { return iv[i]; },
+                                      [&](float score, int id, int slot) {
+                                          dst->score[slot] = score;
+                                          dst->id[slot] = id;
+                                      });
+    pad_row(dst, kept_m, lane);
+}
+
 // Launch shape: spans up to 1024 elements use one wave with V = the next
 // power of two >= span/64; longer spans use 4 waves with V = 4 .. 48 (on
 // 2048-element rows the 4-wave split measured 2 us faster per launch than
@@ -531,8 +705,35 @@ hipError_t launch_fused_shape(const SelectMergeParams& p, hipStream_t stream)
     X(1, 2) X(2, 2) X(4, 2) X(8, 2) X(16, 2) X(32, 2) \
     X(1, 4) X(2, 4) X(4, 4) X(8, 4) X(16, 4) X(32, 4)
 
+#define MSA_FOR_EACH_ROW_SHAPE(X) \
+    X(1, 1) X(2, 1) X(4, 1) X(8, 1) X(16, 1) X(16, 2) X(16, 4) X(16, 8) X(32, 8)
+
+template <int V, int NW>
+hipError_t launch_row_shape(const SelectMergeParams& p, hipStream_t stream)
+{
+    void* args[] = {const_cast<SelectMergeParams*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_row_select_kernel<V, NW>),
+                           dim3((unsigned)((int64_t)p.num_tokens * kHeads)), dim3(NW * 64), args,
+                           0, stream);
+}
+
 hipError_t launch_top16_select_merge(const SelectMergeParams& p, hipStream_t stream)
 {
+    if (p.partial == nullptr) {
+        // no per-range rows asked for: one selection over the whole row.
+        // Spans of 1024 columns per wave (up to 8 waves): on N(0,1) rows of
+        // 8192 columns and K = 8 the row bound then passes about 37 keys
+        // (fewer than 64 in 99.5% of rows); spans of 512 pass about 65.
+        const int nw = p.cols <= 1024 ? 1 : p.cols <= 2048 ? 2 : p.cols <= 4096 ? 4 : 8;
+        const int v = p.cols <= 64 ? 1 : p.cols <= 128 ? 2 : p.cols <= 256 ? 4
+                    : p.cols <= 512 ? 8 : p.cols <= 8192 ? 16 : 32;
+#define X(V, NW)                                   \
+        if (v == V && nw == NW)                    \
+            return launch_row_shape<V, NW>(p, stream);
+        MSA_FOR_EACH_ROW_SHAPE(X)
+#undef X
+        return hipErrorInvalidValue;
+    }
     // one wave per range: V = the next power of two >= ceil(width / 64), <= 32
     int v = 1;
     while (v * 64 < p.width)
@@ -581,6 +782,12 @@ hipError_t warmup_top16_kernels()
     if (e == hipSuccess)                                                                          \
         e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_merge_dedup_kernel<V>));
     MSA_FOR_EACH_DEDUP_SHAPE(X)
+#undef X
+#define X(V, NW)                                                                                 \
+    if (e == hipSuccess)                                                                         \
+        e = hipFuncGetAttributes(&attr,                                                          \
+                                 reinterpret_cast<const void*>(&top16_row_select_kernel<V, NW>));
+    MSA_FOR_EACH_ROW_SHAPE(X)
 #undef X
     return e;
 }

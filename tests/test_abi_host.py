@@ -191,12 +191,12 @@ def test_select_merge_rejects(lib, kw, needle):
 def _score_select(lib, **kw):
     a = dict(q=FAKE, k=FAKE, num_pages=10, bt=FAKE, bt_stride=4, seq=FAKE, batch=2,
              page_size=128, dql=1, out=FAKE, cols=32, nvp=FAKE, init=1, local=2, R=2,
-             rows=FAKE, ws=FAKE, errors=None, stream=None)
+             rows=FAKE, merged=None, ws=FAKE, words=1 << 20, errors=None, stream=None)
     a.update(kw)
     return lib.msa_score_select(a["q"], a["k"], a["num_pages"], a["bt"], a["bt_stride"],
                                 a["seq"], a["batch"], a["page_size"], a["dql"], a["out"],
                                 a["cols"], a["nvp"], a["init"], a["local"], a["R"], a["rows"],
-                                a["ws"], a["errors"], a["stream"])
+                                a["merged"], a["ws"], a["words"], a["errors"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,needle", [
@@ -216,6 +216,10 @@ def _score_select(lib, **kw):
     (dict(cols=8192, R=3), "exceeds 2048"),
     (dict(init=10, local=7), "exceeds"),
     (dict(init=-1), ">= 0"),
+    (dict(words=100), "workspace_words"),
+    (dict(out=None, words=300), "workspace_words"),  # the pool needs T * 4 * cols more
+    (dict(cols=8192, R=65, merged=FAKE), "merged"),
+    (dict(merged=FAKE + 2), "aligned"),
 ])
 def test_score_select_rejects(lib, kw, needle):
     """Host checks of msa_score_select: the scorer's own checks, then the
@@ -382,3 +386,12 @@ def test_prefill_plan_words():
         msa.msa_prefill_plan_words(0, 1, 4)
     with pytest.raises(msa.MsaError):
         msa.msa_prefill_plan_words(10, 1, 8200)
+
+
+def test_score_select_workspace_words():
+    # 128 counter words, a queue word and a counter per range, a ticket per row
+    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8) == 128 + 2 * 32 + 128
+    # the pool starts 16-byte aligned: 320 words, then 128 rows x 8192 floats
+    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8, pool=True) == 320 + 128 * 8192
+    with pytest.raises(msa.MsaError):
+        msa.msa_score_select_workspace_words(1, 9, 32, 1)

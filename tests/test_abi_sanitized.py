@@ -20,13 +20,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_attention_block_msa_amd", "csrc")
-from sparse_attention_block_msa_amd.build import SOURCES  # noqa: E402  (the library's own list)
+# the library's own sources and per-source flags
+from sparse_attention_block_msa_amd.build import SOURCES, compile_flags  # noqa: E402
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
-FLAGS = ["--offload-arch=gfx950", "-O2", "-g", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
 def _asan_runtime():
@@ -43,7 +41,8 @@ def test_abi_host_checks_clean_under_sanitizers(tmp_path):
 
     def compile_one(src):
         obj = tmp_path / (src + ".o")
-        subprocess.run([HIPCC, *FLAGS, *SAN, "-c", "-o", str(obj), os.path.join(CSRC, src)],
+        subprocess.run([HIPCC, *compile_flags(src), "-O2", "-g", *SAN, "-c", "-o", str(obj),
+                        os.path.join(CSRC, src)],
                        check=True, capture_output=True)
         return str(obj)
 

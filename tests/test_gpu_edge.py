@@ -445,7 +445,7 @@ def test_scorer_latency_mode_large_batch():
     plane = torch.full((T, 4, w.cols), int(CANARY_BITS), dtype=torch.int32,
                        device=DEV).view(torch.float32)
     rows = msa.new_rows(T, 4, 2, device=DEV)
-    ws = msa.score_select_workspace(w.batch, 2, device=DEV)
+    ws = msa.score_select_workspace(w.batch, 2, w.cols, 2, device=DEV)
     e2 = torch.zeros(1, dtype=torch.int32, device=DEV)
     msa.msa_score_select(w.index_q.to(DEV), w.index_k.to(DEV), w.block_table.to(DEV),
                          w.seq_lens.to(DEV), plane, w.num_valid_pages.to(DEV), rows, ws,

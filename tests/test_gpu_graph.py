@@ -81,17 +81,19 @@ def test_score_select_graph_replays_leave_workspace_zero():
     T, R = w.num_tokens, 4
     plane = torch.empty((T, 4, w.cols), dtype=torch.float32, device=DEV)
     rows = msa.new_rows(T, 4, R, device=DEV)
-    ws = msa.score_select_workspace(w.batch, R, device=DEV)
+    merged = msa.new_rows(T, 4, device=DEV)
+    ws = msa.score_select_workspace(w.batch, w.dql, w.cols, R, device=DEV)
 
     def launch(stream):
         msa.msa_score_select(q, k, bt, sl, plane, nvp, rows, ws, page_size=w.page_size,
                              decode_query_len=w.dql, init_blocks=w.init_blocks,
-                             local_blocks=w.local_blocks, num_ranges=R, stream=stream)
+                             local_blocks=w.local_blocks, num_ranges=R, merged=merged,
+                             stream=stream)
 
     plane.fill_(float("nan"))  # unwritten columns keep this fill
     launch(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    ref_plane, ref_rows = plane.clone(), rows.clone()
+    ref_plane, ref_rows, ref_merged = plane.clone(), rows.clone(), merged.clone()
     assert int(ws.count_nonzero()) == 0
 
     g = torch.cuda.CUDAGraph()
@@ -104,9 +106,11 @@ def test_score_select_graph_replays_leave_workspace_zero():
     for rep in range(4):
         plane.fill_(float("nan"))
         rows.fill_(-7)
+        merged.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(plane.view(torch.int32), ref_plane.view(torch.int32)), rep
         assert torch.equal(rows, ref_rows), rep
+        assert torch.equal(merged, ref_merged), rep
         assert int(ws.count_nonzero()) == 0, rep

@@ -134,16 +134,16 @@ def test_random_chain(seed):
             if fpart is not None:
                 assert torch.equal(fpart, part)
 
-        counters = msa.score_select_workspace(w.batch, R, device=DEV)
+        counters = msa.score_select_workspace(w.batch, w.dql, cols, R, device=DEV)
         plane2 = torch.full((T, 4, cols), int(CANARY_BITS), dtype=torch.int32,
                             device=DEV).view(torch.float32)
         part2 = msa.new_rows(T, 4, R, device=DEV)
         part2.fill_(ROW_FILL)
-        msa.msa_score_select(q, k, bt, sl, plane2, nvp, part2, counters, page_size=w.page_size,
-                             decode_query_len=w.dql, num_ranges=R, errors=err, **kw)
         final2 = msa.new_rows(T, 4, device=DEV)
         final2.fill_(ROW_FILL)
-        msa.msa_top16_merge(part2, nvp, final2, errors=err, **kw)
+        msa.msa_score_select(q, k, bt, sl, plane2, nvp, part2, counters, page_size=w.page_size,
+                             decode_query_len=w.dql, num_ranges=R, merged=final2, errors=err,
+                             **kw)
         torch.cuda.synchronize()
         assert int(err.item()) == 0
         assert torch.equal(plane2.view(torch.int32), plane.view(torch.int32))

@@ -1,12 +1,14 @@
 """GPU parity of msa_score_select (score plane and per-range Top16 rows in one
 launch), through the C ABI.
 
-Every case runs the fused launch twice on one reused workspace and checks,
-each time, that
+Every case runs the fused launch twice with a plane and twice without one
+(the scores then go to the workspace's pool), on one reused workspace, and
+checks each time that
 * the plane is bit-identical to msa_score_decode's, canary columns included;
-* the range rows are bit-identical to msa_top16_select's on that plane;
+* the range rows are bit-identical to msa_top16_select's on that plane, and
+  the merged rows to msa_top16_merge's of those;
 * the error count equals the two-call path's;
-* the workspace holds zeros again after the launch.
+* the workspace (the pool excepted) holds zeros again after the launch.
 The five workloads are also checked against the oracle: the rows equal the
 oracle's select on the GPU's plane bit for bit, and, after the merge, the
 oracle's chain on its own plane except near-ties within the tolerance band.
@@ -37,7 +39,6 @@ if not torch.cuda.is_available():
 DEV = torch.device("cuda:0")
 FINITE_CANARY = 0xC0A00000  # -5.0: a canary the select may read as a score
 ROW_FILL = 0x7BADBEEF
-_WS = {}
 
 
 def say(*a):
@@ -45,18 +46,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def workspace():
-    """One workspace shared by every test here: each launch must leave it zero."""
-    if "ws" not in _WS:
-        _WS["ws"] = msa.score_select_workspace(1 << 12, 1, device=DEV)  # 4096 counters
-    return _WS["ws"]
-
-
 def run_both(w, *, R=None, cols=None, nvp=None, block_table=None, canary=CANARY_BITS,
-             repeat=2):
-    """Two-call path, then the fused launch `repeat` times; asserts they agree
-    bit for bit. Returns (plane, rows, errors) of the fused launch (numpy,
-    torch int32 on the device, int)."""
+             repeat=2, pool=True):
+    """Two-call path (msa_score_decode, msa_top16_select, msa_top16_merge),
+    then the fused launch `repeat` times with a plane and, if `pool`, as many
+    times without one (scores in the workspace's pool), all on one workspace;
+    asserts they agree bit for bit and that the workspace (pool excepted) is
+    zero after every launch. Returns (plane, rows, errors) of the fused launch
+    with a plane (numpy, torch int32 on the device, int)."""
     T, B = w.num_tokens, w.batch
     R = R or w.num_ranges
     cols = cols or w.cols
@@ -65,39 +62,62 @@ def run_both(w, *, R=None, cols=None, nvp=None, block_table=None, canary=CANARY_
     nvp_t = (w.num_valid_pages if nvp is None else nvp).to(DEV)
     kw = dict(page_size=w.page_size, decode_query_len=w.dql)
     sel = dict(init_blocks=w.init_blocks, local_blocks=w.local_blocks, num_ranges=R)
+    with_merged = R <= 64
 
     plane2 = torch.full((T, 4, cols), int(np.int32(np.uint32(canary))), dtype=torch.int32,
                         device=DEV).view(torch.float32)
     rows2 = msa.new_rows(T, 4, R, device=DEV)
     rows2.fill_(ROW_FILL)
+    merged2 = msa.new_rows(T, 4, device=DEV)
     err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
     msa.msa_score_decode(q, k, bt, sl, plane2, errors=err2, **kw)
     msa.msa_top16_select(plane2, nvp_t, rows2, errors=err2, **sel)
+    if with_merged and R > 1:  # the fused launch counts what the merge counts
+        msa.msa_top16_merge(rows2, nvp_t, merged2, init_blocks=w.init_blocks,
+                            local_blocks=w.local_blocks, errors=err2)
+    else:
+        msa.msa_top16_merge(rows2, nvp_t, merged2, init_blocks=w.init_blocks,
+                            local_blocks=w.local_blocks)
     torch.cuda.synchronize()
+    ref_err = int(err2.item())
     ref_plane = plane2.view(torch.int32).cpu()
     ref_rows = rows2.cpu()
-    ref_err = int(err2.item())
+    ref_merged = merged2.cpu()
 
-    ws = workspace()
-    assert ws.numel() >= B * R * msa.COUNTER_STRIDE
-    for rep in range(repeat):
-        plane1 = torch.full((T, 4, cols), int(np.int32(np.uint32(canary))), dtype=torch.int32,
-                            device=DEV).view(torch.float32)
-        rows1 = msa.new_rows(T, 4, R, device=DEV)
-        rows1.fill_(ROW_FILL)
-        err1 = torch.zeros(1, dtype=torch.int32, device=DEV)
-        msa.msa_score_select(q, k, bt, sl, plane1, nvp_t, rows1, ws, errors=err1, **kw, **sel)
-        torch.cuda.synchronize()
-        got_plane = plane1.view(torch.int32).cpu()
-        n_plane = int((got_plane != ref_plane).sum())
-        assert n_plane == 0, f"launch {rep}: {n_plane} plane words differ from msa_score_decode"
-        got_rows = rows1.cpu()
-        bad = (got_rows != ref_rows).any(dim=-1).nonzero()
-        assert bad.numel() == 0, (f"launch {rep}: {bad.shape[0]} rows differ from "
-                                  f"msa_top16_select; first (t, h, r) {bad[:3].tolist()}")
-        assert int(err1.item()) == ref_err, (int(err1.item()), ref_err)
-        assert int(ws.count_nonzero()) == 0, f"launch {rep} left the workspace non-zero"
-    return got_plane.view(torch.float32).numpy(), rows1, ref_err
+    ws = msa.score_select_workspace(B, w.dql, cols, R, pool=pool, device=DEV)
+    head = msa.msa_score_select_workspace_words(B, w.dql, cols, R, pool=False)
+    for mode in (["plane", "pool"] if pool else ["plane"]):
+        for rep in range(repeat):
+            plane1 = None
+            if mode == "plane":
+                plane1 = torch.full((T, 4, cols), int(np.int32(np.uint32(canary))),
+                                    dtype=torch.int32, device=DEV).view(torch.float32)
+            rows1 = msa.new_rows(T, 4, R, device=DEV)
+            rows1.fill_(ROW_FILL)
+            merged1 = msa.new_rows(T, 4, device=DEV) if with_merged else None
+            if merged1 is not None:
+                merged1.fill_(ROW_FILL)
+            err1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+            msa.msa_score_select(q, k, bt, sl, plane1, nvp_t, rows1, ws, cols=cols,
+                                 merged=merged1, errors=err1, **kw, **sel)
+            torch.cuda.synchronize()
+            what = f"{mode} launch {rep}"
+            if plane1 is not None:
+                got_plane = plane1.view(torch.int32).cpu()
+                n_plane = int((got_plane != ref_plane).sum())
+                assert n_plane == 0, f"{what}: {n_plane} plane words differ from msa_score_decode"
+                rows_out = rows1
+            got_rows = rows1.cpu()
+            bad = (got_rows != ref_rows).any(dim=-1).nonzero()
+            assert bad.numel() == 0, (f"{what}: {bad.shape[0]} rows differ from "
+                                      f"msa_top16_select; first (t, h, r) {bad[:3].tolist()}")
+            if merged1 is not None:
+                badm = (merged1.cpu() != ref_merged).any(dim=-1).nonzero()
+                assert badm.numel() == 0, (f"{what}: {badm.shape[0]} merged rows differ from "
+                                           f"msa_top16_merge; first {badm[:3].tolist()}")
+            assert int(err1.item()) == ref_err, (what, int(err1.item()), ref_err)
+            assert int(ws[:head].count_nonzero()) == 0, f"{what} left the workspace non-zero"
+    return got_plane.view(torch.float32).numpy(), rows_out, ref_err
 
 
 # ---------------------------------------------------------------------------
@@ -199,8 +219,10 @@ def test_score_select_nvp_past_written_and_out_of_range():
     nvp[1] = -2
     nvp[3] = w.cols + 9
     say(f"[test] nvp past written columns cols={w.cols}")
-    _, _, err = run_both(w, R=2, nvp=nvp, canary=FINITE_CANARY)
-    assert err == 2
+    _, _, err = run_both(w, R=2, nvp=nvp, canary=FINITE_CANARY, pool=False)
+    # once per token from the select; the merge misses the forced ids past the
+    # plane of token 3 in its four heads
+    assert err == 2 + 4
 
 
 def test_score_select_bad_block_table_and_narrow_plane():
@@ -212,5 +234,6 @@ def test_score_select_bad_block_table_and_narrow_plane():
     say("[test] bad block-table entries, plane narrower than request 0")
     _, _, err = run_both(w, R=2, block_table=bt, cols=16, canary=FINITE_CANARY)
     # two bad entries; request 0 is wider than the plane (scorer), and its
-    # token's num_valid_pages (24) exceeds cols (select)
-    assert err == 4
+    # token's num_valid_pages (24) exceeds cols (select); the merge then misses
+    # that token's forced ids past the plane in its four heads
+    assert err == 4 + 4
