@@ -153,9 +153,9 @@ int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shar
 
 /*
  * int32 words of msa_score_select's workspace for these sizes (host only):
- * counters, a ready queue and per-range counters, per-(token, head) merge
- * tickets, and, with with_pool != 0 (score_out == NULL), the pool plane of
- * batch * decode_query_len * 4 * cols floats. Returns MSA_ERR_INVALID_ARG for
+ * one 128-byte counter line per (request, column range), per-(token, head)
+ * merge tickets, and, with with_pool != 0 (score_out == NULL), the pool plane
+ * of batch * decode_query_len * 4 * cols floats. Returns MSA_ERR_INVALID_ARG for
  * sizes msa_score_select would reject.
  */
 int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len, int32_t cols,
@@ -182,16 +182,18 @@ int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len
  * merged           device [batch * decode_query_len, 4] rows, or NULL.
  * workspace        device int32 [workspace_words], 16-byte aligned, caller-owned,
  *                  workspace_words >= msa_score_select_workspace_words(...). It must
- *                  hold zeros (past the pool) when the call is made; the launch leaves
- *                  them zero. Launches that share a workspace must not overlap.
+ *                  hold zeros (the pool excepted) when the call is made; the launch
+ *                  leaves them zero, unless it counted a timed-out wait in `errors`
+ *                  (then the caller zeroes it again). Launches that share a workspace
+ *                  must not overlap.
  *
  * score_out (when given) receives exactly what msa_score_decode writes, out
  * exactly what msa_top16_select(plane, ..., num_ranges) then writes, and merged
  * exactly what msa_top16_merge of out writes. The waves that score the plane
- * also run the select jobs: the wave that stores a range's last column queues
- * the range, and a job is only taken once its range is queued. A wave waits
- * for queued work only while every wave of the launch has started, so no
- * wait depends on waves that other work keeps from running; every wait ends.
+ * count each range's stored columns; a fixed subset of them (at most half of
+ * the waves the device holds at once) then runs the select jobs, each waiting
+ * until its range is complete. Scoring never waits, so every wave of the
+ * launch finds a slot and every wait ends.
  */
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
                      const int32_t* block_table, int64_t block_table_stride,

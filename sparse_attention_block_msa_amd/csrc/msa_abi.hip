@@ -238,10 +238,9 @@ int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len
               "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
               MSA_MAX_RANGES);
     const int64_t rows = (int64_t)batch * decode_query_len * MSA_NUM_HEADS;
-    int64_t words = msa::kFusedHeaderWords + 2 * (int64_t)batch * num_ranges + rows;
-    if (with_pool)
-        words = (words + 3) / 4 * 4 + rows * cols;  // the pool starts 16-byte aligned
-    return words;
+    if (with_pool)  // the pool starts 16-byte aligned
+        return msa::fused_pool_offset(batch, decode_query_len, num_ranges) + rows * cols;
+    return msa::fused_counter_words(batch, decode_query_len, num_ranges);
 }
 
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
@@ -275,9 +274,8 @@ int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num
               (long long)workspace_words, (long long)need);
     float* plane = score_out;
     if (pool) {
-        const int64_t off = (msa::kFusedHeaderWords + 2 * (int64_t)batch * num_ranges +
-                             (int64_t)batch * decode_query_len * MSA_NUM_HEADS + 3) / 4 * 4;
-        plane = reinterpret_cast<float*>(workspace + off);
+        plane = reinterpret_cast<float*>(
+            workspace + msa::fused_pool_offset(batch, decode_query_len, num_ranges));
     }
     msa::ScoreSelectParams q;
     int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
@@ -310,6 +308,7 @@ int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num
     q.num_ranges = num_ranges;
     q.width = width;
     q.pool = pool ? 1 : 0;
+    q.helpers = 0;
     return launch_result(msa::launch_score_select(q, stream), fn);
 }
 

@@ -81,11 +81,23 @@ struct SelectMergeParams {
 };
 
 // Scorer plus per-range select (and merge) in one launch (same ranges as
-// SelectParams). Workspace: kFusedHeaderWords words of counters, then
-// 2 * batch * R words (ready queue, range counters), then T * 4 merge
-// tickets, then (pool mode) a 16-byte aligned plane of T * 4 * cols floats.
-constexpr int kFusedHeaderWords = 128;
+// SelectParams). Workspace: one 128-byte line per range (word 0: columns
+// stored, word 1: select jobs done), then T * 4 merge tickets, then (pool
+// mode) a 16-byte aligned plane of T * 4 * cols floats.
+constexpr int kFusedLineWords = 32;
 constexpr int kMaxFusedMergeRanges = 64;
+
+// Words of the counters (range lines and tickets), and the word offset of the
+// pool plane.
+inline int64_t fused_counter_words(int64_t batch, int64_t dql, int64_t num_ranges)
+{
+    return batch * num_ranges * kFusedLineWords + batch * dql * 4;
+}
+inline int64_t fused_pool_offset(int64_t batch, int64_t dql, int64_t num_ranges)
+{
+    return (fused_counter_words(batch, dql, num_ranges) + 3) / 4 * 4;
+}
+
 struct ScoreSelectParams {
     ScoreParams score;       // score.out: the caller's plane, or the pool
     const int32_t* nvp;      // [batch*dql]
@@ -96,6 +108,7 @@ struct ScoreSelectParams {
     int32_t local_blocks;
     int32_t num_ranges;
     int32_t width;           // ceil(cols / R) <= kMaxFusedWidth
+    int32_t helpers;         // waves that run the select jobs (set by the launcher)
     int32_t pool;            // 1: score.out points into the workspace
 };
 

@@ -58,6 +58,7 @@
 // B share gives the same sum.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "msa_internal.h"
@@ -583,36 +584,21 @@ void score_decode_kernel(ScoreParams p)
 // expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Polls of any wait in score_select_kernel before it gives up and counts an
-// error. Every wait there ends by the launch's protocol (below); this bound
-// only keeps a defect from hanging the device.
+// Polls of a helper's wait in score_select_kernel before it gives up and
+// counts an error. Every wait there ends by the launch's protocol (below);
+// this bound only keeps a defect from hanging the device.
 constexpr uint32_t kMaxPolls = 1u << 20;
 
-// Workspace of score_select_kernel (int32 words): four counters on their own
-// 128-byte lines, then the ready queue (a range id + 1 per completed range, in
-// completion order), the per-range column counters, the per-(token, head)
-// merge tickets, and, when the caller passes no plane, the pool plane.
-struct FusedWs {
-    int32_t* started;   // waves that have begun
-    int32_t* finished;  // waves that are done; the last one clears the workspace
-    int32_t* ready;     // completed ranges (the queue's length)
-    int32_t* claimed;   // select jobs taken
-    int32_t* queue;     // [batch * R]
-    int32_t* ctr;       // [batch * R] columns stored per range
-    int32_t* ticket;    // [T * 4] range rows written per (token, head)
-};
-
-__device__ __forceinline__ FusedWs fused_ws(const ScoreSelectParams& q)
+// Counters of range rr (its own 128-byte line: adds to different ranges do not
+// queue behind each other): columns stored, and select jobs done.
+__device__ __forceinline__ int32_t* range_line(const ScoreSelectParams& q, int64_t rr)
 {
-    FusedWs f;
-    f.started = q.workspace;
-    f.finished = q.workspace + 32;
-    f.ready = q.workspace + 64;
-    f.claimed = q.workspace + 96;
-    f.queue = q.workspace + kFusedHeaderWords;
-    f.ctr = f.queue + (int64_t)q.score.batch * q.num_ranges;
-    f.ticket = f.ctr + (int64_t)q.score.batch * q.num_ranges;
-    return f;
+    return q.workspace + rr * kFusedLineWords;
+}
+
+__device__ __forceinline__ int32_t* merge_tickets(const ScoreSelectParams& q)
+{
+    return q.workspace + (int64_t)q.score.batch * q.num_ranges * kFusedLineWords;
 }
 
 // Wave-uniform agent-scope atomics, issued by lane 0.
@@ -632,15 +618,11 @@ __device__ __forceinline__ int lane0_add(int32_t* a, int n)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-__device__ __forceinline__ bool lane0_cas(int32_t* a, int expected, int desired)
+// An add whose old value is not needed (the wave does not wait for it).
+__device__ __forceinline__ void lane0_add_posted(int32_t* a, int n)
 {
-    int ok = 0;
     if (__lane_id() == 0)
-        ok = __hip_atomic_compare_exchange_strong(a, &expected, desired, __ATOMIC_RELAXED,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 ? 1
-                 : 0;
-    return __builtin_amdgcn_readfirstlane(ok) != 0;
+        __hip_atomic_fetch_add(a, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void lane0_store(int32_t* a, int v)
@@ -649,20 +631,12 @@ __device__ __forceinline__ void lane0_store(int32_t* a, int v)
         __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Columns of range r that request b writes (its row's expected count).
-__device__ __forceinline__ int range_columns(const ScoreSelectParams& q, int b, int r)
+// Columns of range r that a request writing wb columns writes (the range
+// counter's final value).
+__device__ __forceinline__ int range_columns(const ScoreSelectParams& q, int wb, int r)
 {
-    bool clamped;
-    const int wb = written_cols(q.score.seq_lens[b], q.score.cols, clamped);
     const int lo = r * q.width;
     return max(0, min(min(lo + q.width, q.score.cols), wb) - lo);
-}
-
-// Appends range rr to the ready queue (its select jobs become claimable).
-__device__ __forceinline__ void publish_range(const FusedWs& f, int64_t rr)
-{
-    const int slot = lane0_add(f.ready, 1);
-    lane0_store(f.queue + slot, (int)rr + 1);
 }
 
 // Merge of row th's R range rows (written through by other waves, read with
@@ -715,28 +689,28 @@ __device__ __forceinline__ void fused_merge(const ScoreSelectParams& q, int64_t 
 // Score plane (or pool) and per-range Top16 rows, and optionally their merge,
 // in one launch ("flashinfer.msa_ops.prepare_msa_icp_indexer", decode: a fused
 // scorer can replace the score and select steps, with caller-owned pool
-// storage). Protocol, with no wait on a wave that may not have started:
-//  1. Every wave counts itself in `started`, then scores its columns as
-//     score_decode_kernel does, storing them written through to the device's
-//     coherence point (sc1). After each request segment it waits for those
-//     stores and adds the segment's columns to each range's counter; the wave
-//     whose add completes a range appends it to the ready queue. Ranges with
-//     no written column are appended by workgroup 0 at the start.
-//  2. Select jobs ((range, row of the range) pairs, numbered in queue order)
-//     are claimed one at a time by compare-and-swap on `claimed`, only below
-//     the number of ready jobs. A wave that finds none ready keeps polling
-//     only while every wave of the grid has started (then every range still
-//     open belongs to running waves, which finish their scoring without
-//     waiting); otherwise it leaves, and the waves that complete the
-//     remaining ranges claim their jobs themselves. A job selects its row of
-//     the range exactly as top16_select_kernel does (agent-scope loads of the
-//     plane) and writes the range row written through.
-//  3. With a merged output, the job then adds 1 to its (token, head) ticket;
-//     the job that brings it to R merges the R rows as msa_top16_merge does
-//     and clears the ticket.
-//  4. Every wave counts itself in `finished` last; the wave that completes
-//     the count clears the counters, the queue and the range counters, so the
-//     workspace holds zeros again for the next launch.
+// storage). Protocol:
+//  1. Every wave scores its columns as score_decode_kernel does, storing them
+//     written through to the device's coherence point (sc1). After each
+//     request segment it waits for those stores, then adds the segment's
+//     columns to each range's counter (a posted add: nothing waits on it).
+//     A range is complete when its counter reaches the columns it writes.
+//  2. Select jobs ((range, row of the range) pairs, range-major) belong to
+//     q.helpers waves spread evenly over the grid's slots, each with a
+//     contiguous block of jobs. For each it waits until the job's range is
+//     complete, selects its row of the range exactly as top16_select_kernel
+//     does (agent-scope loads of the plane), writes the range row written
+//     through, and adds 1 to the range's done count; the helper that
+//     completes that count (every other job of the range has then seen the
+//     range complete) clears both of the range's counters. Only helpers
+//     wait, the launcher keeps them to at most half the waves the device
+//     holds at once, and scoring never waits, so every wave of the grid gets
+//     a slot and every range completes.
+//  3. With a merged output, a job then adds 1 to its (token, head) ticket; the
+//     job that brings it to R merges the R rows as msa_top16_merge does and
+//     clears the ticket.
+// The workspace thus holds zeros again when the launch ends (unless a wait
+// gives up, which counts an error).
 template <int NT, int kParts, int kWavesPerEU, int V, int kUnit>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void score_select_kernel(ScoreSelectParams q)
@@ -749,138 +723,104 @@ void score_select_kernel(ScoreSelectParams q)
     const int lane = threadIdx.x;
     const int R = q.num_ranges;
     const int w = q.width;
-    const FusedWs f = fused_ws(q);
     const int rows_per_range = p.dql * kHeads;
-    const int64_t n_ranges = (int64_t)p.batch * R;
-    const int64_t total_jobs = n_ranges * rows_per_range;
-    const int grid = (int)gridDim.x;
-
-    lane0_add(f.started, 1);
-    if (blockIdx.x == 0) {  // ranges with no written column are ready at once
-        for (int64_t rr = lane; rr < n_ranges; rr += 64) {
-            if (range_columns(q, (int)(rr / R), (int)(rr % R)) == 0) {
-                const int slot =
-                    __hip_atomic_fetch_add(f.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(f.queue + slot, (int)rr + 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
+    const int64_t total_jobs = (int64_t)p.batch * R * rows_per_range;
 
     // 1. scoring
     score_wave_range<NT, kParts, true, kUnit, false>(p, tile, res, [&](int b, int c_begin, int c_end) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the segment's stores are complete
         for (int r = c_begin / w; r * w < c_end; ++r) {
             const int n = min(c_end, (r + 1) * w) - max(c_begin, r * w);
-            const int64_t rr = (int64_t)b * R + r;
-            const int old = lane0_add(f.ctr + rr, n);
-            if (old + n == range_columns(q, b, r))
-                publish_range(f, rr);
+            lane0_add_posted(range_line(q, (int64_t)b * R + r), n);
         }
     });
 
-    // 2. and 3. select jobs, then merges
-    uint32_t polls = 0;
-    bool gave_up = false;
-    while (true) {
-        const int c = lane0_load(f.claimed);
-        if ((int64_t)c >= total_jobs)
-            break;
-        const int64_t ready_jobs = (int64_t)lane0_load(f.ready) * rows_per_range;
-        if ((int64_t)c < ready_jobs) {
-            if (!lane0_cas(f.claimed, c, c + 1))
-                continue;  // another wave took job c
-            polls = 0;
-            const int slot = c / rows_per_range;
-            const int row = c - slot * rows_per_range;
-            int rr1;
-            while ((rr1 = lane0_load(f.queue + slot)) == 0) {  // its publisher is writing it
-                if (++polls > kMaxPolls) {
-                    gave_up = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (gave_up)
-                break;
-            const int64_t rr = rr1 - 1;
-            const int b = (int)(rr / R);
-            const int r = (int)(rr - (int64_t)b * R);
-            const int t = b * p.dql + row / kHeads;
-            const int64_t th = (int64_t)t * kHeads + row % kHeads;
-            // valid ids [0, n): num_valid_pages, clamped to the plane (and,
-            // for the pool, to the columns this launch writes)
-            bool clamped;
-            const int limit = q.pool ? written_cols(p.seq_lens[b], p.cols, clamped) : p.cols;
-            int n = q.nvp[t];
-            if (n < 0 || n > limit) {
-                if (r == 0 && (row % kHeads) == 0 && lane == 0 && p.errors)
+    // 2. and 3. select jobs, then merges. Helper k sits at slot
+    // floor(k * grid / helpers) and runs the range-major jobs
+    // [k * total / helpers, (k + 1) * total / helpers): for even ranges those
+    // are rows of ranges this wave's neighbours scored (on its own XCD), which
+    // complete about when the helper's own scoring does.
+    const int64_t helpers = q.helpers;
+    const int64_t grid = gridDim.x;
+    const int64_t slot = kUnit == 1 ? (int64_t)blockIdx.x : (int64_t)split_slot();
+    const int64_t k = (slot * helpers + grid - 1) / grid;
+    if (k >= helpers || k * grid / helpers != slot)
+        return;
+    int32_t* tickets = merge_tickets(q);
+    const int64_t job_end = (k + 1) * total_jobs / helpers;
+    for (int64_t c = k * total_jobs / helpers; c < job_end; ++c) {
+        const int64_t rr = c / rows_per_range;
+        const int row = (int)(c - rr * rows_per_range);
+        const int b = (int)(rr / R);
+        const int r = (int)(rr - (int64_t)b * R);
+        const int t = b * p.dql + row / kHeads;
+        const int64_t th = (int64_t)t * kHeads + row % kHeads;
+        // valid ids [0, n): num_valid_pages, clamped to the plane (and, for
+        // the pool, to the columns this launch writes)
+        bool clamped;
+        const int wb = written_cols(p.seq_lens[b], p.cols, clamped);
+        const int limit = q.pool ? wb : p.cols;
+        const int nvp = q.nvp[t];
+        int32_t* line = range_line(q, rr);
+        const int want = range_columns(q, wb, r);
+        uint32_t polls = 0;
+        while (lane0_load(line) != want) {
+            if (++polls > kMaxPolls) {
+                if (lane == 0 && p.errors)
                     atomicAdd(p.errors, 1);
-                n = n < 0 ? 0 : limit;
+                return;
             }
-            const int lo = r * w;
-            const int hi = min(lo + w, p.cols);
-            float sv[V];
-            topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
-            topk::select_loaded<V>(sv, lo, hi, topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
-                                   &row_buf, lane, cand);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // the range row, written through (a merging wave reads it)
-            int32_t* dst = reinterpret_cast<int32_t*>(q.out + th * R + r);
-            if (lane < 2 * kTop)
-                __hip_atomic_store(dst + lane, reinterpret_cast<const int32_t*>(&row_buf)[lane],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (q.merged != nullptr) {
-                if (R == 1) {
-                    if (lane < 2 * kTop)
-                        reinterpret_cast<int32_t*>(q.merged + th)[lane] =
-                            reinterpret_cast<const int32_t*>(&row_buf)[lane];
-                } else {
-                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row is stored
-                    if (lane0_add(f.ticket + th, 1) == R - 1) {
-                        const int nm = max(0, q.nvp[t]);  // as msa_top16_merge reads it
-                        if (R <= 4)
-                            fused_merge<1>(q, th, nm, lane, cand);
-                        else if (R <= 8)
-                            fused_merge<2>(q, th, nm, lane, cand);
-                        else if (R <= 16)
-                            fused_merge<4>(q, th, nm, lane, cand);
-                        else
-                            fused_merge<16>(q, th, nm, lane, cand);
-                        lane0_store(f.ticket + th, 0);
-                    }
+            __builtin_amdgcn_s_sleep(4);
+        }
+
+        int n = nvp;
+        if (n < 0 || n > limit) {
+            if (r == 0 && (row % kHeads) == 0 && lane == 0 && p.errors)
+                atomicAdd(p.errors, 1);
+            n = n < 0 ? 0 : limit;
+        }
+        const int lo = r * w;
+        const int hi = min(lo + w, p.cols);
+        float sv[V];
+        topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
+        topk::select_loaded<V>(sv, lo, hi, topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
+                               &row_buf, lane, cand);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // the range row, written through (a merging wave reads it)
+        int32_t* dst = reinterpret_cast<int32_t*>(q.out + th * R + r);
+        if (lane < 2 * kTop)
+            __hip_atomic_store(dst + lane, reinterpret_cast<const int32_t*>(&row_buf)[lane],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (q.merged != nullptr) {
+            if (R == 1) {
+                if (lane < 2 * kTop)
+                    reinterpret_cast<int32_t*>(q.merged + th)[lane] =
+                        reinterpret_cast<const int32_t*>(&row_buf)[lane];
+            } else {
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the row is stored
+                if (lane0_add(tickets + th, 1) == R - 1) {
+                    const int nm = max(0, nvp);  // as msa_top16_merge reads it
+                    if (R <= 4)
+                        fused_merge<1>(q, th, nm, lane, cand);
+                    else if (R <= 8)
+                        fused_merge<2>(q, th, nm, lane, cand);
+                    else if (R <= 16)
+                        fused_merge<4>(q, th, nm, lane, cand);
+                    else
+                        fused_merge<16>(q, th, nm, lane, cand);
+                    lane0_store(tickets + th, 0);
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            continue;
         }
-        // nothing ready: wait only while every wave of the grid is running or done
-        if (lane0_load(f.started) < grid)
-            break;
-        if (++polls > kMaxPolls) {
-            gave_up = true;
-            break;
+        if (lane0_add(line + 1, 1) == rows_per_range - 1) {
+            lane0_store(line, 0);
+            lane0_store(line + 1, 0);
         }
-        __builtin_amdgcn_s_sleep(2);
-    }
-    if (gave_up && lane == 0 && p.errors)
-        atomicAdd(p.errors, 1);
-
-    // 4. the last wave out clears the workspace
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (lane0_add(f.finished, 1) == grid - 1) {
-        for (int64_t i = lane; i < 2 * n_ranges; i += 64)
-            f.queue[i] = 0;  // queue and range counters
-        if (lane == 0) {
-            *f.started = 0;
-            *f.ready = 0;
-            *f.claimed = 0;
-            *f.finished = 0;
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -1015,7 +955,19 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
     if (fn == nullptr)
         return hipErrorInvalidValue;
     const int64_t grid = latency ? max_cols : score_grid(q.score);
-    void* args[] = {const_cast<ScoreSelectParams*>(&q)};
+    // Helpers wait for ranges; at most half of the waves the device holds at
+    // once may, so that the rest of the grid always finds slots.
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64, 0);
+    if (e != hipSuccess)
+        return e;
+    const int64_t resident = (int64_t)per_cu * device_cus();
+    const int64_t jobs = (int64_t)q.score.batch * q.num_ranges * q.score.dql * kHeads;
+    if (resident < 2)
+        return hipErrorInvalidConfiguration;
+    ScoreSelectParams qh = q;
+    qh.helpers = (int)std::min(std::min(jobs, resident / 2), grid);
+    void* args[] = {&qh};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), args, 0, stream);
 }
 

@@ -389,9 +389,12 @@ def test_prefill_plan_words():
 
 
 def test_score_select_workspace_words():
-    # 128 counter words, a queue word and a counter per range, a ticket per row
-    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8) == 128 + 2 * 32 + 128
-    # the pool starts 16-byte aligned: 320 words, then 128 rows x 8192 floats
-    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8, pool=True) == 320 + 128 * 8192
+    # a 32-word counter line per (request, range), a ticket per (token, head)
+    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8) == 32 * 32 + 128
+    # the pool starts 16-byte aligned: 1152 words, then 128 rows x 8192 floats
+    assert msa.msa_score_select_workspace_words(4, 8, 8192, 8, pool=True) == 1152 + 128 * 8192
+    # B=1, dql 1, R 3: 96 + 4 = 100 words, already a multiple of 4
+    assert msa.msa_score_select_workspace_words(1, 1, 32, 3) == 100
+    assert msa.msa_score_select_workspace_words(1, 2, 32, 3, pool=True) == 104 + 8 * 32
     with pytest.raises(msa.MsaError):
         msa.msa_score_select_workspace_words(1, 9, 32, 1)
