@@ -70,6 +70,8 @@ extern "C" {
 #define MSA_PREFILL_PLAN_HEADER_WORDS 8    /* int32 words before a prefill plan's items    */
 #define MSA_PREFILL_ITEM_WORDS 8           /* int32 words per prefill plan item            */
 #define MSA_PREFILL_MAX_BATCH 8192         /* requests one prefill plan takes              */
+#define MSA_NOALLOC_SCRATCH_WORDS (4 * 1024 * 1024) /* int32 words (16 MiB per device) of
+                                                       msa_score_select_noalloc's workspace */
 
 /*
  * One Top16 row (128 bytes). score[i] is the score-plane value of block
@@ -203,6 +205,34 @@ int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num
                      int32_t num_ranges, msa_top16_row* out, msa_top16_row* merged,
                      int32_t* workspace, int64_t workspace_words, int32_t* errors,
                      hipStream_t stream);
+
+/*
+ * msa_score_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The workspace is a device array of
+ * MSA_NOALLOC_SCRATCH_WORDS int32 words inside the library (16 MiB; one copy
+ * per device, held from the library's load until the process ends; its
+ * address is looked up on the first call on each device). The call allocates
+ * nothing: it clears the array's counter words with a small kernel on
+ * `stream` (no memset node, so it can be captured), then launches
+ * msa_score_select's kernel on the array.
+ *
+ * Arguments, outputs and errors are those of msa_score_select. Sizes whose
+ * msa_score_select_workspace_words(batch, decode_query_len, cols, num_ranges,
+ * score_out == NULL) exceeds MSA_NOALLOC_SCRATCH_WORDS return
+ * MSA_ERR_INVALID_ARG with nothing launched (with score_out NULL that is
+ * about batch * decode_query_len * 4 * cols <= 4 Mi pool floats). Every call
+ * on a device shares that device's array, which keeps the last call's
+ * contents (with score_out NULL, its pool scores): calls that overlap on one
+ * device (several streams or host threads) race, and the caller orders them.
+ */
+int msa_score_select_noalloc(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                             const int32_t* block_table, int64_t block_table_stride,
+                             const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                             int32_t decode_query_len, float* score_out, int32_t cols,
+                             const int32_t* num_valid_pages, int32_t init_blocks,
+                             int32_t local_blocks, int32_t num_ranges, msa_top16_row* out,
+                             msa_top16_row* merged, int32_t* errors, hipStream_t stream);
 
 /*
  * Step 2: Top16 select per (token, head, column range).

@@ -39,7 +39,10 @@ EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
            "msa_score_columns", "msa_warmup", "msa_last_error", "msa_stream_read_probe",
            "msa_contraction_probe", "msa_prefill_plan_words", "msa_prefill_window_plan",
-           "msa_prefill_local", "msa_prefill_merge", "msa_score_select_workspace_words")
+           "msa_prefill_local", "msa_prefill_merge", "msa_score_select_workspace_words",
+           "msa_score_select_noalloc")
+
+NOALLOC_SCRATCH_WORDS = 4 * 1024 * 1024  # MSA_NOALLOC_SCRATCH_WORDS
 
 PREFILL_WINDOW_TOKENS = 64  # MSA_PREFILL_WINDOW_TOKENS
 PREFILL_PLAN_HEADER_WORDS = 8
@@ -81,6 +84,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_score_select_workspace_words.argtypes = [i32, i32, i32, i32, i32]
     lib.msa_score_select_workspace_words.restype = i64
     lib.msa_score_select.restype = ctypes.c_int
+    lib.msa_score_select_noalloc.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, P, i32, P, i32,
+                                             i32, i32, P, P, P, P]
+    lib.msa_score_select_noalloc.restype = ctypes.c_int
     lib.msa_score_decode_sharded.argtypes = [P, P, i64, P, i64, P, i32, i32, i32, i32, i32, P,
                                              i32, P, P]
     lib.msa_score_decode_sharded.restype = ctypes.c_int
@@ -289,17 +295,9 @@ def score_select_workspace(batch: int, decode_query_len: int, cols: int, num_ran
                        dtype=torch.int32, device=device)
 
 
-def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
-                     seq_lens: torch.Tensor, score_out: torch.Tensor | None,
-                     num_valid_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                     *, page_size: int, decode_query_len: int, init_blocks: int,
-                     local_blocks: int, num_ranges: int = 1, cols: int | None = None,
-                     merged: torch.Tensor | None = None, errors: torch.Tensor | None = None,
-                     stream=None) -> None:
-    """Score plane (or, with score_out None, the workspace's pool of `cols`
-    columns), per-range Top16 rows `out` [T, 4, R, 32] and optionally their
-    merge `merged` [T, 4, 32], in one launch. `workspace` is a zeroed int32
-    tensor (see score_select_workspace)."""
+def _score_select_args(index_q, index_k, block_table, seq_lens, score_out, num_valid_pages, out,
+                       page_size, decode_query_len, num_ranges, cols, merged):
+    """Checked arguments of msa_score_select up to `merged` (marshalling only)."""
     q = _u8(index_q, "index_q")
     k = _u8(index_k, "index_k")
     B = seq_lens.numel()
@@ -321,7 +319,7 @@ def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
         args = (q.data_ptr(), k.data_ptr(), k.shape[0], block_table.data_ptr(),
                 block_table.shape[1], seq_lens.data_ptr(), B, page_size, decode_query_len,
                 None, int(cols))
-    _dev(q, num_valid_pages, out, workspace)
+    _dev(q, num_valid_pages, out)
     _need(num_valid_pages.dtype == torch.int32 and num_valid_pages.shape == (T,),
           "num_valid_pages: int32 [T]")
     _need(out.dtype == torch.int32 and out.shape == (T, NUM_HEADS, num_ranges, ROW_WORDS) and
@@ -330,13 +328,49 @@ def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: 
         _dev(out, merged)
         _need(merged.dtype == torch.int32 and merged.shape == (T, NUM_HEADS, ROW_WORDS) and
               merged.is_contiguous(), f"merged: contiguous int32 [{T}, 4, 32]")
+    return (*args, num_valid_pages.data_ptr())
+
+
+def msa_score_select(index_q: torch.Tensor, index_k: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, score_out: torch.Tensor | None,
+                     num_valid_pages: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                     *, page_size: int, decode_query_len: int, init_blocks: int,
+                     local_blocks: int, num_ranges: int = 1, cols: int | None = None,
+                     merged: torch.Tensor | None = None, errors: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """Score plane (or, with score_out None, the workspace's pool of `cols`
+    columns), per-range Top16 rows `out` [T, 4, R, 32] and optionally their
+    merge `merged` [T, 4, 32], in one launch. `workspace` is a zeroed int32
+    tensor (see score_select_workspace)."""
+    args = _score_select_args(index_q, index_k, block_table, seq_lens, score_out,
+                              num_valid_pages, out, page_size, decode_query_len, num_ranges,
+                              cols, merged)
+    _dev(out, workspace)
     _need(workspace.dtype == torch.int32 and workspace.dim() == 1 and workspace.is_contiguous(),
           "workspace: contiguous int32 [words]")
-    _check(load().msa_score_select(*args, num_valid_pages.data_ptr(), init_blocks, local_blocks,
-                                   num_ranges, out.data_ptr(),
+    _check(load().msa_score_select(*args, init_blocks, local_blocks, num_ranges, out.data_ptr(),
                                    merged.data_ptr() if merged is not None else None,
                                    workspace.data_ptr(), workspace.numel(), _errors_ptr(errors),
                                    _stream_handle(stream)))
+
+
+def msa_score_select_noalloc(index_q: torch.Tensor, index_k: torch.Tensor,
+                             block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             score_out: torch.Tensor | None, num_valid_pages: torch.Tensor,
+                             out: torch.Tensor, *, page_size: int, decode_query_len: int,
+                             init_blocks: int, local_blocks: int, num_ranges: int = 1,
+                             cols: int | None = None, merged: torch.Tensor | None = None,
+                             errors: torch.Tensor | None = None, stream=None) -> None:
+    """msa_score_select on the library's own device scratch array (no
+    workspace argument, nothing allocated); calls on one device must not
+    overlap."""
+    args = _score_select_args(index_q, index_k, block_table, seq_lens, score_out,
+                              num_valid_pages, out, page_size, decode_query_len, num_ranges,
+                              cols, merged)
+    _check(load().msa_score_select_noalloc(*args, init_blocks, local_blocks, num_ranges,
+                                           out.data_ptr(),
+                                           merged.data_ptr() if merged is not None else None,
+                                           _errors_ptr(errors), _stream_handle(stream)))
 
 
 def msa_top16_select(scores: torch.Tensor, num_valid_pages: torch.Tensor, out: torch.Tensor, *,

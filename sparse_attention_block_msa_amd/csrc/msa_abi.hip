@@ -1,11 +1,21 @@
 // C-ABI entry points: host-side argument checks, then one kernel launch each
-// on the caller's stream. Nothing here allocates or synchronises.
+// on the caller's stream (msa_score_select_noalloc: two). Nothing here
+// allocates or synchronises.
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <algorithm>
+#include <mutex>
 
 #include "contraction_probe.h"
 #include "msa_internal.h"
 #include "stream_probe.h"
+
+// The workspace of msa_score_select_noalloc: counters and, for calls
+// without a plane, the pool. One copy per device, from the library's load
+// until the process ends. Host code uses only the device address that
+// hipGetSymbolAddress returns for it (scratch_address), never this name.
+static __device__ __align__(256) int32_t scratch[MSA_NOALLOC_SCRATCH_WORDS];
 
 namespace {
 
@@ -37,6 +47,34 @@ bool aligned(const void* ptr, uintptr_t a)
         if (!(cond))                                           \
             return fail(MSA_ERR_INVALID_ARG, __VA_ARGS__);     \
     } while (0)
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+int32_t* g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+int scratch_address(const char* fn, int32_t** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(MSA_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MSA_ERR_INVALID_ARG, "%s: device %d is past the %d this library tracks", fn,
+                    dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(MSA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s",
+                        fn, dev, hipGetErrorString(e));
+        g_scratch[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return MSA_OK;
+}
 
 int check_forced(const char* fn, int32_t init_blocks, int32_t local_blocks)
 {
@@ -161,6 +199,120 @@ int merge_impl(const char* fn, const msa_top16_row* partial, int32_t num_tokens,
     return MSA_OK;
 }
 
+
+// Zeroes n int32 words (a kernel, so that a captured graph records no memset
+// node).
+__global__ void clear_words_kernel(int32_t* p, int64_t n)
+{
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step)
+        p[i] = 0;
+}
+
+hipError_t launch_clear_words(int32_t* p, int64_t n, hipStream_t stream)
+{
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+// Workspace words of msa_score_select for these sizes, or MSA_ERR_INVALID_ARG
+// (message set) for sizes it rejects.
+int64_t score_select_words(const char* fn, int32_t batch, int32_t decode_query_len,
+                           int32_t cols, int32_t num_ranges, bool with_pool)
+{
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    const int64_t rows = (int64_t)batch * decode_query_len * MSA_NUM_HEADS;
+    if (with_pool)  // the pool starts 16-byte aligned
+        return msa::fused_pool_offset(batch, decode_query_len, num_ranges) + rows * cols;
+    return msa::fused_counter_words(batch, decode_query_len, num_ranges);
+}
+
+// msa_score_select on `workspace`; with clear_counters, the workspace's
+// counter words are first cleared by a kernel on `stream` (after every check
+// has passed).
+int score_select_impl(const char* fn, const uint8_t* index_q, const uint8_t* index_k,
+                      int64_t num_pages, const int32_t* block_table, int64_t block_table_stride,
+                      const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                      int32_t decode_query_len, float* score_out, int32_t cols,
+                      const int32_t* num_valid_pages, int32_t init_blocks, int32_t local_blocks,
+                      int32_t num_ranges, msa_top16_row* out, msa_top16_row* merged,
+                      int32_t* workspace, int64_t workspace_words, bool clear_counters,
+                      int32_t* errors, hipStream_t stream)
+{
+    MSA_CHECK(workspace && aligned(workspace, 16), "%s: workspace must be non-null and 16-byte "
+              "aligned", fn);
+    const bool pool = score_out == nullptr;
+    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
+              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
+              MSA_MAX_RANGES);
+    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
+              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
+              MSA_MAX_SCORE_COLS);
+    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
+    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
+              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
+              decode_query_len);
+    const int64_t need = score_select_words(fn, batch, decode_query_len, cols, num_ranges, pool);
+    MSA_CHECK(workspace_words >= need, "%s: workspace_words (%lld) must be >= %lld", fn,
+              (long long)workspace_words, (long long)need);
+    float* plane = score_out;
+    if (pool) {
+        plane = reinterpret_cast<float*>(
+            workspace + msa::fused_pool_offset(batch, decode_query_len, num_ranges));
+    }
+    msa::ScoreSelectParams q;
+    int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
+                          seq_lens, batch, page_size, decode_query_len, plane, cols, errors,
+                          &q.score);
+    if (rc != MSA_OK)
+        return rc;
+    MSA_CHECK(num_valid_pages && out, "%s: null pointer argument", fn);
+    MSA_CHECK(aligned(num_valid_pages, 4) && aligned(out, 4) && aligned(merged, 4),
+              "%s: arrays must be 4-byte aligned", fn);
+    const int64_t tokens = (int64_t)batch * decode_query_len;
+    MSA_CHECK(tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
+              "%s: tokens*4*num_ranges must be < 2^31", fn);
+    const int32_t width = (cols + num_ranges - 1) / num_ranges;
+    MSA_CHECK(width <= msa::kMaxFusedWidth,
+              "%s: ceil(cols / num_ranges) = %d exceeds %d; use msa_score_decode + "
+              "msa_top16_select", fn, width, msa::kMaxFusedWidth);
+    MSA_CHECK(merged == nullptr || num_ranges <= msa::kMaxFusedMergeRanges,
+              "%s: a merged output needs num_ranges <= %d (got %d); use msa_top16_merge", fn,
+              msa::kMaxFusedMergeRanges, num_ranges);
+    rc = check_forced(fn, init_blocks, local_blocks);
+    if (rc != MSA_OK)
+        return rc;
+    q.nvp = num_valid_pages;
+    q.out = out;
+    q.merged = merged;
+    q.workspace = workspace;
+    q.init_blocks = init_blocks;
+    q.local_blocks = local_blocks;
+    q.num_ranges = num_ranges;
+    q.width = width;
+    q.pool = pool ? 1 : 0;
+    q.helpers = 0;
+    if (clear_counters) {
+        const int64_t n = msa::fused_counter_words(batch, decode_query_len, num_ranges);
+        rc = launch_result(launch_clear_words(workspace, n, stream), fn);
+        if (rc != MSA_OK)
+            return rc;
+    }
+    return launch_result(msa::launch_score_select(q, stream), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,22 +377,9 @@ int msa_score_decode_sharded(const uint8_t* index_q, const uint8_t* index_k_shar
 int64_t msa_score_select_workspace_words(int32_t batch, int32_t decode_query_len, int32_t cols,
                                          int32_t num_ranges, int32_t with_pool)
 {
-    static const char* fn = "msa_score_select_workspace_words";
     g_last_error[0] = '\0';
-    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
-    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
-              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
-              decode_query_len);
-    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
-              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
-              MSA_MAX_SCORE_COLS);
-    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
-              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
-              MSA_MAX_RANGES);
-    const int64_t rows = (int64_t)batch * decode_query_len * MSA_NUM_HEADS;
-    if (with_pool)  // the pool starts 16-byte aligned
-        return msa::fused_pool_offset(batch, decode_query_len, num_ranges) + rows * cols;
-    return msa::fused_counter_words(batch, decode_query_len, num_ranges);
+    return score_select_words("msa_score_select_workspace_words", batch, decode_query_len, cols,
+                              num_ranges, with_pool != 0);
 }
 
 int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
@@ -253,63 +392,40 @@ int msa_score_select(const uint8_t* index_q, const uint8_t* index_k, int64_t num
                      hipStream_t stream)
 {
     g_last_error[0] = '\0';
-    const char* fn = "msa_score_select";
-    MSA_CHECK(workspace && aligned(workspace, 16), "%s: workspace must be non-null and 16-byte "
-              "aligned", fn);
-    const bool pool = score_out == nullptr;
-    MSA_CHECK(num_ranges >= 1 && num_ranges <= cols && num_ranges <= MSA_MAX_RANGES,
-              "%s: num_ranges (%d) must be in [1, min(cols, %d)]", fn, num_ranges,
-              MSA_MAX_RANGES);
-    MSA_CHECK(cols > 0 && cols <= MSA_MAX_SCORE_COLS && cols % 4 == 0,
-              "%s: cols (%d) must satisfy 0 < cols <= %d and cols %% 4 == 0", fn, cols,
-              MSA_MAX_SCORE_COLS);
-    MSA_CHECK(batch >= 1 && batch <= (1 << 22), "%s: batch (%d) must be in [1, 2^22]", fn, batch);
-    MSA_CHECK(decode_query_len >= 1 && 4 * decode_query_len <= 32,
-              "%s: decode_query_len (%d) must satisfy 1 <= len and 4*len <= 32", fn,
-              decode_query_len);
-    const int64_t need =
-        msa_score_select_workspace_words(batch, decode_query_len, cols, num_ranges, pool ? 1 : 0);
+    return score_select_impl("msa_score_select", index_q, index_k, num_pages, block_table,
+                             block_table_stride, seq_lens, batch, page_size, decode_query_len,
+                             score_out, cols, num_valid_pages, init_blocks, local_blocks,
+                             num_ranges, out, merged, workspace, workspace_words, false, errors,
+                             stream);
+}
+
+int msa_score_select_noalloc(const uint8_t* index_q, const uint8_t* index_k, int64_t num_pages,
+                             const int32_t* block_table, int64_t block_table_stride,
+                             const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                             int32_t decode_query_len, float* score_out, int32_t cols,
+                             const int32_t* num_valid_pages, int32_t init_blocks,
+                             int32_t local_blocks, int32_t num_ranges, msa_top16_row* out,
+                             msa_top16_row* merged, int32_t* errors, hipStream_t stream)
+{
     g_last_error[0] = '\0';
-    MSA_CHECK(workspace_words >= need, "%s: workspace_words (%lld) must be >= %lld", fn,
-              (long long)workspace_words, (long long)need);
-    float* plane = score_out;
-    if (pool) {
-        plane = reinterpret_cast<float*>(
-            workspace + msa::fused_pool_offset(batch, decode_query_len, num_ranges));
-    }
-    msa::ScoreSelectParams q;
-    int rc = score_params(fn, index_q, index_k, num_pages, block_table, block_table_stride,
-                          seq_lens, batch, page_size, decode_query_len, plane, cols, errors,
-                          &q.score);
+    const char* fn = "msa_score_select_noalloc";
+    const int64_t need =
+        score_select_words(fn, batch, decode_query_len, cols, num_ranges, score_out == nullptr);
+    if (need < 0)
+        return MSA_ERR_INVALID_ARG;  // message set by score_select_words
+    MSA_CHECK(need <= MSA_NOALLOC_SCRATCH_WORDS,
+              "%s: these sizes need %lld workspace words (counters%s), more than the %d of "
+              "the library's scratch array; use msa_score_select with a workspace",
+              fn, (long long)need, score_out == nullptr ? " and the pool plane" : "",
+              MSA_NOALLOC_SCRATCH_WORDS);
+    int32_t* ws = nullptr;
+    const int rc = scratch_address(fn, &ws);
     if (rc != MSA_OK)
         return rc;
-    MSA_CHECK(num_valid_pages && out, "%s: null pointer argument", fn);
-    MSA_CHECK(aligned(num_valid_pages, 4) && aligned(out, 4) && aligned(merged, 4),
-              "%s: arrays must be 4-byte aligned", fn);
-    const int64_t tokens = (int64_t)batch * decode_query_len;
-    MSA_CHECK(tokens * MSA_NUM_HEADS * num_ranges <= 0x7FFFFFFF,
-              "%s: tokens*4*num_ranges must be < 2^31", fn);
-    const int32_t width = (cols + num_ranges - 1) / num_ranges;
-    MSA_CHECK(width <= msa::kMaxFusedWidth,
-              "%s: ceil(cols / num_ranges) = %d exceeds %d; use msa_score_decode + "
-              "msa_top16_select", fn, width, msa::kMaxFusedWidth);
-    MSA_CHECK(merged == nullptr || num_ranges <= msa::kMaxFusedMergeRanges,
-              "%s: a merged output needs num_ranges <= %d (got %d); use msa_top16_merge", fn,
-              msa::kMaxFusedMergeRanges, num_ranges);
-    rc = check_forced(fn, init_blocks, local_blocks);
-    if (rc != MSA_OK)
-        return rc;
-    q.nvp = num_valid_pages;
-    q.out = out;
-    q.merged = merged;
-    q.workspace = workspace;
-    q.init_blocks = init_blocks;
-    q.local_blocks = local_blocks;
-    q.num_ranges = num_ranges;
-    q.width = width;
-    q.pool = pool ? 1 : 0;
-    q.helpers = 0;
-    return launch_result(msa::launch_score_select(q, stream), fn);
+    return score_select_impl(fn, index_q, index_k, num_pages, block_table, block_table_stride,
+                             seq_lens, batch, page_size, decode_query_len, score_out, cols,
+                             num_valid_pages, init_blocks, local_blocks, num_ranges, out, merged,
+                             ws, MSA_NOALLOC_SCRATCH_WORDS, true, errors, stream);
 }
 
 int msa_top16_select(const float* scores, int32_t num_tokens, int32_t cols,

@@ -398,3 +398,18 @@ def test_score_select_workspace_words():
     assert msa.msa_score_select_workspace_words(1, 2, 32, 3, pool=True) == 104 + 8 * 32
     with pytest.raises(msa.MsaError):
         msa.msa_score_select_workspace_words(1, 9, 32, 1)
+
+
+def test_score_select_noalloc_rejects_oversize(lib):
+    """Sizes past the library's scratch array are refused before any device call."""
+    # pool of 64 * 8 * 4 * 8192 floats > 4 Mi words
+    rc = lib.msa_score_select_noalloc(FAKE, FAKE, 10, FAKE, 64, FAKE, 64, 128, 8, None, 8192,
+                                      FAKE, 1, 2, 8, FAKE, None, None, None)
+    assert rc == msa.MSA_ERR_INVALID_ARG
+    assert "scratch" in lib.msa_last_error().decode()
+    # sizes msa_score_select_workspace_words rejects are refused the same way
+    rc = lib.msa_score_select_noalloc(FAKE, FAKE, 10, FAKE, 64, FAKE, 1, 128, 9, None, 32,
+                                      FAKE, 1, 2, 1, FAKE, None, None, None)
+    assert rc == msa.MSA_ERR_INVALID_ARG
+    assert "msa_score_select_noalloc" in lib.msa_last_error().decode()
+    assert msa.NOALLOC_SCRATCH_WORDS == 4 * 1024 * 1024
