@@ -1,43 +1,47 @@
 """Benchmark of the decode-time block indexer on one MI355X.
 
-One step = the whole chain on one batch of the long-context workload
+One step = the whole decode path on one batch of the long-context workload
 (4 requests x 1,048,576 keys, page_size 256, decode_query_len 8,
-plane 32 x 4 x 8192, Top16 over 8 column ranges, the per-range lists merged
-by msa_top16_merge):
+plane 32 x 4 x 8192, Top16 over 8 column ranges, the per-range lists merged):
 
-    msa_score_decode -> msa_top16_select (R=8) -> msa_top16_merge
+    msa_score_decode -> msa_top16_select_merge (per-range rows written, and
+                        their merge, in one launch)
 
-Two other forms of the same step, with bit-identical rows, are timed beside
-it: select and merge in one launch (msa_score_decode ->
-msa_top16_select_merge, the range rows kept in LDS;
-e2e.one_launch_select_merge), and the plane with the per-range rows in one
-launch followed by the merge (msa_score_select -> msa_top16_merge;
-e2e.score_select_then_merge). One rank's share of the same workload on a
-cache split by rows over 2 or 4 ranks (msa_score_decode_sharded ->
-msa_top16_select_mapped, then the owner's msa_top16_merge_dedup) is
-reported under e2e.sharded_rank_share.
+Where that one-launch form does not apply (one range, or more than 16, or
+ranges wider than 2048 columns) the step is msa_score_decode ->
+msa_top16_select [-> msa_top16_merge]. The other forms of the same step, all
+with bit-identical merged rows, are timed beside it under e2e.other_forms:
+the three-launch chain (score -> select -> merge), the whole-row select
+(select_merge without per-range rows), and msa_score_select (plane in the
+workspace pool, range rows and merge in the scoring launch). One rank's
+share of the same workload on a cache split by rows over 2 or 4 ranks
+(msa_score_decode_sharded -> msa_top16_select_mapped, then the owner's
+msa_top16_merge_dedup) is reported under e2e.sharded_rank_share, and the
+prefill chain on one 8192-token window under `prefill`.
 
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
 timing. Before every step a read pass over a 1 GiB buffer evicts index-K
 from the 256 MB Infinity Cache; it sits outside the step's event pair. (A
 read, not a fill: a 1 GiB fill would leave the caches full of dirty lines
-whose write-back the next kernel would pay for.) The step time is measured with HIP
-events on the stream the kernels run on; a second pass records an event
-between the kernels for per-kernel times. The roofline figure takes the
-scorer's per-launch duration from K launches back to back between one event
-pair, which leaves out the dispatch delay after each event record (that is
-what the kernel trace measures). The contract's wall clock brackets all K
-steps, fills included, with a synchronize on both sides.
+whose write-back the next kernel would pay for.) Step times are measured
+with HIP events on the stream the kernels run on; mean, p10, p50 and p90 are
+reported with their fractions of HBM peak. A second pass records an event
+between the kernels of the three-launch chain for per-kernel times. The
+roofline figure takes the scorer's per-launch duration from K launches back
+to back between one event pair, which leaves out the dispatch delay after
+each event record (that is what the kernel trace measures). The contract's
+wall clock brackets all K steps, reads included, with a synchronize on both
+sides.
 
 Prints one JSON line. `value` is scored keys/s, i.e. the sum of seq_len over
 the mean step time. `roofline` rates the scorer, the dominant kernel, against
 HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
 `roofline.mfma` is the scorer's MFMA work and busy fraction from rocprofv3
 counters (committed under profiles/, valid while the scorer's source hash
-matches). `roofline.stream_read_probe` times msa_stream_read_probe, a plain streaming
-read with no other work, over as many index-K bytes in the same way: the
-streaming ceiling the scorer's rate is read against. `cpu_baseline` times the oracle on the
-same workload.
+matches). `roofline.stream_read_probe` times msa_stream_read_probe, a plain
+streaming read with no other work, over as many index-K bytes and over
+4 GiB, in the same way: the streaming ceilings the scorer's rate is read
+against. `cpu_baseline` times the oracle on the same workload.
 """
 from __future__ import annotations
 
@@ -55,10 +59,12 @@ sys.path.insert(0, HERE)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30           # read before each step; > 256 MB Infinity Cache
 COPY_BYTES = 512 << 20          # calibration copy: reads and writes this many bytes
+PROBE_BIG_BYTES = 4 << 30       # the long streaming-read probe
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_score_decode_long_b4_s1m.json")
 MFMA_FILE = os.path.join(HERE, "profiles", "mfma_score_decode_long_b4_s1m.json")
 KERNEL_SOURCES = [os.path.join(HERE, "sparse_attention_block_msa_amd", "csrc", f)
-                  for f in ("score_decode.hip", "msa_internal.h")]
+                  for f in ("score_decode.hip", "score_tile.h", "msa_internal.h")]
 
 
 def kernel_source_hash() -> str:
@@ -226,6 +232,86 @@ def mfma_accuracy(tiles: int = 2048, seed: int = 77) -> dict:
     return result
 
 
+def timed_steps(fn, steps, stream, flush=None):
+    """K calls of fn, each after a cache-evicting read (when given) and inside
+    its own event pair; returns the sorted per-step times in ms."""
+    import torch
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.sum()
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(e[0].elapsed_time(e[1]) for e in evs)
+
+
+def step_stats(ms, launch_bytes, keys):
+    """Mean and percentiles of per-step times, as rates against HBM."""
+    mean = sum(ms) / len(ms)
+    pick = lambda f: ms[min(len(ms) - 1, int(len(ms) * f))]
+    frac = lambda t: launch_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    return {"ms_per_step": mean, "keys_per_s": keys / (mean * 1e-3),
+            "hbm_gbps": launch_bytes / (mean * 1e-3) / 1e9, "frac_of_peak": frac(mean),
+            "step_ms_p10": pick(0.1), "step_ms_p50": pick(0.5), "step_ms_p90": pick(0.9),
+            "frac_of_peak_p50": frac(pick(0.5)), "frac_of_peak_p90": frac(pick(0.9))}
+
+
+def prefill_figure(dev, stream, runs: int = 10) -> dict:
+    """The prefill chain (window plan -> local scoring and select -> merge) on
+    one long query window: 8192 query tokens at the end of a 65,536-key
+    request, page_size 256. Its contraction is compute-bound (4 * 8192 query
+    rows per key), so it is rated in useful MFMA flops: 2 * 128 per (query
+    row, visible key), against the bf16 dense peak."""
+    import torch
+
+    import sparse_attention_block_msa_amd as msa
+    import workloads
+
+    w = workloads.generate(name="prefill_q8192_s64k_p256", batch=1, seq=("fixed", 65536),
+                           q_lens=("fixed", 8192), page_size=256, dql=1, init=4, local=4,
+                           ranges=1, seed=3105)
+    T, R = w.num_tokens, w.num_ranges
+    q, k = w.index_q.to(dev), w.index_k.to(dev)
+    bt, qo = w.block_table.to(dev), w.qo_indptr.to(dev)
+    sl, nvp = w.seq_lens.to(dev), w.num_valid_pages.to(dev)
+    plane = torch.empty((T, 4, w.cols), dtype=torch.float32, device=dev)
+    plan = msa.new_prefill_plan(T, w.batch, w.cols, device=dev)
+    carrier = msa.new_rows(T, 4, R, device=dev)
+    merged = msa.new_rows(T, 4, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    sel = dict(init_blocks=w.init_blocks, local_blocks=w.local_blocks)
+
+    def chain():
+        msa.msa_prefill_window_plan(qo, sl, plan, num_tokens=T, cols=w.cols, errors=err,
+                                    stream=stream)
+        msa.msa_prefill_local(q, k, bt, plan, plane, nvp, carrier, page_size=w.page_size,
+                              num_ranges=R, errors=err, stream=stream, **sel)
+        msa.msa_prefill_merge(carrier, nvp, merged, errors=err, stream=stream, **sel)
+
+    for _ in range(3):
+        chain()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(runs):
+        chain()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"prefill: device error counter = {int(err.item())}")
+    ms = e[0].elapsed_time(e[1]) / runs
+    pos = w.positions.to(torch.float64)
+    useful = float(2 * 128 * 4 * (pos + 1).sum())
+    tflops = useful / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "query_tokens": T, "keys": int(w.seq_lens.sum()),
+            "step": "msa_prefill_window_plan -> msa_prefill_local -> msa_prefill_merge",
+            "ms_per_chain": ms, "chain_timing": f"{runs} chains back to back between one event pair",
+            "useful_flop": useful, "achieved_tflops": tflops,
+            "peak_tflops": BF16_PEAK_TFLOPS, "frac_of_bf16_peak": tflops / BF16_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +320,7 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload number (1..5)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting read pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill figure")
     ap.add_argument("--mfma-accuracy", action="store_true",
                     help="only measure the accumulation error of the fp8 and bf16 MFMA forms "
                          "(msa_contraction_probe) and print it as one JSON line")
@@ -267,106 +354,97 @@ def main():
     part = msa.new_rows(T, 4, R, device=dev)
     final = msa.new_rows(T, 4, device=dev)
     errors = torch.zeros(1, dtype=torch.int32, device=dev)
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else torch.ones(FLUSH_BYTES // 4, dtype=torch.float32,
+                                                 device=dev)
     msa.msa_warmup()
     stream = torch.cuda.current_stream()
+    sel = dict(init_blocks=w.init_blocks, local_blocks=w.local_blocks, errors=errors,
+               stream=stream)
+    keys = w.total_keys
+    launch_bytes = workloads.index_k_bytes(w)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def score():
         msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
                              decode_query_len=w.dql, errors=errors, stream=stream)
+
+    # Forms of the step; all leave bit-identical merged rows (the tests check
+    # each form against the others and the oracle).
+    one_launch = 1 < R <= 16 and -(-w.cols // R) <= 2048
+
+    def step_three(ev=None):
+        # score -> per-range select -> merge, three launches
+        if ev:
+            ev[0].record(stream)
+        score()
         if ev:
             ev[1].record(stream)
-        msa.msa_top16_select(plane, nvp, part, init_blocks=w.init_blocks,
-                             local_blocks=w.local_blocks, num_ranges=R, errors=errors,
-                             stream=stream)
+        msa.msa_top16_select(plane, nvp, part, num_ranges=R, **sel)
         if ev:
             ev[2].record(stream)
         if R > 1:
-            msa.msa_top16_merge(part, nvp, final, init_blocks=w.init_blocks,
-                                local_blocks=w.local_blocks, errors=errors, stream=stream)
+            msa.msa_top16_merge(part, nvp, final, **sel)
         if ev:
             ev[3].record(stream)
 
-    def step_fused():
-        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
-                             decode_query_len=w.dql, errors=errors, stream=stream)
-        msa.msa_top16_select_merge(plane, nvp, final, init_blocks=w.init_blocks,
-                                   local_blocks=w.local_blocks, num_ranges=R,
-                                   errors=errors, stream=stream)
+    def step_headline():
+        # score -> per-range select and their merge in one launch (the
+        # per-range rows are written as well)
+        score()
+        msa.msa_top16_select_merge(plane, nvp, final, num_ranges=R, partial=part, **sel)
 
-    # select and merge in one launch where that form applies (at most 16
-    # ranges of at most 2048 columns)
-    fused_applies = 1 < R <= 16 and -(-w.cols // R) <= 2048
+    def step_row_select():
+        # score -> the merged rows straight from the whole row (no per-range rows)
+        score()
+        msa.msa_top16_select_merge(plane, nvp, final, num_ranges=R, **sel)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush.sum()
-        step()
-        if fused_applies:
-            step_fused()
-    torch.cuda.synchronize()
-
-    # Timed region 1 (the headline): K steps, an event pair around each step
-    # only, so nothing is recorded between the kernels of a step.
-    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                   for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.sum()
-        step_events[i][0].record(stream)
-        step()
-        step_events[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    # Timed region 1b: the same K steps with select and merge in one launch
-    # (msa_top16_select_merge), reported beside the headline.
-    fused_ms = None
-    if fused_applies:
-        fused_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                        for _ in range(args.steps)]
-        for i in range(args.steps):
-            if not args.no_flush:
-                flush.sum()
-            fused_events[i][0].record(stream)
-            step_fused()
-            fused_events[i][1].record(stream)
-        torch.cuda.synchronize()
-        fused_ms = sum(ev[0].elapsed_time(ev[1]) for ev in fused_events) / args.steps
-
-    # Timed region 1c: the same K steps with the plane and the range rows from
-    # one launch (msa_score_select), then msa_top16_merge; reported beside the
-    # headline.
     ws = msa.score_select_workspace(w.batch, w.dql, w.cols, R, pool=True, device=dev)
 
     def step_score_select():
-        # plane in the workspace's pool (scores unused), range rows and their
-        # merge from the same launch
+        # range rows and their merge from the scoring launch (plane in the pool)
         msa.msa_score_select(q, k, bt, sl, None, nvp, part, ws, page_size=w.page_size,
-                             decode_query_len=w.dql, init_blocks=w.init_blocks,
-                             local_blocks=w.local_blocks, num_ranges=R, cols=w.cols,
-                             merged=final if R <= 64 else None, errors=errors, stream=stream)
+                             decode_query_len=w.dql, num_ranges=R, cols=w.cols,
+                             merged=final if R <= 64 else None, **sel)
 
-    score_select_ms = None
+    headline = step_headline if one_launch else step_three
+    headline_name = ("msa_score_decode -> msa_top16_select_merge (per-range rows written, "
+                     "merged in the same launch)" if one_launch else
+                     "msa_score_decode -> msa_top16_select" +
+                     (" -> msa_top16_merge" if R > 1 else ""))
+    forms = {"three_launch_chain": step_three}
+    if one_launch:
+        forms["row_select"] = step_row_select
     if -(-w.cols // R) <= 2048:
-        for _ in range(args.warmup):
-            step_score_select()
-        ss_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                     for _ in range(args.steps)]
-        for i in range(args.steps):
-            if not args.no_flush:
-                flush.sum()
-            ss_events[i][0].record(stream)
-            step_score_select()
-            ss_events[i][1].record(stream)
-        torch.cuda.synchronize()
-        score_select_ms = sum(ev[0].elapsed_time(ev[1]) for ev in ss_events) / args.steps
+        forms["fused_score_select"] = step_score_select
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.sum()
+        headline()
+        for f in forms.values():
+            f()
+    torch.cuda.synchronize()
+
+    # Timed region 1 (the headline): K steps, an event pair around each step
+    # only; the contract's wall clock brackets all K steps, reads included.
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_ms = timed_steps(headline, args.steps, stream, flush)
+    wall = time.perf_counter() - wall0
+
+    # Timed region 1b: the other forms of the step, timed the same way.
+    alt = {}
+    for name, f in forms.items():
+        alt[name] = step_stats(timed_steps(f, args.steps, stream, flush), launch_bytes, keys)
+    alt["three_launch_chain"]["step"] = ("msa_score_decode -> msa_top16_select" +
+                                         (" -> msa_top16_merge" if R > 1 else ""))
+    if "row_select" in alt:
+        alt["row_select"]["step"] = ("msa_score_decode -> msa_top16_select_merge without "
+                                     "per-range rows (whole-row select)")
+    if "fused_score_select" in alt:
+        alt["fused_score_select"]["step"] = ("msa_score_select: plane in the workspace pool, "
+                                             "range rows and their merge in one launch")
 
     # Timed region 1d: one rank's share of the same workload on a cache whose
     # pages are split by rows over world_size ranks (msa_score_decode_sharded
@@ -391,54 +469,44 @@ def main():
                 msa.msa_score_decode_sharded(q, shard, bt, sl, splane, page_size=w.page_size,
                                              decode_query_len=w.dql, rank=0, world_size=ws_n,
                                              errors=errors, stream=stream)
-                msa.msa_top16_select_mapped(splane, nvp, spart, init_blocks=w.init_blocks,
-                                            local_blocks=w.local_blocks, num_ranges=R,
-                                            index_scale=scale, index_offset=offset,
-                                            errors=errors, stream=stream)
+                msa.msa_top16_select_mapped(splane, nvp, spart, num_ranges=R,
+                                            index_scale=scale, index_offset=offset, **sel)
 
             for _ in range(args.warmup):
                 step_rank()
-            ev_r = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                    for _ in range(args.steps)]
-            for i in range(args.steps):
-                if not args.no_flush:
-                    flush.sum()
-                ev_r[i][0].record(stream)
-                step_rank()
-                ev_r[i][1].record(stream)
+            rank_ms = timed_steps(step_rank, args.steps, stream, flush)
             # owner merge of every rank's rows (rank 0's rows stand in for all)
             all_rows = spart.repeat(1, 1, ws_n, 1).contiguous()
             merged = msa.new_rows(T, 4, device=dev)
+
+            def owner_merge():
+                # rank 0's rows repeated stand in for every rank's: the forced
+                # ids other ranks would hold are missing, so no error counter
+                msa.msa_top16_merge_dedup(all_rows, nvp, merged, init_blocks=w.init_blocks,
+                                          local_blocks=w.local_blocks, stream=stream)
+
             for _ in range(args.warmup):
-                msa.msa_top16_merge_dedup(all_rows, nvp, merged, init_blocks=w.init_blocks,
-                                          local_blocks=w.local_blocks, stream=stream)
-            ev_m = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                    for _ in range(args.steps)]
-            for i in range(args.steps):
-                ev_m[i][0].record(stream)
-                msa.msa_top16_merge_dedup(all_rows, nvp, merged, init_blocks=w.init_blocks,
-                                          local_blocks=w.local_blocks, stream=stream)
-                ev_m[i][1].record(stream)
-            torch.cuda.synchronize()
-            rank_ms = sum(e[0].elapsed_time(e[1]) for e in ev_r) / args.steps
-            merge_ms = sum(e[0].elapsed_time(e[1]) for e in ev_m) / args.steps
+                owner_merge()
+            merge_ms = timed_steps(owner_merge, args.steps, stream)
+            rank_mean = sum(rank_ms) / len(rank_ms)
             rank_bytes = rank_keys * 128
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
-                "rank_step_ms": rank_ms,
-                "rank_hbm_gbps": rank_bytes / (rank_ms * 1e-3) / 1e9,
-                "rank_frac_of_peak": rank_bytes / (rank_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                "owner_merge_ms": merge_ms, "merged_rows_per_head": ws_n * R}
+                "rank_step_ms": rank_mean,
+                "rank_hbm_gbps": rank_bytes / (rank_mean * 1e-3) / 1e9,
+                "rank_frac_of_peak": rank_bytes / (rank_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "owner_merge_ms": sum(merge_ms) / len(merge_ms),
+                "merged_rows_per_head": ws_n * R}
             del shard, splane, spart, all_rows, merged
 
-    # Timed region 2: K steps with an event between every kernel,
-    # for per-kernel durations (the events themselves lengthen these steps).
+    # Timed region 2: the three-launch chain with an event between every
+    # kernel, for per-kernel durations (the events lengthen these steps).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps per kernel", file=sys.stderr, flush=True)
     for i in range(args.steps):
-        if not args.no_flush:
+        if flush is not None:
             flush.sum()
-        step(events[i])
+        step_three(events[i])
     torch.cuda.synchronize()
     # Timed region 3: the scorer alone, K launches back to back between one
     # event pair (a cache-evicting read first), for its per-launch duration
@@ -447,34 +515,39 @@ def main():
     # loads, so a launch finds little of the previous one's data resident.
     print(f"[bench] timing {args.steps} back-to-back scorer launches", file=sys.stderr,
           flush=True)
-    if not args.no_flush:
+    if flush is not None:
         flush.sum()
     b2b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     b2b[0].record(stream)
     for _ in range(args.steps):
-        msa.msa_score_decode(q, k, bt, sl, plane, page_size=w.page_size,
-                             decode_query_len=w.dql, errors=errors, stream=stream)
+        score()
     b2b[1].record(stream)
     torch.cuda.synchronize()
     score_b2b_ms = b2b[0].elapsed_time(b2b[1]) / args.steps
     # Timed region 3b: the streaming-read probe (a plain read, no other work)
-    # over as many index-K bytes, timed the same way: the streaming ceiling
-    # the scorer's rate is read against.
-    # as many bytes as the scorer's algorithmic read, in whole 16 KiB blocks
-    # from the start of the cache (pages in storage order)
-    probe_bytes = max(16384, workloads.index_k_bytes(w) // 16384 * 16384)
+    # over as many index-K bytes, timed the same way, and over 4 GiB (where
+    # the launch's ramp and tail weigh least): the streaming ceilings the
+    # scorer's rate is read against.
+    probe_bytes = max(16384, launch_bytes // 16384 * 16384)
     probe_bytes = min(probe_bytes, k.numel() // 16384 * 16384)
     sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
-    msa.msa_stream_read_probe(k, sink, nbytes=probe_bytes, stream=stream)
-    if not args.no_flush:
-        flush.sum()
-    b2b_probe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    b2b_probe[0].record(stream)
-    for _ in range(args.steps):
-        msa.msa_stream_read_probe(k, sink, nbytes=probe_bytes, stream=stream)
-    b2b_probe[1].record(stream)
-    torch.cuda.synchronize()
-    probe_ms = b2b_probe[0].elapsed_time(b2b_probe[1]) / args.steps
+
+    def probe_ms(buf, nbytes, launches):
+        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+        if flush is not None:
+            flush.sum()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(launches):
+            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / launches
+
+    probe_launch_ms = probe_ms(k, probe_bytes, args.steps)
+    big = torch.empty(PROBE_BIG_BYTES, dtype=torch.uint8, device=dev)
+    big_ms = probe_ms(big, PROBE_BIG_BYTES, 10)
+    del big
     if int(errors.item()) != 0:
         raise RuntimeError(f"device error counter = {int(errors.item())}")
     if args.calibrate_copy:
@@ -484,20 +557,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    step_ms = sorted(ev[0].elapsed_time(ev[1]) for ev in step_events)
+    prefill = None
+    if not args.no_prefill:
+        print("[bench] prefill chain", file=sys.stderr, flush=True)
+        prefill = prefill_figure(dev, stream)
+
+    head = step_stats(step_ms, launch_bytes, keys)
     score_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
     select_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
     merge_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
     mean = lambda xs: sum(xs) / len(xs)
-    ms_step = mean(step_ms)
-    keys = w.total_keys
-    launch_bytes = workloads.index_k_bytes(w)
+    ms_step = head["ms_per_step"]
     value = keys / (ms_step * 1e-3)
-    e2e_gbps = launch_bytes / (ms_step * 1e-3) / 1e9
-    score_mean = mean(score_ms)
     achieved = launch_bytes / (score_b2b_ms * 1e-3) / 1e9
     traffic = load_traffic(launch_bytes)  # HBM bytes per launch, from the committed counters
-    probe_gbps = probe_bytes / (probe_ms * 1e-3) / 1e9
+    probe_gbps = probe_bytes / (probe_launch_ms * 1e-3) / 1e9
+    big_gbps = PROBE_BIG_BYTES / (big_ms * 1e-3) / 1e9
 
     out = {
         "metric": "index-K scored keys/s and achieved HBM GB/s (% of peak), score+Top16, 1 GPU",
@@ -516,29 +591,19 @@ def main():
                    "page_size": w.page_size, "decode_query_len": w.dql, "cols": w.cols,
                    "ranges": R, "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
                    "index_k_bytes": launch_bytes, "parallelism": "single-gpu",
-                   "cache_flush_between_steps": not args.no_flush},
-        "e2e": {"step": "msa_score_decode -> msa_top16_select" +
-                        (" -> msa_top16_merge" if R > 1 else ""),
-                "hbm_gbps": e2e_gbps, "frac_of_peak": e2e_gbps / HBM_PEAK_GBPS,
+                   "cache_flush_between_steps": flush is not None},
+        "e2e": {"step": headline_name,
+                **{kk: vv for kk, vv in head.items() if kk != "keys_per_s"},
+                "target_frac_of_peak": 0.70,
                 # each key is scored against its request's 4 * dql query rows
                 "dot_products_per_s": value * 4 * w.dql,
-                "step_ms_p10": step_ms[len(step_ms) // 10],
-                "step_ms_p50": step_ms[len(step_ms) // 2],
-                "step_ms_p90": step_ms[(len(step_ms) * 9) // 10],
-                "kernels_ms": {"score_decode": score_mean, "top16_select": mean(select_ms),
-                               "top16_merge": mean(merge_ms)},
+                "kernels_ms_three_launch_chain": {
+                    "score_decode": mean(score_ms), "top16_select": mean(select_ms),
+                    "top16_merge": mean(merge_ms),
+                    "step_with_kernel_events": mean([ev[0].elapsed_time(ev[3])
+                                                     for ev in events])},
                 "score_decode_ms_back_to_back": score_b2b_ms,
-                "step_ms_with_kernel_events": mean([ev[0].elapsed_time(ev[3]) for ev in events]),
-                "one_launch_select_merge": None if fused_ms is None else {
-                    "ms_per_step": fused_ms, "keys_per_s": keys / (fused_ms * 1e-3),
-                    "hbm_gbps": launch_bytes / (fused_ms * 1e-3) / 1e9,
-                    "frac_of_peak": launch_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-                "score_select_then_merge": None if score_select_ms is None else {
-                    "ms_per_step": score_select_ms,
-                    "keys_per_s": keys / (score_select_ms * 1e-3),
-                    "hbm_gbps": launch_bytes / (score_select_ms * 1e-3) / 1e9,
-                    "frac_of_peak":
-                        launch_bytes / (score_select_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "other_forms": alt,
                 "sharded_rank_share": sharded or None,
                 "wall_s_all_steps_incl_flush": wall},
         "roofline": {"kernel": "score_decode", "bound": "hbm", "achieved": achieved,
@@ -550,11 +615,17 @@ def main():
                      "traffic_detail": traffic,
                      "mfma": load_mfma(),
                      "stream_read_probe": {
-                         "what": "msa_stream_read_probe over as many index-K bytes, pages "
-                                 "in storage order: a plain streaming read with no other work",
-                         "launch_ms": probe_ms, "achieved": probe_gbps,
-                         "frac_of_peak": probe_gbps / HBM_PEAK_GBPS,
-                         "scorer_frac_of_probe": achieved / probe_gbps}},
+                         "what": "msa_stream_read_probe, a plain streaming read with no other "
+                                 "work, launches back to back between one event pair",
+                         "same_bytes": {"bytes": probe_bytes, "launch_ms": probe_launch_ms,
+                                        "achieved": probe_gbps,
+                                        "frac_of_peak": probe_gbps / HBM_PEAK_GBPS},
+                         "4_gib": {"bytes": PROBE_BIG_BYTES, "launch_ms": big_ms,
+                                   "achieved": big_gbps,
+                                   "frac_of_peak": big_gbps / HBM_PEAK_GBPS},
+                         "scorer_frac_of_probe_same_bytes": achieved / probe_gbps,
+                         "scorer_frac_of_probe_4_gib": achieved / big_gbps}},
+        "prefill": prefill,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

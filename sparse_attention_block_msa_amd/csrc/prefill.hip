@@ -20,17 +20,19 @@
 //    listed by (request, window, column range) in a caller-owned plan:
 //    a header (item count, and the batch, token count and plane width the
 //    plan was made for) followed by 8-word items.
-//  * Chunk scorer, one 4-wave workgroup per item. The window's 256 query rows
-//    (64 tokens x 4 heads, contiguous in index_q) are split 64 per wave and
+//  * Chunk scorer, one 2-wave workgroup per item. The window's 256 query rows
+//    (64 tokens x 4 heads, contiguous in index_q) are split 128 per wave and
 //    converted once to bf16 MFMA B operands held in registers. For every
-//    column of the item the four waves stage the block's 16 KiB of keys in
-//    LDS (global_load_lds, 32 rows per wave, XOR-swizzled as in the decode
-//    scorer), then each wave contracts them with its 64 rows (8 key tiles x
-//    4 query tiles x 4 chained v_mfma_f32_16x16x32_bf16), masks keys past a
-//    token's position in the blocks that reach past the wave's first token,
-//    takes the block max and stores its 64 rows' values. A key meets up to
-//    256 query rows here, 2*128*256 flops per 128-byte key: the kernel is
-//    MFMA-bound, and several workgroups per CU hide each other's DMA waits.
+//    column of the item the two waves stage the block's 16 KiB of keys in
+//    LDS (global_load_lds, 64 rows per wave, XOR-swizzled as in the decode
+//    scorer; the next column's DMA is in flight while a column is
+//    contracted), then each wave contracts them with its 128 rows (8 key
+//    tiles x 8 query tiles x 4 chained v_mfma_f32_16x16x32_bf16), masks keys
+//    past a token's position in the blocks that reach past the wave's first
+//    token and takes the block max. The maxima wait in LDS and go out as
+//    32-byte runs per row every 8 columns. A key meets up to 256 query rows
+//    here, 2*128*256 flops per 128-byte key: the kernel is MFMA-bound, and
+//    several workgroups per CU hide each other's DMA waits.
 //    Keys are loaded with the default cache policy, since every window of a
 //    request re-reads the same blocks.
 //  * Workgroups take items in an XCD-aware order (workgroup i runs on XCD
@@ -193,6 +195,10 @@ constexpr int kWaveRows = 16 * kWaveTiles;
 constexpr int kWaves = kWindow * kHeads / kWaveRows;
 constexpr int kWaveKeyRows = kBlockTokens / kWaves;  // key rows each wave stages per block
 static_assert(kWaves * kWaveRows == kWindow * kHeads && kWaveKeyRows % 8 == 0, "bad shape");
+// Plane columns a lane holds before storing them (a 32-byte run per row).
+constexpr int kStoreCols = 8;
+static_assert(kItemCols % kStoreCols == 0 && kStoreCols % 4 == 0, "runs must stay aligned");
+static_assert(kWaveTiles == 8, "a lane stores two rows, wave rows lane and lane + 64");
 
 // One column of one item for one wave: the block in `tile` against the
 // wave's kWaveRows query rows. On return mx[n] holds, in every lane, the
@@ -278,6 +284,10 @@ __attribute__((amdgpu_waves_per_eu(MSA_PREFILL_WAVES_PER_EU)))
 void prefill_score_kernel(PrefillScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kBlockTokens * kDim];
+    // each lane's block maxima of kStoreCols columns for its two rows, laid
+    // out [column][row slot][thread] so that a lane's accesses never share a
+    // bank with another lane's
+    __shared__ float held[kStoreCols][2][kWaves * 64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -389,9 +399,31 @@ void prefill_score_kernel(PrefillScoreParams p)
 #pragma unroll
             for (int n = 0; n < kWaveTiles; n += 4) {
                 const float v = g == 0 ? mx[n] : g == 1 ? mx[n + 1] : g == 2 ? mx[n + 2] : mx[n + 3];
-                // wave row 16n + lane: token offset (16n + lane) / 4
-                if (4 * n + (lane >> 2) < wave_tokens)
-                    out_rows[(int64_t)16 * n * p.cols + c] = v;
+                held[i % kStoreCols][n / 4][tid] = v;
+            }
+            // Every kStoreCols columns (and after the item's last), each
+            // lane stores its rows' held run of columns: plane stores share
+            // the vector-memory counter with the key DMA, so fewer, wider
+            // stores stall the next column's wait less, and whole 16-byte
+            // runs leave no partly written lines behind.
+            if (i % kStoreCols == kStoreCols - 1 || i == ncols - 1) {
+                const int i0 = i - i % kStoreCols;  // col0 + i0 is a multiple of kStoreCols
+                const int nb = i - i0 + 1;
+#pragma unroll
+                for (int n = 0; n < kWaveTiles; n += 4) {
+                    // wave row 16n + lane: token offset (16n + lane) / 4
+                    if (4 * n + (lane >> 2) >= wave_tokens)
+                        continue;
+                    float* dst = out_rows + (int64_t)16 * n * p.cols + col0 + i0;
+                    int j = 0;
+                    for (; j + 4 <= nb; j += 4) {
+                        const v4f v = {held[j][n / 4][tid], held[j + 1][n / 4][tid],
+                                       held[j + 2][n / 4][tid], held[j + 3][n / 4][tid]};
+                        *reinterpret_cast<v4f*>(dst + j) = v;
+                    }
+                    for (; j < nb; ++j)
+                        dst[j] = held[j][n / 4][tid];
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);  // this wave's reads of `cur` returned

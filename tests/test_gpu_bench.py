@@ -26,9 +26,10 @@ FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
 @pytest.mark.parametrize("config", [1, 2])
 def test_bench_small_workloads(config):
     print(f"[test] bench.py --config {config}", flush=True)
+    extra = [] if config == 1 else ["--no-prefill"]
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config",
-                          str(config), "--steps", "3", "--warmup", "1", "--no-cpu-baseline"],
-                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+                          str(config), "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+                          *extra], capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-3000:]
     lines = [l for l in res.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1, res.stdout[-2000:]
@@ -38,5 +39,12 @@ def test_bench_small_workloads(config):
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["value"] > 0
     r = d["roofline"]
     assert r["bound"] == "hbm" and 0 < r["frac"] < 1.5
-    assert r["stream_read_probe"]["launch_ms"] > 0
-    assert d["e2e"]["frac_of_peak"] > 0
+    probe = r["stream_read_probe"]
+    assert probe["same_bytes"]["launch_ms"] > 0 and probe["4_gib"]["achieved"] > 0
+    e2e = d["e2e"]
+    assert e2e["frac_of_peak"] > 0 and e2e["step_ms_p50"] <= e2e["step_ms_p90"]
+    assert "three_launch_chain" in e2e["other_forms"]
+    if config == 1:
+        assert d["prefill"]["achieved_tflops"] > 0
+    else:
+        assert d["prefill"] is None
