@@ -35,11 +35,11 @@
 //    per instruction) and contracted with v_mfma_f32_16x16x32_bf16, four
 //    instructions chained through the fp32 accumulator per 128-dim dot
 //    product. The fp8 MFMA forms (16x16x128 f8f6f4, 16x16x32 fp8) were
-//    measured on gfx950 to sum groups of fp8 products with up to about
-//    2e-5 of sum|q_i k_i| error on N(0,1) data and 2.4e-4 on full-range
-//    codes, above the 1e-5 bound this kernel guarantees; the bf16 form
-//    measured at most 3e-7. The path is HBM-bound either way (8*dql flop per
-//    index-K byte), so the bf16 rate costs no throughput.
+//    measured on gfx950 (msa_contraction_probe) to sum groups of fp8
+//    products with up to about 2e-5 of sum|q_i k_i| error on N(0,1) data and
+//    2e-4 on full-range codes, above the 1e-5 bound this kernel guarantees;
+//    the bf16 form measured at most 3e-7. The path is HBM-bound either way
+//    (8*dql flop per index-K byte), so the bf16 rate costs no throughput.
 //  * Lane l of a 16x16 result holds keys 4*(l/16)..+3 of the tile for query
 //    row l%16, so the block max is a per-lane max over 8 tiles x 4 values
 //    followed by a max across the four 16-lane groups. The causal mask is

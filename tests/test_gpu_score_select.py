@@ -11,7 +11,8 @@ checks each time that
 * the workspace (the pool excepted) holds zeros again after the launch.
 The five workloads are also checked against the oracle: the rows equal the
 oracle's select on the GPU's plane bit for bit, and, after the merge, the
-oracle's chain on its own plane except near-ties within the tolerance band.
+oracle's chain on its own plane by the admissibility rule of tests/parity.py
+(the rows must be the exact selection of some plane within tolerance).
 Edge cases: every decode_query_len at both page sizes with empty and short
 requests, range boundaries inside 4-column groups, one column per range,
 batches above 64, num_valid_pages past the written columns or outside
@@ -237,3 +238,53 @@ def test_score_select_bad_block_table_and_narrow_plane():
     # token's num_valid_pages (24) exceeds cols (select); the merge then misses
     # that token's forced ids past the plane in its four heads
     assert err == 4 + 4
+
+
+# ---------------------------------------------------------------------------
+# other work on the device at the same time
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_score_select_beside_other_work(n):
+    """The fused launch waits only in its helper waves (at most half of what
+    the device holds), so its result does not depend on getting the whole
+    device: here a second stream (default priority) keeps a long run of
+    elementwise kernels in flight while the fused launch runs, and the rows,
+    merged rows and error count must still equal the two-call path's, with
+    the workspace zero afterwards."""
+    w = workloads.config(n)
+    T, R = w.num_tokens, w.num_ranges
+    say(f"[test] score_select beside other work, config {n}")
+    q, k, sl = w.index_q.to(DEV), w.index_k.to(DEV), w.seq_lens.to(DEV)
+    bt, nvp = w.block_table.to(DEV), w.num_valid_pages.to(DEV)
+    kw = dict(page_size=w.page_size, decode_query_len=w.dql)
+    sel = dict(init_blocks=w.init_blocks, local_blocks=w.local_blocks)
+
+    plane = torch.empty((T, 4, w.cols), dtype=torch.float32, device=DEV)
+    ref_rows = msa.new_rows(T, 4, R, device=DEV)
+    ref_merged = msa.new_rows(T, 4, device=DEV)
+    ref_err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    msa.msa_score_decode(q, k, bt, sl, plane, errors=ref_err, **kw)
+    msa.msa_top16_select(plane, nvp, ref_rows, num_ranges=R, errors=ref_err, **sel)
+    msa.msa_top16_merge(ref_rows, nvp, ref_merged, errors=ref_err if R > 1 else None, **sel)
+    torch.cuda.synchronize()
+
+    busy = torch.ones(1 << 28, dtype=torch.float32, device=DEV)  # 1 GiB
+    other = torch.cuda.Stream(device=DEV)
+    ws = msa.score_select_workspace(w.batch, w.dql, w.cols, R, pool=True, device=DEV)
+    head = msa.msa_score_select_workspace_words(w.batch, w.dql, w.cols, R, pool=False)
+    main = torch.cuda.current_stream()
+    for rep in range(3):
+        rows = msa.new_rows(T, 4, R, device=DEV)
+        merged = msa.new_rows(T, 4, device=DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        with torch.cuda.stream(other):
+            for _ in range(8):
+                busy.mul_(1.0)
+        msa.msa_score_select(q, k, bt, sl, None, nvp, rows, ws, cols=w.cols, merged=merged,
+                             num_ranges=R, errors=err, stream=main, **kw, **sel)
+        torch.cuda.synchronize()
+        assert torch.equal(rows.cpu(), ref_rows.cpu()), f"rep {rep}: range rows differ"
+        assert torch.equal(merged.cpu(), ref_merged.cpu()), f"rep {rep}: merged rows differ"
+        assert int(err.item()) == int(ref_err.item()) == 0
+        assert int(ws[:head].count_nonzero()) == 0, f"rep {rep}: workspace left non-zero"
