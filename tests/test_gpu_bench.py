@@ -42,7 +42,9 @@ def test_bench_small_workloads(config):
     probe = r["stream_read_probe"]
     assert probe["same_bytes"]["launch_ms"] > 0 and probe["4_gib"]["achieved"] > 0
     e2e = d["e2e"]
-    assert e2e["frac_of_peak"] > 0 and e2e["step_ms_p50"] <= e2e["step_ms_p90"]
+    pairs = e2e["per_step_event_pairs"]
+    assert e2e["frac_of_peak"] > 0 and pairs["step_ms_p50"] <= pairs["step_ms_p90"]
+    assert e2e["timing"]
     assert "three_launch_chain" in e2e["other_forms"]
     if config == 1:
         assert d["prefill"]["achieved_tflops"] > 0
