@@ -10,7 +10,8 @@ select -> merge) against the CPU oracle, through the C ABI.
   tests/parity.py;
 * shapes: a short ragged chunk (1, 17 and 64 tokens), chunks crossing block
   and page boundaries at page_size 256 (with outlier blocks), empty chunks
-  and an empty request, a ragged batch of six, and a long window of 8192
+  and an empty request, a ragged batch of six, 300 small requests (more than
+  the plan kernel's threads), and a long window of 8192
   tokens at the end of a 65536-key request (sampled rows against the oracle,
   every row against the -inf pattern the causal rule fixes);
 * errors: a plan made for another plane runs nothing; bad block-table
@@ -54,6 +55,9 @@ CASES = {
                          ranges=1, seed=3103, cols=12),
     "ragged_b6": dict(batch=6, seq=("uniform", 2000, 20000), q_lens=("uniform", 1, 700),
                       page_size=128, dql=1, init=2, local=2, ranges=4, seed=3104),
+    # more requests than the plan kernel has threads: its scan runs in passes
+    "many_requests_b300": dict(batch=300, seq=("uniform", 1, 700), q_lens=("uniform", 0, 24),
+                               page_size=128, dql=1, init=1, local=2, ranges=2, seed=3106),
 }
 
 LONG = dict(batch=1, seq=("fixed", 65536), q_lens=("fixed", 8192), page_size=256, dql=1, init=4,
