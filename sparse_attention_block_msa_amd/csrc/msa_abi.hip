@@ -214,8 +214,9 @@ hipError_t launch_clear_words(int32_t* p, int64_t n, hipStream_t stream)
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
-    return hipGetLastError();
+    void* args[] = {&p, &n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&clear_words_kernel),
+                           dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
 // Workspace words of msa_score_select for these sizes, or MSA_ERR_INVALID_ARG
