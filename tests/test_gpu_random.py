@@ -10,8 +10,9 @@ request), page size, decode_query_len, number of column ranges (up to 16, or
   oracle's select and merge on the GPU's own plane;
 * msa_top16_select_merge (where the one-launch form applies): bit for bit the
   two-launch rows, with and without the range rows;
-* msa_score_select then msa_top16_merge: bit for bit the plane and rows of
-  the separate launches;
+* msa_score_select with its merge: bit for bit the plane and rows of the
+  separate launches, then the same without a plane (pool in the workspace) and
+  as msa_score_select_noalloc (where the sizes fit its scratch array);
 * the row-sharded chain over world size 2 or 4 (every rank's
   msa_score_decode_sharded and msa_top16_select_mapped, then
   msa_top16_merge_dedup of all ranks' rows): bit for bit the merged rows.
@@ -150,6 +151,29 @@ def test_random_chain(seed):
         assert torch.equal(part2, part)
         assert torch.equal(final2, final)
         assert int(counters.count_nonzero()) == 0
+
+        # the same launch without a plane (scores in the workspace's pool), and
+        # its variant on the library's own scratch array: the same rows
+        pool_ws = msa.score_select_workspace(w.batch, w.dql, cols, R, pool=True, device=DEV)
+        head = msa.msa_score_select_workspace_words(w.batch, w.dql, cols, R, pool=False)
+        fits = (msa.msa_score_select_workspace_words(w.batch, w.dql, cols, R, pool=True)
+                <= msa.NOALLOC_SCRATCH_WORDS)
+        for noalloc in ((False, True) if fits else (False,)):
+            part3 = msa.new_rows(T, 4, R, device=DEV)
+            part3.fill_(ROW_FILL)
+            final3 = msa.new_rows(T, 4, device=DEV)
+            final3.fill_(ROW_FILL)
+            common = dict(page_size=w.page_size, decode_query_len=w.dql, num_ranges=R, cols=cols,
+                          merged=final3, errors=err, **kw)
+            if noalloc:
+                msa.msa_score_select_noalloc(q, k, bt, sl, None, nvp, part3, **common)
+            else:
+                msa.msa_score_select(q, k, bt, sl, None, nvp, part3, pool_ws, **common)
+            torch.cuda.synchronize()
+            assert int(err.item()) == 0
+            assert torch.equal(part3, part), f"noalloc={noalloc}: range rows differ"
+            assert torch.equal(final3, final), f"noalloc={noalloc}: merged rows differ"
+        assert int(pool_ws[:head].count_nonzero()) == 0
 
     # the row-sharded chain: every rank's share, then the owner's merge
     pages = -(-int(w.seq_lens.max()) // w.page_size)
