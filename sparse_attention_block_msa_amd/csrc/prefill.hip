@@ -198,7 +198,9 @@ static_assert(kWaves * kWaveRows == kWindow * kHeads && kWaveKeyRows % 8 == 0, "
 // Plane columns a lane holds before storing them (a 32-byte run per row).
 constexpr int kStoreCols = 8;
 static_assert(kItemCols % kStoreCols == 0 && kStoreCols % 4 == 0, "runs must stay aligned");
-static_assert(kWaveTiles == 8, "a lane stores two rows, wave rows lane and lane + 64");
+// a lane stores kWaveTiles / 4 rows: wave rows lane, lane + 64, ...
+static_assert(kWaveTiles % 4 == 0, "whole 16-lane groups per row slot");
+constexpr int kLaneRows = kWaveTiles / 4;
 
 // One column of one item for one wave: the block in `tile` against the
 // wave's kWaveRows query rows. On return mx[n] holds, in every lane, the
@@ -284,10 +286,10 @@ __attribute__((amdgpu_waves_per_eu(MSA_PREFILL_WAVES_PER_EU)))
 void prefill_score_kernel(PrefillScoreParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kBlockTokens * kDim];
-    // each lane's block maxima of kStoreCols columns for its two rows, laid
+    // each lane's block maxima of kStoreCols columns for its rows, laid
     // out [column][row slot][thread] so that a lane's accesses never share a
     // bank with another lane's
-    __shared__ float held[kStoreCols][2][kWaves * 64];
+    __shared__ float held[kStoreCols][kLaneRows][kWaves * 64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
