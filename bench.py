@@ -490,6 +490,22 @@ def main():
         alt["fused_score_select"]["step"] = ("msa_score_select: plane in the workspace pool, "
                                              "range rows and their merge in one launch")
 
+    sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+
+    def probe_ms(buf, nbytes, launches):
+        """msa_stream_read_probe over nbytes of buf: K launches back to back
+        between one event pair, after a cache-evicting read."""
+        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+        if flush is not None:
+            flush.sum()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(launches):
+            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / launches
+
     # Timed region 1d: one rank's share of the same workload on a cache whose
     # pages are split by rows over world_size ranks (msa_score_decode_sharded
     # -> msa_top16_select_mapped over R ranges), and the owner's merge of all
@@ -534,11 +550,31 @@ def main():
             merge_ms = timed_steps(owner_merge, args.steps, stream)
             rank_mean = sum(rank_ms) / len(rank_ms)
             rank_bytes = rank_keys * 128
+            # the rank's scorer alone, back to back, against a plain read of
+            # as many bytes (the ceiling at this size, ramp and tail included)
+            if flush is not None:
+                flush.sum()
+            ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev_s[0].record(stream)
+            for _ in range(args.steps):
+                msa.msa_score_decode_sharded(q, shard, bt, sl, splane, page_size=w.page_size,
+                                             decode_query_len=w.dql, rank=0, world_size=ws_n,
+                                             errors=errors, stream=stream)
+            ev_s[1].record(stream)
+            torch.cuda.synchronize()
+            rank_score_ms = ev_s[0].elapsed_time(ev_s[1]) / args.steps
+            rank_probe_bytes = min(rank_bytes, shard.numel()) // 16384 * 16384
+            rank_probe_ms = probe_ms(shard, rank_probe_bytes, args.steps)
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
                 "rank_step_ms": rank_mean,
                 "rank_hbm_gbps": rank_bytes / (rank_mean * 1e-3) / 1e9,
                 "rank_frac_of_peak": rank_bytes / (rank_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "rank_scorer_ms_back_to_back": rank_score_ms,
+                "rank_scorer_hbm_gbps": rank_bytes / (rank_score_ms * 1e-3) / 1e9,
+                "stream_read_probe_same_bytes_ms": rank_probe_ms,
+                "rank_scorer_frac_of_probe":
+                    (rank_bytes / rank_score_ms) / (rank_probe_bytes / rank_probe_ms),
                 "owner_merge_ms": sum(merge_ms) / len(merge_ms),
                 "merged_rows_per_head": ws_n * R}
             del shard, splane, spart, all_rows, merged
@@ -574,20 +610,6 @@ def main():
     # scorer's rate is read against.
     probe_bytes = max(16384, launch_bytes // 16384 * 16384)
     probe_bytes = min(probe_bytes, k.numel() // 16384 * 16384)
-    sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
-
-    def probe_ms(buf, nbytes, launches):
-        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
-        if flush is not None:
-            flush.sum()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(launches):
-            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / launches
-
     probe_launch_ms = probe_ms(k, probe_bytes, args.steps)
     big = torch.empty(PROBE_BIG_BYTES, dtype=torch.uint8, device=dev)
     big_ms = probe_ms(big, PROBE_BIG_BYTES, 10)
