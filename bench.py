@@ -47,8 +47,8 @@ HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
 counters (committed under profiles/, valid while the scorer's source hash
 matches). `roofline.stream_read_probe` times msa_stream_read_probe, a plain
 streaming read with no other work, over as many index-K bytes and over
-4 GiB, in the same way: the streaming ceilings the scorer's rate is read
-against. `cpu_baseline` times the oracle on the same workload.
+4 GiB, in the same way and at each of its shapes: the fastest shape at each
+size is the streaming ceiling the scorer's rate is read against. `cpu_baseline` times the oracle on the same workload.
 """
 from __future__ import annotations
 
@@ -67,6 +67,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30           # read before each step; > 256 MB Infinity Cache
 COPY_BYTES = 512 << 20          # calibration copy: reads and writes this many bytes
 PROBE_BIG_BYTES = 4 << 30       # the long streaming-read probe
+PROBE_SHAPES = (2, 4, 8, 16)    # the probe's blocks per wave; the ceiling is the best
 ROTATE_MIN_BYTES = 768 << 20    # other index-K bytes read between two uses of one copy
 MAX_COPIES = 4                  # index-K copies the headline rotates over, at most
 ROTATE_WARMUP_STEPS = 100       # untimed back-to-back steps before the headline's K
@@ -492,19 +493,26 @@ def main():
 
     sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
 
-    def probe_ms(buf, nbytes, launches):
-        """msa_stream_read_probe over nbytes of buf: K launches back to back
-        between one event pair, after a cache-evicting read."""
-        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+    def probe_shape_ms(buf, nbytes, launches, bpw):
+        """msa_stream_read_probe over nbytes of buf, bpw blocks per wave: K
+        launches back to back between one event pair, after a cache-evicting
+        read."""
+        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, blocks_per_wave=bpw, stream=stream)
         if flush is not None:
             flush.sum()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for _ in range(launches):
-            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, stream=stream)
+            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, blocks_per_wave=bpw,
+                                      stream=stream)
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / launches
+
+    def probe_ms(buf, nbytes, launches):
+        """The fastest probe shape's launch time, and every shape's."""
+        shapes = {bpw: probe_shape_ms(buf, nbytes, launches, bpw) for bpw in PROBE_SHAPES}
+        return min(shapes.values()), shapes
 
     # Timed region 1d: one rank's share of the same workload on a cache whose
     # pages are split by rows over world_size ranks (msa_score_decode_sharded
@@ -564,7 +572,7 @@ def main():
             torch.cuda.synchronize()
             rank_score_ms = ev_s[0].elapsed_time(ev_s[1]) / args.steps
             rank_probe_bytes = min(rank_bytes, shard.numel()) // 16384 * 16384
-            rank_probe_ms = probe_ms(shard, rank_probe_bytes, args.steps)
+            rank_probe_ms, _ = probe_ms(shard, rank_probe_bytes, args.steps)
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
                 "rank_step_ms": rank_mean,
@@ -610,9 +618,9 @@ def main():
     # scorer's rate is read against.
     probe_bytes = max(16384, launch_bytes // 16384 * 16384)
     probe_bytes = min(probe_bytes, k.numel() // 16384 * 16384)
-    probe_launch_ms = probe_ms(k, probe_bytes, args.steps)
+    probe_launch_ms, probe_shapes = probe_ms(k, probe_bytes, args.steps)
     big = torch.empty(PROBE_BIG_BYTES, dtype=torch.uint8, device=dev)
-    big_ms = probe_ms(big, PROBE_BIG_BYTES, 10)
+    big_ms, big_shapes = probe_ms(big, PROBE_BIG_BYTES, 10)
     del big
     if int(errors.item()) != 0:
         raise RuntimeError(f"device error counter = {int(errors.item())}")
@@ -688,13 +696,16 @@ def main():
                      "mfma": load_mfma(),
                      "stream_read_probe": {
                          "what": "msa_stream_read_probe, a plain streaming read with no other "
-                                 "work, launches back to back between one event pair",
+                                 "work, launches back to back between one event pair; the "
+                                 "fastest of its shapes (16 KiB blocks per wave) at each size",
                          "same_bytes": {"bytes": probe_bytes, "launch_ms": probe_launch_ms,
                                         "achieved": probe_gbps,
-                                        "frac_of_peak": probe_gbps / HBM_PEAK_GBPS},
+                                        "frac_of_peak": probe_gbps / HBM_PEAK_GBPS,
+                                        "launch_ms_by_blocks_per_wave": probe_shapes},
                          "4_gib": {"bytes": PROBE_BIG_BYTES, "launch_ms": big_ms,
                                    "achieved": big_gbps,
-                                   "frac_of_peak": big_gbps / HBM_PEAK_GBPS},
+                                   "frac_of_peak": big_gbps / HBM_PEAK_GBPS,
+                                   "launch_ms_by_blocks_per_wave": big_shapes},
                          "scorer_frac_of_probe_same_bytes": achieved / probe_gbps,
                          "scorer_frac_of_probe_4_gib": achieved / big_gbps}},
         "prefill": prefill,

@@ -457,20 +457,25 @@ int msa_warmup(void);
 /*
  * Measurement aid, not a step of the indexer: no page defines it. It reads
  * `bytes` of device memory at `src` once, with no other work (non-temporal
- * 16-byte loads, a whole 16 KiB block in flight per wave, the fastest plain
- * read shape measured on the device), so its rate is the streaming ceiling
- * that msa_score_decode's rate can be read against. Benchmarks time it
- * beside the scorer over as many index-K bytes.
+ * 16-byte loads, a whole 16 KiB block in flight per wave), so its rate is the
+ * streaming ceiling that msa_score_decode's rate can be read against.
+ * Benchmarks time it beside the scorer over as many index-K bytes, and over
+ * a buffer large enough that a launch's ramp and tail weigh little.
  *
- * src   device, 16-byte aligned; bytes a positive multiple of 16384.
- * sink  device uint32[MSA_STREAM_PROBE_SINK_WORDS]. The probe xors every
- *       dword of the buffer into these words (each wave's share into one of
- *       them), so a caller that zeroes them first can check that the xor of
- *       all words is the xor of the buffer, i.e. that every byte was read.
+ * src              device, 16-byte aligned; bytes a positive multiple of 16384.
+ * blocks_per_wave  2, 4, 8 or 16: consecutive 16 KiB blocks each wave reads.
+ *                  The fastest shape depends on the size (measured: 2 on
+ *                  512 MiB, 16 on 4 GiB), so a ceiling is the best of them.
+ * sink             device uint32[MSA_STREAM_PROBE_SINK_WORDS]. The probe xors
+ *                  every dword of the buffer into these words (each wave's
+ *                  share into one of them), so a caller that zeroes them
+ *                  first can check that the xor of all words is the xor of
+ *                  the buffer, i.e. that every byte was read.
  * Returns MSA_OK, MSA_ERR_INVALID_ARG (null pointer, misaligned src, bad
- * size; nothing launched) or MSA_ERR_LAUNCH.
+ * size or blocks_per_wave; nothing launched) or MSA_ERR_LAUNCH.
  */
-int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int msa_stream_read_probe(const void* src, int64_t bytes, int32_t blocks_per_wave,
+                          uint32_t* sink, hipStream_t stream);
 
 /*
  * Measurement aid, not a step of the indexer: no page defines it. The pages

@@ -104,7 +104,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_score_columns.restype = i32
     lib.msa_warmup.argtypes = []
     lib.msa_warmup.restype = ctypes.c_int
-    lib.msa_stream_read_probe.argtypes = [P, i64, P, P]
+    lib.msa_stream_read_probe.argtypes = [P, i64, i32, P, P]
     lib.msa_stream_read_probe.restype = ctypes.c_int
     lib.msa_prefill_plan_words.argtypes = [i64, i32, i32]
     lib.msa_prefill_plan_words.restype = i64
@@ -191,11 +191,12 @@ def msa_warmup() -> None:
 
 
 def msa_stream_read_probe(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int | None = None,
-                          stream=None) -> None:
+                          blocks_per_wave: int = 2, stream=None) -> None:
     """Measurement aid: a plain streaming read of the first `nbytes` (default
-    all) of the contiguous device tensor `src`, xoring every dword into the
-    words of `sink` (int32 [>= 1024] on the device; the xor of its words is
-    the xor of the bytes read)."""
+    all) of the contiguous device tensor `src`, `blocks_per_wave` (2, 4, 8 or
+    16) consecutive 16 KiB blocks per wave, xoring every dword into the words
+    of `sink` (int32 [>= 1024] on the device; the xor of its words is the xor
+    of the bytes read)."""
     _dev(src, sink)
     _need(src.is_contiguous(), "src: contiguous")
     total = src.numel() * src.element_size()
@@ -203,8 +204,8 @@ def msa_stream_read_probe(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int 
     _need(0 < nbytes <= total, f"nbytes must be in (0, {total}]")
     _need(sink.dtype == torch.int32 and sink.numel() >= STREAM_PROBE_SINK_WORDS and
           sink.is_contiguous(), f"sink: contiguous int32 [>= {STREAM_PROBE_SINK_WORDS}]")
-    _check(load().msa_stream_read_probe(src.data_ptr(), nbytes, sink.data_ptr(),
-                                        _stream_handle(stream)))
+    _check(load().msa_stream_read_probe(src.data_ptr(), nbytes, int(blocks_per_wave),
+                                        sink.data_ptr(), _stream_handle(stream)))
 
 
 def msa_contraction_probe(q: torch.Tensor, k: torch.Tensor, out: torch.Tensor, *, form: int,

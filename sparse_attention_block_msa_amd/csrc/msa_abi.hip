@@ -519,7 +519,8 @@ int msa_top16_select_merge(const float* scores, int32_t num_tokens, int32_t cols
     return launch_result(msa::launch_top16_select_merge(p, stream), fn);
 }
 
-int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream)
+int msa_stream_read_probe(const void* src, int64_t bytes, int32_t blocks_per_wave,
+                          uint32_t* sink, hipStream_t stream)
 {
     static const char* fn = "msa_stream_read_probe";
     g_last_error[0] = '\0';
@@ -528,9 +529,12 @@ int msa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStr
     MSA_CHECK(bytes > 0 && bytes % msa::kProbeBlockBytes == 0,
               "%s: bytes (%lld) must be a positive multiple of %lld", fn, (long long)bytes,
               (long long)msa::kProbeBlockBytes);
+    MSA_CHECK(blocks_per_wave == 2 || blocks_per_wave == 4 || blocks_per_wave == 8 ||
+                  blocks_per_wave == 16,
+              "%s: blocks_per_wave (%d) must be 2, 4, 8 or 16", fn, (int)blocks_per_wave);
     return launch_result(msa::launch_stream_read_probe(static_cast<const uint8_t*>(src),
-                                                       bytes / msa::kProbeBlockBytes, sink,
-                                                       stream),
+                                                       bytes / msa::kProbeBlockBytes,
+                                                       blocks_per_wave, sink, stream),
                          fn);
 }
 

@@ -13,10 +13,12 @@ namespace msa {
 constexpr int64_t kProbeBlockBytes = 16384;  // one B128 block of index-K rows
 constexpr int kProbeSinkWords = MSA_STREAM_PROBE_SINK_WORDS;
 
-// Reads `blocks` contiguous 16 KiB blocks of src and xors every dword of
-// them into sink[0 .. kProbeSinkWords): wave w's share goes to word
-// w % kProbeSinkWords, so that no single word takes every wave's atomic.
-hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, uint32_t* sink,
-                                    hipStream_t stream);
+// Reads `blocks` contiguous 16 KiB blocks of src, blocks_per_wave (2, 4, 8
+// or 16; anything else: hipErrorInvalidValue) consecutive ones per wave, and
+// xors every dword of them into sink[0 .. kProbeSinkWords): wave w's share
+// goes to word w % kProbeSinkWords, so that no single word takes every
+// wave's atomic.
+hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, int blocks_per_wave,
+                                    uint32_t* sink, hipStream_t stream);
 
 }  // namespace msa

@@ -1,18 +1,19 @@
 // Streaming-read probe: how fast this device streams a buffer that is read
 // once, with no other work.
 //
-// Each 64-lane wave reads two 16 KiB blocks. Per block, every lane issues
-// sixteen non-temporal 16-byte loads (1 KiB per instruction across the wave),
-// so a wave holds a whole block in flight, and folds the loaded dwords into a
-// running xor. Workgroups hold four waves and the grid covers the buffer at
-// once, so the hardware keeps as many waves resident as fit. Of the plain
-// read shapes measured on MI355X with an event pair around each launch after
-// a cache eviction (registers or LDS DMA, persistent or not, one or four
-// waves per workgroup, 2 to 32 blocks per wave), this one streamed fastest:
-// 80-82 us for 512 MiB. A wave xors its lanes' values together and adds the
-// result to one of the sink's words with one atomic xor (spread over the
-// words: one word taking all 16 384 atomics of a 512 MiB read made the
-// launch take 208 us instead of 85 us).
+// Each 64-lane wave reads kBlocks consecutive 16 KiB blocks (2, 4, 8 or 16).
+// Per block, every lane issues sixteen non-temporal 16-byte loads (1 KiB per
+// instruction across the wave), so a wave holds a whole block in flight, and
+// folds the loaded dwords into a running xor. Workgroups hold four waves and
+// the grid covers the buffer at once, so the hardware keeps as many waves
+// resident as fit. Measured on MI355X with an event pair around each launch
+// after a cache eviction, two blocks per wave streamed 512 MiB fastest
+// (80-82 us) among the plain read shapes tried (registers or LDS DMA,
+// persistent or not, one or four waves per workgroup, 2 to 32 blocks per
+// wave); over 4 GiB, sixteen blocks per wave streamed fastest. A wave xors its
+// lanes' values together and adds the result to one of the sink's words with
+// one atomic xor (spread over the words: one word taking all 16 384 atomics
+// of a 512 MiB read made the launch take 208 us instead of 85 us).
 #include "stream_probe.h"
 
 namespace msa {
@@ -21,17 +22,17 @@ namespace {
 typedef int probe_v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kProbeWavesPerGroup = 4;
-constexpr int kProbeBlocksPerWave = 2;
 
+template <int kBlocks>
 __global__ __launch_bounds__(64 * kProbeWavesPerGroup)
 void stream_read_probe_kernel(const uint8_t* src, int64_t blocks, uint32_t* sink)
 {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * kProbeWavesPerGroup + (threadIdx.x >> 6);
     uint32_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < kProbeBlocksPerWave; ++i) {
-        const int64_t b = wave * kProbeBlocksPerWave + i;
+#pragma unroll 2
+    for (int i = 0; i < kBlocks; ++i) {
+        const int64_t b = wave * kBlocks + i;
         if (b >= blocks)
             break;
         const uint8_t* block = src + b * kProbeBlockBytes;
@@ -47,20 +48,27 @@ void stream_read_probe_kernel(const uint8_t* src, int64_t blocks, uint32_t* sink
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         acc ^= (uint32_t)__shfl_xor((int)acc, off);
-    if (lane == 0 && wave * kProbeBlocksPerWave < blocks)
+    if (lane == 0 && wave * kBlocks < blocks)
         atomicXor(sink + wave % kProbeSinkWords, acc);
 }
 
 }  // namespace
 
-hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, uint32_t* sink,
-                                    hipStream_t stream)
+hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, int blocks_per_wave,
+                                    uint32_t* sink, hipStream_t stream)
 {
-    const int64_t per_group = (int64_t)kProbeWavesPerGroup * kProbeBlocksPerWave;
+    const void* fn = nullptr;
+    switch (blocks_per_wave) {
+    case 2: fn = reinterpret_cast<const void*>(&stream_read_probe_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&stream_read_probe_kernel<4>); break;
+    case 8: fn = reinterpret_cast<const void*>(&stream_read_probe_kernel<8>); break;
+    case 16: fn = reinterpret_cast<const void*>(&stream_read_probe_kernel<16>); break;
+    default: return hipErrorInvalidValue;
+    }
+    const int64_t per_group = (int64_t)kProbeWavesPerGroup * blocks_per_wave;
     const int64_t groups = (blocks + per_group - 1) / per_group;
     void* args[] = {&src, &blocks, &sink};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_probe_kernel),
-                           dim3((unsigned)groups), dim3(64 * kProbeWavesPerGroup), args, 0,
+    return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kProbeWavesPerGroup), args, 0,
                            stream);
 }
 

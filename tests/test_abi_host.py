@@ -305,11 +305,14 @@ def test_merge_dedup_rejects(lib, kw, needle):
     (dict(nbytes=0), "multiple"),
     (dict(nbytes=-16384), "multiple"),
     (dict(nbytes=16384 + 16), "multiple"),
+    (dict(bpw=0), "blocks_per_wave"),
+    (dict(bpw=3), "blocks_per_wave"),
+    (dict(bpw=32), "blocks_per_wave"),
 ])
 def test_stream_read_probe_rejects(lib, kw, needle):
-    a = dict(src=FAKE, nbytes=1 << 20, sink=FAKE, stream=None)
+    a = dict(src=FAKE, nbytes=1 << 20, bpw=2, sink=FAKE, stream=None)
     a.update(kw)
-    assert lib.msa_stream_read_probe(a["src"], a["nbytes"], a["sink"],
+    assert lib.msa_stream_read_probe(a["src"], a["nbytes"], a["bpw"], a["sink"],
                                      a["stream"]) == msa.MSA_ERR_INVALID_ARG
     assert needle in lib.msa_last_error().decode()
 

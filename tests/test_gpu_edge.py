@@ -417,15 +417,16 @@ def test_plane_beyond_2g_elements():
 
 
 @pytest.mark.parametrize("blocks", [1, 7, 3000])
-def test_stream_read_probe_reads_every_byte(blocks):
+@pytest.mark.parametrize("bpw", [2, 4, 8, 16])
+def test_stream_read_probe_reads_every_byte(blocks, bpw):
     """The streaming-read probe (the benchmark's ceiling for the scorer) reads
-    every byte once: its xor of all the buffer's dwords equals the host's,
-    for a partial last workgroup and a partial last wave."""
+    every byte once at every shape: its xor of all the buffer's dwords equals
+    the host's, for a partial last workgroup and a partial last wave."""
     g = torch.Generator().manual_seed(blocks)
     host = torch.randint(0, 256, (blocks * 16384,), dtype=torch.uint8, generator=g)
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=DEV)
-    msa.msa_stream_read_probe(host.to(DEV), sink)
+    msa.msa_stream_read_probe(host.to(DEV), sink, blocks_per_wave=bpw)
     torch.cuda.synchronize()
     assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
 
