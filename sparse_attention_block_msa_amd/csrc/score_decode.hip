@@ -717,7 +717,7 @@ void score_select_kernel(ScoreSelectParams q)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];
-    __shared__ topk::Candidate cand[64];
+    __shared__ topk::Candidate cand[topk::kCandSlots];
     __shared__ msa_top16_row row_buf;
     const ScoreParams& p = q.score;
     const int lane = threadIdx.x;

@@ -32,7 +32,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
 {
     __shared__ msa_top16_row part[NW];
-    __shared__ Candidate cand[NW][64];
+    __shared__ Candidate cand[NW][kCandSlots];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t job = blockIdx.x;  // ((t * 4) + h) * R + r
@@ -70,7 +70,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
 {
     __shared__ msa_top16_row part[NW];
-    __shared__ Candidate cand[NW][64];
+    __shared__ Candidate cand[NW][kCandSlots];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
@@ -380,7 +380,7 @@ template <int V, int VM>
 __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergeParams p)
 {
     __shared__ msa_top16_row part[kMaxFusedRanges];
-    __shared__ Candidate cand[kMaxFusedRanges][64];
+    __shared__ Candidate cand[kMaxFusedRanges][kCandSlots];
     const int lane = threadIdx.x & 63;
     const int r = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
@@ -454,7 +454,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergeParams p)
 {
     constexpr int VM = NW * kTop / 64 > 0 ? NW * kTop / 64 : 1;  // merge values per lane
-    __shared__ Candidate seg[NW][64];
+    __shared__ Candidate seg[NW][kCandSlots];
     __shared__ int seg_count[NW];
     __shared__ uint32_t theta_w[NW];
     __shared__ msa_top16_row part[NW];

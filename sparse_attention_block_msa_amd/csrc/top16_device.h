@@ -43,9 +43,12 @@ __device__ __forceinline__ int is_forced(int id, int n, int init_blocks, int loc
     return id >= 0 && id < n && (id < init_blocks || id >= n - local_blocks);
 }
 
-// Value of lane (this lane ^ j), j a power of two below 64, without LDS
-// addressing: DPP quad permutes for 1 and 2, swizzle (bitmask mode, within
-// each 32-lane half) for 4, 8 and 16, the permlane32 swap for 32.
+// Value of lane (this lane ^ j), j a power of two below 64, on the VALU
+// alone (no LDS round trip): DPP quad permutes for 1 and 2; DPP row rotates
+// within 16-lane rows for 4 (rotate by 12 reads lane +4, by 4 reads lane -4;
+// the lane's bit 2 picks) and 8 (rotate by 8); the permlane16 and permlane32
+// swaps for 16 and 32. (Lane layouts checked on the device. The LDS swizzle
+// these replace for 4, 8 and 16 waited an LDS round trip per exchange.)
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane)
 {
@@ -53,11 +56,19 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane)
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
     } else if constexpr (J == 2) {
         return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
-    } else if constexpr (J == 32) {
+    } else if constexpr (J == 4) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, true);
+        const uint32_t down = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);
+        return (lane & 4) ? down : up;
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
+    } else if constexpr (J == 16) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? sw[0] : sw[1];
+    } else {
+        static_assert(J == 32, "lane_xor: J must be a power of two below 64");
         const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
         return lane < 32 ? sw[1] : sw[0];
-    } else {
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (J << 10) | 0x1F);
     }
 }
 
@@ -240,13 +251,51 @@ struct Candidate {
     int id;
 };
 
+// Entries of a buffer handed to wave_select_filtered / select_row /
+// select_loaded: 64 compacted entries, then one spill entry per lane, which
+// the compaction's unselected lanes write to (so that its stores need no
+// branch).
+constexpr int kCandSlots = 128;
+
+// Compacts the selected elements (keys >= theta, and with kForced also the
+// elements whose bit of fbits is set) in element order into buf[0 .. 64);
+// returns how many were selected (uniform). Only the first 64 are stored;
+// callers take another path when more are selected. Keys are stored as they
+// are: forced elements carry key 0. Every element is stored, an unselected
+// one (or one past 64) to its lane's spill entry 64 + lane, so the loop has
+// no branch; each register costs one ballot, its count on the scalar unit
+// and one LDS store.
+template <bool kForced, int V, class IdOf>
+__device__ __forceinline__ int compact_selected(const uint32_t (&u)[V], const float (&sv)[V],
+                                                uint64_t fbits, uint32_t theta, int lane,
+                                                Candidate* buf, IdOf&& id_of)
+{
+    const int spill = 64 + lane;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        bool sel = u[i] >= theta;
+        if constexpr (kForced)
+            sel = sel || ((fbits >> i) & 1ull);
+        const uint64_t mask = __ballot(sel);
+        const int slot = min(sel ? base + lanes_below(mask) : spill, spill);
+        Candidate c;
+        c.key = u[i];
+        c.score = sv[i];
+        c.id = id_of(i);
+        buf[slot] = c;
+        base += __popcll(mask);
+    }
+    return base;
+}
+
 // Wave-level select, same contract as wave_select, for V > 1 values per lane.
-// Elements are (u[i], sv[i], id_of(i)). Every key of the best K is >= theta,
-// the K-th largest of the 64 per-lane maxima (at least K keys are >= it), so
-// when the keys >= theta plus the forced elements number at most 64 they are
-// compacted in element order into `buf` (one per lane) and ranked there with
-// one value per lane; otherwise (the compaction counts them as it goes and
-// stops writing past 64) the full V-value search runs.
+// Elements are (u[i], sv[i], id_of(i)); forced elements carry key 0. Every
+// key of the best K is >= theta, the K-th largest of the 64 per-lane maxima
+// (at least K keys are >= it), so when the keys >= theta plus the forced
+// elements number at most 64 they are compacted in element order into `buf`
+// (kCandSlots entries; one per lane) and ranked there with one value per
+// lane; otherwise the full V-value search runs.
 template <int V, class IdOf, class Emit>
 __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], const float (&sv)[V],
                                                     uint64_t fbits, int budget, int n_cand,
@@ -261,22 +310,13 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
     uint32_t theta = 1u;
     if (K > 0)
         theta = max(kth_largest_of_lanes(lane_max, K, lane), 1u);
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const bool forced = (fbits >> i) & 1ull;
-        const bool sel = forced || (K > 0 && u[i] >= theta);
-        const uint64_t mask = __ballot(sel);
-        const int slot = base + lanes_below(mask);
-        if (sel && slot < 64) {
-            Candidate c;
-            c.key = forced ? 0u : u[i];
-            c.score = sv[i];
-            c.id = id_of(i);
-            buf[slot] = c;
-        }
-        base += __popcll(mask);
-    }
+    // with no candidate to keep, theta admits no key (a key of ~0u, a NaN
+    // score, may pass it but is then never kept: the budget is 0)
+    if (K == 0)
+        theta = ~0u;
+    const int base = __ballot(fbits != 0ull) != 0ull
+                         ? compact_selected<true>(u, sv, fbits, theta, lane, buf, id_of)
+                         : compact_selected<false>(u, sv, fbits, theta, lane, buf, id_of);
     if (base > 64)  // heavy ties at theta: rank all V values per lane instead
         return wave_select<V>(u, fbits, budget, n_cand,
                               [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
@@ -419,6 +459,17 @@ __device__ __forceinline__ ColumnIds column_ids(int n, int init_blocks, int loca
     return ci;
 }
 
+// Bits i (0 <= i < V) of the elements of this lane that fall in columns
+// [a, b): element i of the lane is column col0 + 64 i (col0 = span_lo + lane),
+// so they are the i in [ceil((a - col0) / 64), ceil((b - col0) / 64)).
+template <int V>
+__device__ __forceinline__ uint64_t column_interval_bits(int a, int b, int col0)
+{
+    const int lo = max(0, (a - col0 + 63) >> 6);
+    const int hi = min(V, max(0, (b - col0 + 63) >> 6));
+    return hi > lo ? (1ull << hi) - (1ull << lo) : 0ull;
+}
+
 // Selects over a span loaded by load_span, within the column range ending at
 // hi. The candidate budget is 16 minus the forced ids found in the span.
 // Writes the kept entries (global ids) and the padding to dst and returns the
@@ -429,30 +480,26 @@ __device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, 
                                              Candidate* buf)
 {
     // Valid columns of the span: [span_lo, valid_hi). Forced columns are
-    // [0, init_end) and [local_begin, valid_end); both counts are interval
-    // arithmetic, so no ballots are spent on them.
+    // [0, init_end) and [local_begin, valid_end), so the candidates (valid,
+    // not forced) are the one interval [cand_lo, cand_hi). Counts and masks
+    // are interval arithmetic: no per-element test but one compare.
     const int valid_hi = min(min(hi, ci.valid_end), span_lo + V * 64);
     const int n_valid = max(0, valid_hi - span_lo);
     const int n_init = max(0, min(valid_hi, ci.init_end) - span_lo);
     const int n_local = max(0, valid_hi - max(span_lo, ci.local_begin));
     const int n_both = max(0, min(valid_hi, ci.init_end) - max(span_lo, ci.local_begin));
     const int n_forced = n_init + n_local - n_both;
+    const int cand_lo = max(span_lo, ci.init_end);
+    const uint32_t cand_len = (uint32_t)max(0, min(valid_hi, ci.local_begin) - cand_lo);
+    const int rel = span_lo + lane - cand_lo;  // element i: column - cand_lo = rel + 64 i
     uint32_t u[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        u[i] = (uint32_t)(rel + 64 * i) < cand_len ? order_key(sv[i]) : 0u;
     uint64_t fbits = 0;
-    if (n_forced == 0) {  // the usual case away from a row's ends
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-            u[i] = span_lo + i * 64 + lane < valid_hi ? order_key(sv[i]) : 0u;
-    } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int c = span_lo + i * 64 + lane;
-            const bool valid = c < valid_hi;
-            const bool forced = valid && (c < ci.init_end || c >= ci.local_begin);
-            u[i] = valid && !forced ? order_key(sv[i]) : 0u;
-            fbits |= (uint64_t)forced << i;
-        }
-    }
+    if (n_forced > 0)  // only near a row's ends
+        fbits = column_interval_bits<V>(span_lo, min(valid_hi, ci.init_end), span_lo + lane) |
+                column_interval_bits<V>(max(span_lo, ci.local_begin), valid_hi, span_lo + lane);
     const int kept = select_row<V>(u, sv, fbits, kTop - n_forced, n_valid - n_forced, lane, buf,
                                    [&](int i) { return ci.scale * (span_lo + i * 64 + lane) + ci.offset; },
                                    [&](float score, int id, int slot) {
