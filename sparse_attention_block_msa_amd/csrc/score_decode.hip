@@ -646,7 +646,7 @@ __device__ __forceinline__ int range_columns(const ScoreSelectParams& q, int wb,
 // cover R * 16 <= 64 * VM entries.
 template <int VM>
 __device__ __forceinline__ void fused_merge(const ScoreSelectParams& q, int64_t th, int n,
-                                            int lane, topk::Candidate* buf)
+                                            int lane, topk::CandBuf* buf)
 {
     using namespace topk;
     const int total = q.num_ranges * kTop;
@@ -717,7 +717,7 @@ void score_select_kernel(ScoreSelectParams q)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[(8 / kParts) * 16 * kDim];
     __shared__ __attribute__((aligned(16))) float res[32][kChunk];
-    __shared__ topk::Candidate cand[topk::kCandSlots];
+    __shared__ topk::CandBuf cand;
     __shared__ msa_top16_row row_buf;
     const ScoreParams& p = q.score;
     const int lane = threadIdx.x;
@@ -784,7 +784,7 @@ void score_select_kernel(ScoreSelectParams q)
         float sv[V];
         topk::load_span<V, true>(p.out + th * p.cols, p.cols, lo, lane, sv);
         topk::select_loaded<V>(sv, lo, hi, topk::column_ids(n, q.init_blocks, q.local_blocks, 1, 0),
-                               &row_buf, lane, cand);
+                               &row_buf, lane, &cand);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -803,13 +803,13 @@ void score_select_kernel(ScoreSelectParams q)
                 if (lane0_add(tickets + th, 1) == R - 1) {
                     const int nm = max(0, nvp);  // as msa_top16_merge reads it
                     if (R <= 4)
-                        fused_merge<1>(q, th, nm, lane, cand);
+                        fused_merge<1>(q, th, nm, lane, &cand);
                     else if (R <= 8)
-                        fused_merge<2>(q, th, nm, lane, cand);
+                        fused_merge<2>(q, th, nm, lane, &cand);
                     else if (R <= 16)
-                        fused_merge<4>(q, th, nm, lane, cand);
+                        fused_merge<4>(q, th, nm, lane, &cand);
                     else
-                        fused_merge<16>(q, th, nm, lane, cand);
+                        fused_merge<16>(q, th, nm, lane, &cand);
                     lane0_store(tickets + th, 0);
                 }
             }

@@ -32,7 +32,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
 {
     __shared__ msa_top16_row part[NW];
-    __shared__ Candidate cand[NW][kCandSlots];
+    __shared__ CandBuf cand[NW];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t job = blockIdx.x;  // ((t * 4) + h) * R + r
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
     const ColumnIds ci = column_ids(n, p.init_blocks, p.local_blocks, p.index_scale,
                                     p.index_offset);
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
-    select_loaded<V>(sv, span_lo, hi, ci, dst, lane, cand[wave]);
+    select_loaded<V>(sv, span_lo, hi, ci, dst, lane, &cand[wave]);
 
     if (NW > 1) {
         __syncthreads();
@@ -70,7 +70,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
 {
     __shared__ msa_top16_row part[NW];
-    __shared__ Candidate cand[NW][kCandSlots];
+    __shared__ CandBuf cand[NW];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
     const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
     msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
     const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
-    const int kept = select_row<V>(u, sv, fbits, budget, count_keys<V>(u), lane, cand[wave],
+    const int kept = select_row<V>(u, sv, fbits, budget, count_keys<V>(u), lane, &cand[wave],
                                    [&](int i) { return iv[i]; },
                                    [&](float score, int id, int slot) {
                                        dst->score[slot] = score;
@@ -375,12 +375,20 @@ __global__ __launch_bounds__(64) void top16_merge_dedup_kernel(MergeParams p)
 // r selects range r exactly as top16_select_kernel does with one wave per
 // range, writes its row to `partial` (when given) and to LDS, and wave 0 then
 // merges the R rows exactly as top16_merge_kernel does (every forced id of
-// the row is in one of them, so the budget is 16 - |forced of [0, n)|).
+// the row is in one of them, so the budget is K = 16 - |forced of [0, n)|).
+// The merge first prunes: wave r also reports theta_r, the key of its
+// range's K-th best candidate (0 if it has fewer or the search did not
+// rank them). The row's K-th best key is at least every theta_r (range r
+// alone holds K keys >= theta_r), so the row's best K are among the entries
+// with keys >= max theta_r, and with forced entries those usually fit one
+// wave: they are ranked as the range selects rank their survivors.
+// Otherwise the merge selects over all R rows.
 template <int V, int VM>
 __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergeParams p)
 {
     __shared__ msa_top16_row part[kMaxFusedRanges];
-    __shared__ Candidate cand[kMaxFusedRanges][kCandSlots];
+    __shared__ CandBuf cand[kMaxFusedRanges];
+    __shared__ uint32_t range_kth[kMaxFusedRanges];
     const int lane = threadIdx.x & 63;
     const int r = threadIdx.x >> 6;
     const int64_t th = blockIdx.x;  // t * 4 + h
@@ -395,10 +403,14 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
             atomicAdd(p.errors, 1);
         n = n < 0 ? 0 : p.cols;
     }
+    const int budget = kTop - forced_count(n, p.init_blocks, p.local_blocks);
     msa_top16_row* mine = &part[r];
+    uint32_t kth = 0u;
     select_loaded<V>(sv, lo, min(lo + p.width, p.cols), column_ids(n, p.init_blocks,
                                                                   p.local_blocks, 1, 0),
-                     mine, lane, cand[r]);
+                     mine, lane, &cand[r], budget, &kth);
+    if (lane == 0)
+        range_kth[r] = kth;
     __syncthreads();
     if (p.partial && lane < 2 * kTop)
         reinterpret_cast<int*>(p.partial + th * p.num_ranges + r)[lane] =
@@ -407,6 +419,9 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
         return;
 
     // wave 0: merge the R rows from LDS
+    uint32_t theta = 1u;
+    for (int w = 0; w < p.num_ranges; ++w)
+        theta = max(theta, range_kth[w]);
     const int total = p.num_ranges * kTop;
     float mv[VM];
     int iv[VM];
@@ -426,12 +441,18 @@ __global__ __launch_bounds__(1024) void top16_select_merge_kernel(SelectMergePar
         fm |= (uint64_t)forced << i;
     }
     msa_top16_row* dst = p.out + th;
-    const int kept_m = select_row<VM>(um, mv, fm, kTop - forced_count(n, p.init_blocks, p.local_blocks),
-                                      count_keys<VM>(um), lane, cand[0], [&](int i) { return iv[i]; },
-                                      [&](float score, int id, int slot) {
-                                          dst->score[slot] = score;
-                                          dst->id[slot] = id;
-                                      });
+    auto emit = [&](float score, int id, int slot) {
+        dst->score[slot] = score;
+        dst->id[slot] = id;
+    };
+    const int n_cand = count_keys<VM>(um);
+    const int K = min(budget, n_cand);
+    const int survivors = compact_selected<true>(um, mv, fm, K > 0 ? theta : ~0u, lane, &cand[0],
+                                                 [&](int i) { return iv[i]; });
+    const int kept_m = survivors <= 64
+                           ? rank_select(&cand[0], survivors, K, lane, 0, nullptr, emit)
+                           : select_row<VM>(um, mv, fm, budget, n_cand, lane, &cand[0],
+                                            [&](int i) { return iv[i]; }, emit);
     pad_row(dst, kept_m, lane);
 }
 
@@ -454,7 +475,7 @@ template <int V, int NW>
 __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergeParams p)
 {
     constexpr int VM = NW * kTop / 64 > 0 ? NW * kTop / 64 : 1;  // merge values per lane
-    __shared__ Candidate seg[NW][kCandSlots];
+    __shared__ CandBuf seg[NW];
     __shared__ int seg_count[NW];
     __shared__ uint32_t theta_w[NW];
     __shared__ msa_top16_row part[NW];
@@ -512,13 +533,8 @@ __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergePa
         const bool sel = forced || (K > 0 && u[i] >= theta);
         const uint64_t mask = __ballot(sel);
         const int slot = base + lanes_below(mask);
-        if (sel && slot < 64) {
-            Candidate c;
-            c.key = forced ? 0u : u[i];  // candidates have keys >= theta >= 1
-            c.score = sv[i];
-            c.id = span_lo + i * 64 + lane;
-            seg[wave][slot] = c;
-        }
+        if (sel && slot < 64)  // candidates have keys >= theta >= 1
+            cand_store(&seg[wave], slot, forced ? 0u : u[i], sv[i], span_lo + i * 64 + lane);
         base += __popcll(mask);
     }
     if (lane == 0)
@@ -544,7 +560,7 @@ __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergePa
             for (int w = 0; w < NW; ++w) {
                 const int cnt = seg_count[w];
                 if (e >= before && e < before + cnt)
-                    c = seg[w][e - before];
+                    c = cand_load(&seg[w], e - before);
                 before += cnt;
             }
             return c;
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergePa
     }
 
     // fallback: select every span, then merge the NW rows
-    select_loaded<V>(sv, span_lo, p.cols, ci, &part[wave], lane, seg[wave]);
+    select_loaded<V>(sv, span_lo, p.cols, ci, &part[wave], lane, &seg[wave]);
     __syncthreads();
     if (wave != 0)
         return;
@@ -600,7 +616,7 @@ __global__ __launch_bounds__(NW * 64) void top16_row_select_kernel(SelectMergePa
         um[i] = valid && !forced ? order_key(mv[i]) : 0u;
         fm |= (uint64_t)forced << i;
     }
-    const int kept_m = select_row<VM>(um, mv, fm, K, count_keys<VM>(um), lane, seg[0],
+    const int kept_m = select_row<VM>(um, mv, fm, K, count_keys<VM>(um), lane, &seg[0],
                                       [&](int i) { return iv[i]; },
                                       [&](float score, int id, int slot) {
                                           dst->score[slot] = score;

@@ -242,20 +242,52 @@ __device__ __forceinline__ int wave_select(const uint32_t (&u)[V], uint64_t fbit
     return base;
 }
 
-// Compaction buffer of one wave: up to 64 entries (key, raw score, id).
-// In wave_select_filtered's buffer a forced entry has key 0, every other
-// entry a key >= 1, so ids keep all 31 bits.
+// One entry (key, raw score, id); the duplicate-aware merge's buffer.
 struct Candidate {
     uint32_t key;
     float score;
     int id;
 };
 
-// Entries of a buffer handed to wave_select_filtered / select_row /
-// select_loaded: 64 compacted entries, then one spill entry per lane, which
+// Compaction buffer of one wave (wave_select_filtered / select_row /
+// select_loaded): 64 compacted entries, then one spill entry per lane, which
 // the compaction's unselected lanes write to (so that its stores need no
-// branch).
+// branch). Forced entries carry key 0, the others keys >= 1, so ids keep all
+// 31 bits. Stored as two arrays of 8-byte words, so that a wave's stores
+// and reads of one word per lane touch consecutive banks:
+//  * pair[s] = key << 32 | order, order = ~s: the pairs order entries by key,
+//    then by lower slot, and are unique within a buffer;
+//  * payload[s] = id << 32 | score bits.
 constexpr int kCandSlots = 128;
+struct CandBuf {
+    uint64_t pair[kCandSlots];
+    uint64_t payload[kCandSlots];
+};
+
+// Two ds_write2_b32, whose data operands are any registers: with 8-byte
+// stores (or one 16-byte store) the compiler forms register pairs (tuples)
+// for every element of a fully unrolled compaction, which pushed the
+// 32-values-per-lane select past its register budget. A wave's LDS
+// operations complete in order, so these untracked stores need no wait
+// before its own later reads.
+__device__ __forceinline__ void cand_store(CandBuf* b, int slot, uint32_t key, float score,
+                                           int id)
+{
+    typedef __attribute__((address_space(3))) uint64_t lds_u64;
+    const uint32_t a = (uint32_t)(uintptr_t)(lds_u64*)&b->pair[slot];
+    const uint32_t c = (uint32_t)(uintptr_t)(lds_u64*)&b->payload[slot];
+    asm volatile("ds_write2_b32 %0, %2, %3 offset1:1\n\t"
+                 "ds_write2_b32 %1, %4, %5 offset1:1"
+                 :
+                 : "v"(a), "v"(c), "v"(~(uint32_t)slot), "v"(key), "v"(score), "v"(id)
+                 : "memory");
+}
+
+__device__ __forceinline__ Candidate cand_load(const CandBuf* b, int slot)
+{
+    const uint64_t w = b->payload[slot];
+    return {(uint32_t)(b->pair[slot] >> 32), __uint_as_float((uint32_t)w), (int)(w >> 32)};
+}
 
 // Compacts the selected elements (keys >= theta, and with kForced also the
 // elements whose bit of fbits is set) in element order into buf[0 .. 64);
@@ -268,7 +300,7 @@ constexpr int kCandSlots = 128;
 template <bool kForced, int V, class IdOf>
 __device__ __forceinline__ int compact_selected(const uint32_t (&u)[V], const float (&sv)[V],
                                                 uint64_t fbits, uint32_t theta, int lane,
-                                                Candidate* buf, IdOf&& id_of)
+                                                CandBuf* buf, IdOf&& id_of)
 {
     const int spill = 64 + lane;
     int base = 0;
@@ -278,15 +310,57 @@ __device__ __forceinline__ int compact_selected(const uint32_t (&u)[V], const fl
         if constexpr (kForced)
             sel = sel || ((fbits >> i) & 1ull);
         const uint64_t mask = __ballot(sel);
-        const int slot = min(sel ? base + lanes_below(mask) : spill, spill);
-        Candidate c;
-        c.key = u[i];
-        c.score = sv[i];
-        c.id = id_of(i);
-        buf[slot] = c;
+        const int at = base + lanes_below(mask);  // every lane: no exec-masked region
+        const int slot = min(sel ? at : spill, spill);
+        cand_store(buf, slot, u[i], sv[i], id_of(i));
         base += __popcll(mask);
     }
     return base;
+}
+
+// Ranks the n <= 64 entries buf[0, n) that compact_selected stored (element
+// order; forced entries carry key 0, the others keys >= 1) and keeps the
+// forced ones and the K best others by key descending, then lower slot (=
+// lower element): each lane counts the entries whose (key, order) pair
+// exceeds its own, reading every pair from LDS at one address for all lanes
+// (a broadcast), two per instruction. The pairs are unique, so the ranks
+// are; no tie pass is needed. Kept entries are emitted in slot order with
+// emit(score, id, slot) for slots below kTop. With q > 0, *qkey receives the
+// key of the non-forced entry of rank q - 1 (0 if there are fewer than q).
+// Returns the number kept (uniform).
+template <class Emit>
+__device__ __forceinline__ int rank_select(CandBuf* buf, int n, int K, int lane, int q,
+                                           uint32_t* qkey, Emit&& emit)
+{
+    if (n < 64 && lane == 0)  // a zero pair past the last entry: pairs are read two at a time
+        buf->pair[n] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool have = lane < n;
+    uint64_t me = 0ull, payload = 0ull;
+    if (have) {
+        me = buf->pair[lane];
+        payload = buf->payload[lane];
+    }
+    int rank = 0;
+    for (int j = 0; j < n; j += 2)
+        rank += (int)(buf->pair[j] > me) + (int)(buf->pair[j + 1] > me);
+    const uint32_t key = (uint32_t)(me >> 32);
+    const bool forced = have && key == 0u;
+    const bool keep = forced || (have && rank < K);
+    const uint64_t kept = __ballot(keep);
+    const int slot = lanes_below(kept);
+    if (keep && slot < kTop)
+        emit(__uint_as_float((uint32_t)payload), (int)(payload >> 32), slot);
+    if (q > 0) {
+        const uint64_t at = __ballot(have && !forced && rank == q - 1);
+        *qkey = at ? (uint32_t)__builtin_amdgcn_readlane((int)key, (int)__builtin_ctzll(at)) : 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return __popcll(kept);
 }
 
 // Wave-level select, same contract as wave_select, for V > 1 values per lane.
@@ -295,12 +369,14 @@ __device__ __forceinline__ int compact_selected(const uint32_t (&u)[V], const fl
 // (at least K keys are >= it), so when the keys >= theta plus the forced
 // elements number at most 64 they are compacted in element order into `buf`
 // (kCandSlots entries; one per lane) and ranked there with one value per
-// lane; otherwise the full V-value search runs.
+// lane (rank_select, whose q / qkey this passes on); otherwise the full
+// V-value search runs (and *qkey, if asked for, is 0).
 template <int V, class IdOf, class Emit>
 __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], const float (&sv)[V],
                                                     uint64_t fbits, int budget, int n_cand,
-                                                    int lane, Candidate* buf, IdOf&& id_of,
-                                                    Emit&& emit)
+                                                    int lane, CandBuf* buf, IdOf&& id_of,
+                                                    Emit&& emit, int q = 0,
+                                                    uint32_t* qkey = nullptr)
 {
     uint32_t lane_max = 0;
 #pragma unroll
@@ -317,22 +393,13 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
     const int base = __ballot(fbits != 0ull) != 0ull
                          ? compact_selected<true>(u, sv, fbits, theta, lane, buf, id_of)
                          : compact_selected<false>(u, sv, fbits, theta, lane, buf, id_of);
-    if (base > 64)  // heavy ties at theta: rank all V values per lane instead
+    if (base > 64) {  // heavy ties at theta: rank all V values per lane instead
+        if (q > 0)
+            *qkey = 0u;
         return wave_select<V>(u, fbits, budget, n_cand,
                               [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    Candidate mine = {0u, -INFINITY, -1};
-    if (lane < base)
-        mine = buf[lane];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint32_t u1[1] = {mine.key};
-    const uint64_t f1 = (lane < base && mine.key == 0u) ? 1ull : 0ull;
-    return wave_select<1>(u1, f1, budget, n_cand,
-                          [&](int, int slot) { emit(mine.score, mine.id, slot); });
+    }
+    return rank_select(buf, base, K, lane, q, qkey, emit);
 }
 
 #ifndef MSA_SELECT_DIRECT_MAX_V
@@ -341,15 +408,21 @@ __device__ __forceinline__ int wave_select_filtered(const uint32_t (&u)[V], cons
 
 // Picks the search for V values per lane: direct for small V, filtered above.
 // n_cand is the number of candidate keys (u != 0).
+// With q > 0, *qkey receives the key of the candidate of rank q - 1 when the
+// filtered search finds it (0 otherwise, and always on the direct path).
 template <int V, class IdOf, class Emit>
 __device__ __forceinline__ int select_row(const uint32_t (&u)[V], const float (&sv)[V],
                                           uint64_t fbits, int budget, int n_cand, int lane,
-                                          Candidate* buf, IdOf&& id_of, Emit&& emit)
+                                          CandBuf* buf, IdOf&& id_of, Emit&& emit, int q = 0,
+                                          uint32_t* qkey = nullptr)
 {
-    if (V <= MSA_SELECT_DIRECT_MAX_V)
+    if (V <= MSA_SELECT_DIRECT_MAX_V) {
+        if (q > 0)
+            *qkey = 0u;
         return wave_select<V>(u, fbits, budget, n_cand,
                               [&](int i, int slot) { emit(sv[i], id_of(i), slot); });
-    return wave_select_filtered<V>(u, sv, fbits, budget, n_cand, lane, buf, id_of, emit);
+    }
+    return wave_select_filtered<V>(u, sv, fbits, budget, n_cand, lane, buf, id_of, emit, q, qkey);
 }
 
 __device__ __forceinline__ void pad_row(msa_top16_row* row, int kept, int lane)
@@ -473,11 +546,11 @@ __device__ __forceinline__ uint64_t column_interval_bits(int a, int b, int col0)
 // Selects over a span loaded by load_span, within the column range ending at
 // hi. The candidate budget is 16 minus the forced ids found in the span.
 // Writes the kept entries (global ids) and the padding to dst and returns the
-// number kept.
+// number kept. q / qkey: as select_row.
 template <int V>
 __device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, int hi,
                                              const ColumnIds& ci, msa_top16_row* dst, int lane,
-                                             Candidate* buf)
+                                             CandBuf* buf, int q = 0, uint32_t* qkey = nullptr)
 {
     // Valid columns of the span: [span_lo, valid_hi). Forced columns are
     // [0, init_end) and [local_begin, valid_end), so the candidates (valid,
@@ -505,7 +578,8 @@ __device__ __forceinline__ int select_loaded(const float (&sv)[V], int span_lo, 
                                    [&](float score, int id, int slot) {
                                        dst->score[slot] = score;
                                        dst->id[slot] = id;
-                                   });
+                                   },
+                                   q, qkey);
     pad_row(dst, kept, lane);
     return kept;
 }
