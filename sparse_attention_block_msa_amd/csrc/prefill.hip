@@ -222,6 +222,12 @@ __device__ __forceinline__ void prefill_block(const uint8_t* tile,
         // each other, and a tile's result is read kWaveTiles MFMAs after its
         // last step was issued
         v4f a[kWaveTiles];
+        // The wave issues its MFMA burst at raised priority, so that on its
+        // SIMD the burst goes first and the other wave's conversions and
+        // maxima fill the cycles the matrix core is busy. Measured (chains
+        // back to back, outputs bit-identical): 460-463 -> 437-449 us on the
+        // 8192-token window, 275 -> 256-270 us on four 2048-token chunks.
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int n = 0; n < kWaveTiles; ++n)
             a[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.op[0], qb[n].op[0], zero, 0, 0, 0);
@@ -232,6 +238,7 @@ __device__ __forceinline__ void prefill_block(const uint8_t* tile,
                 a[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb.op[s], qb[n].op[s], a[n], 0, 0,
                                                                0);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int n = 0; n < kWaveTiles; ++n) {
             v4f x = a[n];
