@@ -872,7 +872,10 @@ const void* score_latency_kernel_fn()
 template <int NT, int V, bool kLatency>
 const void* score_select_kernel_fn()
 {
-    constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
+    // 32 values per lane do not fit the 3-waves-per-SIMD register budget of
+    // the 16-row scorer (spills): that instance takes the 2-wave budget
+    constexpr int kRegWaves = NT == 1 ? (V >= 32 ? 2 : MSA_SCORE_REG_WAVES_16)
+                                      : MSA_SCORE_REG_WAVES_32;
     if constexpr (kLatency)  // one column per wave, a block per DMA round trip
         return reinterpret_cast<const void*>(
             &score_select_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, V, 1>);
