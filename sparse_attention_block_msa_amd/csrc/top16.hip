@@ -112,6 +112,28 @@ __global__ __launch_bounds__(NW * 64) void top16_merge_kernel(MergeParams p)
         atomicAdd(p.errors, 1);
 
     const int expected_forced = forced_count(n, p.init_blocks, p.local_blocks);
+    if (V == 1 && p.num_ranges == 1) {
+        // One row in (a prefill merge with R = 1): when it is already what the
+        // merge would make of it (valid ids ascending in front, every forced
+        // id present, canonical padding behind), the merge is the row itself
+        // and is copied; any other row takes the selection below.
+        const bool valid = lane < kTop && iv[0] >= 0;
+        const uint64_t vmask = __ballot(valid);
+        const int m = __popcll(vmask);
+        // (a key of 0, a NaN score with every bit set, is no candidate: the
+        // selection would drop it)
+        const bool entry_ok = lane >= kTop ||
+                              (valid ? order_key(sv[0]) != 0u
+                                     : iv[0] == -1 && __float_as_uint(sv[0]) == 0xFF800000u);
+        if (vmask == (1ull << m) - 1ull && __ballot(!entry_ok) == 0ull && !disorder_mask &&
+            n_forced == expected_forced) {
+            if (lane < kTop) {
+                p.out[th].score[lane] = sv[0];
+                p.out[th].id[lane] = iv[0];
+            }
+            return;
+        }
+    }
     msa_top16_row* dst = NW == 1 ? p.out + th : &part[wave];
     const int budget = NW == 1 ? kTop - expected_forced : kTop - n_forced;
     const int kept = select_row<V>(u, sv, fbits, budget, count_keys<V>(u), lane, &cand[wave],

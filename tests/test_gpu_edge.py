@@ -460,3 +460,42 @@ def test_scorer_latency_mode_large_batch():
     assert np.array_equal(plane.cpu().numpy().view(np.uint32), got.view(np.uint32))
     assert torch.equal(rows, ref_rows)
     assert int(ws.count_nonzero()) == 0
+
+
+def test_single_row_merge_equals_full_merge():
+    """msa_top16_merge with R = 1 copies a row that is already its own merge
+    (valid ids ascending in front, every forced id, canonical padding) and
+    selects any other: its rows must equal the R = 2 merge of the same row
+    and an all-padding row (the full selection over the same entries), for
+    well-formed rows and for rows with swapped entries, a forced id replaced,
+    non-canonical padding, a hole before the last entry and a repeated id."""
+    rng = np.random.default_rng(2024)
+    T, cols, init, local = 6, 300, 2, 3
+    plane = plane_of(rng, T, cols, "normal")
+    nvp = np.array([cols, 100, 40, 7, 0, cols], dtype=np.int32)
+    _, _, err, rows1, nvp_t = gpu_select(plane, nvp, init, local, 1)
+    assert err == 0
+    rows = rows1.cpu().clone()  # [T, 4, 1, 32] int32: 16 scores then 16 ids
+    sc = rows[:, :, 0, :16].view(torch.float32)
+    ids = rows[:, :, 0, 16:]
+    # token 1: swap two valid entries; token 2: replace the first forced id
+    # (0) by a candidate id; token 3: padding with a finite score; token 5:
+    # a hole (id -1) before the last valid entry, and a repeated id
+    sc[1, 0, [1, 2]] = sc[1, 0, [2, 1]].clone()
+    ids[1, 0, [1, 2]] = ids[1, 0, [2, 1]].clone()
+    ids[2, 1, 0] = 30
+    sc[2, 1, 0] = 9.0
+    last = int((ids[3, 2] >= 0).sum())
+    if last < 16:
+        sc[3, 2, last] = 0.5
+    ids[5, 3, 5] = -1
+    ids[5, 0, 4] = ids[5, 0, 3]
+    single = rows.to(DEV)
+    ms1, mi1, _ = gpu_merge(single, nvp_t, init, local)
+    pad = torch.empty_like(rows)
+    pad[..., :16] = torch.tensor(float("-inf")).view(torch.int32)
+    pad[..., 16:] = -1
+    pair = torch.cat([rows, pad], dim=2).contiguous().to(DEV)
+    ms2, mi2, _ = gpu_merge(pair, nvp_t, init, local)
+    assert np.array_equal(mi1, mi2)
+    assert np.array_equal(ms1.view(np.uint32), ms2.view(np.uint32))
