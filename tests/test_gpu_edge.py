@@ -462,6 +462,62 @@ def test_scorer_latency_mode_large_batch():
     assert int(ws.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("R", [1, 2])
+def test_merge_many_rows_equals_row_per_group(R):
+    """msa_top16_merge over more than 16 384 rows launches several rows per
+    workgroup (one wave each): its rows and error count must equal those of
+    launches over slices of fewer rows, which take one row per workgroup.
+    With R = 1 some rows are malformed (swapped entries, a replaced forced
+    id, a repeated id, non-canonical padding), so both the copy of a row that
+    is already its own merge and the full selection run in the many-row
+    shape."""
+    rng = np.random.default_rng(4242 + R)
+    T, cols, init, local = 4200, 48, 2, 3  # 16 800 rows
+    plane = plane_of(rng, T, cols, "ties" if R == 2 else "normal")
+    nvp = rng.integers(0, cols + 1, size=T).astype(np.int32)
+    _, _, err, rows_d, nvp_t = gpu_select(plane, nvp, init, local, R)
+    assert err == 0
+    rows = rows_d.cpu().clone()
+    if R == 1:
+        sc = rows[:, :, 0, :16].view(torch.float32)
+        ids = rows[:, :, 0, 16:]
+        bad = rng.choice(T, size=300, replace=False)
+        for i, t in enumerate(bad):
+            h = i % 4
+            m = int((ids[t, h] >= 0).sum())
+            kind = i % 4
+            if kind == 0 and m >= 3:
+                sc[t, h, [1, 2]] = sc[t, h, [2, 1]].clone()
+                ids[t, h, [1, 2]] = ids[t, h, [2, 1]].clone()
+            elif kind == 1 and m >= 1:
+                ids[t, h, 0] = cols - 1
+                sc[t, h, 0] = 7.0
+            elif kind == 2 and m >= 2:
+                ids[t, h, 1] = ids[t, h, 0]
+            elif m < 16:
+                sc[t, h, m] = 0.25
+    rows = rows.contiguous().to(DEV)
+    ms, mi, err_all = gpu_merge(rows, nvp_t, init, local)
+    pieces_s, pieces_i, err_pieces = [], [], 0
+    for lo in range(0, T, 1500):  # 6000 rows per launch
+        s_, i_, e_ = gpu_merge(rows[lo:lo + 1500].contiguous(), nvp_t[lo:lo + 1500].contiguous(),
+                               init, local)
+        pieces_s.append(s_)
+        pieces_i.append(i_)
+        err_pieces += e_
+    assert np.array_equal(mi, np.concatenate(pieces_i))
+    assert np.array_equal(ms.view(np.uint32), np.concatenate(pieces_s).view(np.uint32))
+    assert err_all == err_pieces
+    if R == 2:
+        # well-formed input: the merge is the oracle's
+        ps = msa.row_scores(rows.cpu()).numpy()
+        pi = msa.row_ids(rows.cpu()).numpy()
+        os_, oi, missing = oracle.top16_merge(ps, pi, nvp, init_blocks=init, local_blocks=local)
+        assert missing == 0 and err_all == 0
+        assert np.array_equal(mi, oi)
+        assert np.array_equal(ms.view(np.uint32), os_.view(np.uint32))
+
+
 def test_single_row_merge_equals_full_merge():
     """msa_top16_merge with R = 1 copies a row that is already its own merge
     (valid ids ascending in front, every forced id, canonical padding) and
