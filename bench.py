@@ -25,9 +25,10 @@ with a synchronize on both sides (the contract's wall clock brackets the
 same K steps), as a decode loop runs them: step i reads index-K copy
 i % n, the copies standing in for successive layers' caches, with at least
 768 MiB of other copies read between two uses of one copy so that the
-256 MB Infinity Cache holds none of it. 100 untimed back-to-back steps come
-first: the first ~40 after an idle spell run slower while the device
-settles under sustained load. Workloads too small for that (more than 4
+256 MB Infinity Cache holds none of it. 400 untimed back-to-back steps come
+first: after an idle spell the first ~175 run slower (about 105 -> 91 us per
+step at config 5) while the device settles under sustained load, and the
+step then holds steady. Workloads too small for that (more than 4
 copies) time an event pair around each step instead. Beside it, every
 form of the step is also timed with an event pair around each step after a
 read pass over a 1 GiB buffer that evicts index-K (outside the pair; a read,
@@ -70,7 +71,7 @@ PROBE_BIG_BYTES = 4 << 30       # the long streaming-read probe
 PROBE_SHAPES = (2, 4, 8, 16)    # the probe's blocks per wave; the ceiling is the best
 ROTATE_MIN_BYTES = 768 << 20    # other index-K bytes read between two uses of one copy
 MAX_COPIES = 4                  # index-K copies the headline rotates over, at most
-ROTATE_WARMUP_STEPS = 100       # untimed back-to-back steps before the headline's K
+ROTATE_WARMUP_STEPS = 400       # untimed back-to-back steps before the headline's K
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_score_decode_long_b4_s1m.json")
 MFMA_FILE = os.path.join(HERE, "profiles", "mfma_score_decode_long_b4_s1m.json")
@@ -447,10 +448,12 @@ def main():
     rotate = flush is not None and n_copies <= MAX_COPIES
     kcopies = [k] + [k.clone() for _ in range(n_copies - 1)] if rotate else [k]
     if rotate:
-        # Untimed back-to-back steps first. Measured on MI355X, the first ~40
-        # back-to-back steps after an idle or lightly loaded spell run slower
-        # (the scorer 94 -> 83 us over about 3.5 ms) while the device settles
-        # under sustained load; the timed steps start once it has.
+        # Untimed back-to-back steps first. Measured on MI355X at config 5
+        # (events every 25 steps, two trials after 2 s idle): 105, 101-108,
+        # 96-99, 95, 91-93, 90 us per step over the first 150 steps, then
+        # 88.6-89.2 us from about step 175 on, for the 1200 steps measured;
+        # the device settles under sustained load (about 16 ms here). The
+        # timed steps start once it has.
         for i in range(max(args.warmup, ROTATE_WARMUP_STEPS)):
             headline(kk=kcopies[i % n_copies])
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
