@@ -16,8 +16,9 @@ the three-launch chain (score -> select -> merge), the whole-row select
 workspace pool, range rows and merge in the scoring launch). One rank's
 share of the same workload on a cache split by rows over 2 or 4 ranks
 (msa_score_decode_sharded -> msa_top16_select_mapped, then the owner's
-msa_top16_merge_dedup) is reported under e2e.sharded_rank_share, and the
-prefill chain on one 8192-token window under `prefill`.
+msa_top16_merge_dedup) is reported under e2e.sharded_rank_share (steps back
+to back over rotating shard copies, as the headline, and one per event pair),
+and the prefill chain on one 8192-token window under `prefill`.
 
 Inputs are seeded and synthetic (workloads.py) and resident in HBM before
 timing. The headline times K steps back to back between one event pair,
@@ -546,6 +547,32 @@ def main():
             for _ in range(args.warmup):
                 step_rank()
             rank_ms = timed_steps(step_rank, args.steps, stream, flush)
+            # the same step back to back over rotating shard copies, as the
+            # headline times its steps (a rank of a decode loop runs them so)
+            n_shards = -(-ROTATE_MIN_BYTES // shard.numel()) + 1
+            rotate_shards = flush is not None and n_shards <= 2 * MAX_COPIES
+            shards = ([shard] + [shard.clone() for _ in range(n_shards - 1)]
+                      if rotate_shards else [])
+
+            def step_rank_on(kk):
+                msa.msa_score_decode_sharded(q, kk, bt, sl, splane, page_size=w.page_size,
+                                             decode_query_len=w.dql, rank=0, world_size=ws_n,
+                                             errors=errors, stream=stream)
+                msa.msa_top16_select_mapped(splane, nvp, spart, num_ranges=R,
+                                            index_scale=scale, index_offset=offset, **sel)
+
+            rank_btb_ms = None
+            if rotate_shards:
+                for i in range(ROTATE_WARMUP_STEPS):
+                    step_rank_on(shards[i % n_shards])
+                ev_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev_r[0].record(stream)
+                for i in range(args.steps):
+                    step_rank_on(shards[i % n_shards])
+                ev_r[1].record(stream)
+                torch.cuda.synchronize()
+                rank_btb_ms = ev_r[0].elapsed_time(ev_r[1]) / args.steps
+            del shards
             # owner merge of every rank's rows (rank 0's rows stand in for all)
             all_rows = spart.repeat(1, 1, ws_n, 1).contiguous()
             merged = msa.new_rows(T, 4, device=dev)
@@ -578,6 +605,14 @@ def main():
             rank_probe_ms, _ = probe_ms(shard, rank_probe_bytes, args.steps)
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
+                "rank_step_ms_back_to_back": rank_btb_ms,
+                "rank_frac_of_peak_back_to_back":
+                    rank_bytes / (rank_btb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS
+                    if rank_btb_ms else None,
+                "rank_step_timing_back_to_back": (
+                    f"{args.steps} steps back to back between one event pair over "
+                    f"{n_shards} rotating shard copies, after {ROTATE_WARMUP_STEPS} untimed")
+                    if rank_btb_ms else None,
                 "rank_step_ms": rank_mean,
                 "rank_hbm_gbps": rank_bytes / (rank_mean * 1e-3) / 1e9,
                 "rank_frac_of_peak": rank_bytes / (rank_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
