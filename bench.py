@@ -40,7 +40,9 @@ fractions of HBM peak. A further pass records an event between the kernels
 of the three-launch chain for per-kernel times. The roofline figure takes
 the scorer's per-launch duration from K launches back to back between one
 event pair, which leaves out the dispatch delay after each event record
-(that is what the kernel trace measures).
+(that is what the kernel trace measures); they rotate over the same index-K
+copies as the headline, after 400 untimed launches (the scorer alone
+settles over ~300 launches from idle).
 
 Prints one JSON line. `value` is scored keys/s, i.e. the sum of seq_len over
 the mean step time. `roofline` rates the scorer, the dominant kernel, against
@@ -48,9 +50,11 @@ HBM. Its algorithmic bytes are 128 B per key, so 536,870,912 B per launch.
 `roofline.mfma` is the scorer's MFMA work and busy fraction from rocprofv3
 counters (committed under profiles/, valid while the scorer's source hash
 matches). `roofline.stream_read_probe` times msa_stream_read_probe, a plain
-streaming read with no other work, over as many index-K bytes and over
-4 GiB, in the same way and at each of its shapes: the fastest shape at each
-size is the streaming ceiling the scorer's rate is read against. `cpu_baseline` times the oracle on the same workload.
+streaming read with no other work, over as many index-K bytes (the same
+copies, the same warm-up) and over 4 GiB, in the same way and at each of its
+shapes: the fastest shape at each size is the streaming ceiling the
+scorer's rate is read against. `cpu_baseline` times the oracle on the same
+workload.
 """
 from __future__ import annotations
 
@@ -480,7 +484,6 @@ def main():
         timing = ("an event pair around each step, after a read of a 1 GiB buffer that "
                   "evicts index-K from the Infinity Cache" if flush is not None else
                   "an event pair around each step (no eviction)")
-    del kcopies
 
     # Timed region 1b: the other forms of the step, timed the same way.
     alt = {}
@@ -497,25 +500,29 @@ def main():
 
     sink = torch.zeros(msa.STREAM_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
 
-    def probe_shape_ms(buf, nbytes, launches, bpw):
-        """msa_stream_read_probe over nbytes of buf, bpw blocks per wave: K
-        launches back to back between one event pair, after a cache-evicting
-        read."""
-        msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, blocks_per_wave=bpw, stream=stream)
-        if flush is not None:
+    def probe_shape_ms(bufs, nbytes, launches, bpw, warm):
+        """msa_stream_read_probe over nbytes, bpw blocks per wave: `warm`
+        untimed launches, then K launches back to back between one event
+        pair, launch i reading bufs[i % len(bufs)] (a cache-evicting read
+        first when there is one buffer)."""
+        for i in range(warm):
+            msa.msa_stream_read_probe(bufs[i % len(bufs)], sink, nbytes=nbytes,
+                                      blocks_per_wave=bpw, stream=stream)
+        if flush is not None and len(bufs) == 1:
             flush.sum()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(launches):
-            msa.msa_stream_read_probe(buf, sink, nbytes=nbytes, blocks_per_wave=bpw,
-                                      stream=stream)
+        for i in range(launches):
+            msa.msa_stream_read_probe(bufs[i % len(bufs)], sink, nbytes=nbytes,
+                                      blocks_per_wave=bpw, stream=stream)
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / launches
 
-    def probe_ms(buf, nbytes, launches):
+    def probe_ms(bufs, nbytes, launches, warm=1):
         """The fastest probe shape's launch time, and every shape's."""
-        shapes = {bpw: probe_shape_ms(buf, nbytes, launches, bpw) for bpw in PROBE_SHAPES}
+        shapes = {bpw: probe_shape_ms(bufs, nbytes, launches, bpw, warm)
+                  for bpw in PROBE_SHAPES}
         return min(shapes.values()), shapes
 
     # Timed region 1d: one rank's share of the same workload on a cache whose
@@ -602,7 +609,7 @@ def main():
             torch.cuda.synchronize()
             rank_score_ms = ev_s[0].elapsed_time(ev_s[1]) / args.steps
             rank_probe_bytes = min(rank_bytes, shard.numel()) // 16384 * 16384
-            rank_probe_ms, _ = probe_ms(shard, rank_probe_bytes, args.steps)
+            rank_probe_ms, _ = probe_ms([shard], rank_probe_bytes, args.steps)
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
                 "rank_step_ms_back_to_back": rank_btb_ms,
@@ -635,30 +642,38 @@ def main():
         step_three(events[i])
     torch.cuda.synchronize()
     # Timed region 3: the scorer alone, K launches back to back between one
-    # event pair (a cache-evicting read first), for its per-launch duration
-    # without the dispatch delay that follows each event record. Launches
-    # stream 537 MB each through a 256 MB Infinity Cache with non-temporal
-    # loads, so a launch finds little of the previous one's data resident.
+    # event pair, for its per-launch duration without the dispatch delay that
+    # follows each event record. Where the headline rotates index-K copies,
+    # so does this, after ROTATE_WARMUP_STEPS untimed launches: measured at
+    # config 5 from idle (events every 25 launches), the scorer alone takes
+    # about 300 launches to settle (98 -> 82.4 us per launch). Otherwise the
+    # launches follow a cache-evicting read.
     print(f"[bench] timing {args.steps} back-to-back scorer launches", file=sys.stderr,
           flush=True)
-    if flush is not None:
+    n_rot = len(kcopies)
+    if rotate:
+        for i in range(ROTATE_WARMUP_STEPS):
+            score(kcopies[i % n_rot])
+    elif flush is not None:
         flush.sum()
     b2b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     b2b[0].record(stream)
-    for _ in range(args.steps):
-        score()
+    for i in range(args.steps):
+        score(kcopies[i % n_rot])
     b2b[1].record(stream)
     torch.cuda.synchronize()
     score_b2b_ms = b2b[0].elapsed_time(b2b[1]) / args.steps
     # Timed region 3b: the streaming-read probe (a plain read, no other work)
-    # over as many index-K bytes, timed the same way, and over 4 GiB (where
-    # the launch's ramp and tail weigh least): the streaming ceilings the
-    # scorer's rate is read against.
+    # over as many index-K bytes, timed the same way (the same copies, the same
+    # warm-up), and over 4 GiB (where the launch's ramp and tail weigh least):
+    # the streaming ceilings the scorer's rate is read against.
     probe_bytes = max(16384, launch_bytes // 16384 * 16384)
     probe_bytes = min(probe_bytes, k.numel() // 16384 * 16384)
-    probe_launch_ms, probe_shapes = probe_ms(k, probe_bytes, args.steps)
+    probe_launch_ms, probe_shapes = probe_ms(kcopies, probe_bytes, args.steps,
+                                             ROTATE_WARMUP_STEPS if rotate else 1)
+    del kcopies
     big = torch.empty(PROBE_BIG_BYTES, dtype=torch.uint8, device=dev)
-    big_ms, big_shapes = probe_ms(big, PROBE_BIG_BYTES, 10)
+    big_ms, big_shapes = probe_ms([big], PROBE_BIG_BYTES, 10, 2)
     del big
     if int(errors.item()) != 0:
         raise RuntimeError(f"device error counter = {int(errors.item())}")
@@ -728,13 +743,18 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": launch_bytes,
                      "launch_ms": score_b2b_ms,
-                     "launch_ms_source": "K scorer launches back to back between one event pair",
+                     "launch_ms_source": (
+                         "K scorer launches back to back between one event pair" +
+                         (f", launch i on index-K copy i % {n_copies}, after "
+                          f"{ROTATE_WARMUP_STEPS} untimed" if rotate else
+                          ", after a cache-evicting read")),
                      "traffic": None if traffic is None else traffic["total_bytes"],
                      "traffic_detail": traffic,
                      "mfma": load_mfma(),
                      "stream_read_probe": {
                          "what": "msa_stream_read_probe, a plain streaming read with no other "
-                                 "work, launches back to back between one event pair; the "
+                                 "work, launches back to back between one event pair (over "
+                                 "as many bytes: the scorer's copies and warm-up); the "
                                  "fastest of its shapes (16 KiB blocks per wave) at each size",
                          "same_bytes": {"bytes": probe_bytes, "launch_ms": probe_launch_ms,
                                         "achieved": probe_gbps,
