@@ -192,23 +192,45 @@ __device__ __forceinline__ int split_slot()
     return (i % kXcds) * (grid / kXcds) + i / kXcds;
 }
 
-__device__ __forceinline__ int wave_sum(int v)
+// Wave-wide sum and inclusive prefix sum on the VALU alone (the lane
+// exchanges of topk::lane_xor: DPP and permlane swaps, no LDS round trip).
+// They sit on every wave's path to its first index-K load, where a shuffle
+// through ds_bpermute cost an LDS round trip and a wait per step.
+__device__ __forceinline__ int wave_sum(int v, int lane)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v += __shfl_xor(v, off);
+    v += (int)topk::lane_xor<1>((uint32_t)v, lane);
+    v += (int)topk::lane_xor<2>((uint32_t)v, lane);
+    v += (int)topk::lane_xor<4>((uint32_t)v, lane);
+    v += (int)topk::lane_xor<8>((uint32_t)v, lane);
+    v += (int)topk::lane_xor<16>((uint32_t)v, lane);
+    v += (int)topk::lane_xor<32>((uint32_t)v, lane);
     return v;
+}
+
+// Butterfly prefix sum: before the step with partner distance j, `total` is
+// the sum over the aligned block of j lanes holding this lane and `prefix`
+// the sum over that block's lanes up to this one; the partner block (lanes
+// ^ j) holds the other half of the aligned 2j-lane block, and it precedes
+// this lane's half when bit j of the lane is set.
+template <int J>
+__device__ __forceinline__ void scan_step(int& prefix, int& total, int lane)
+{
+    const int o = (int)topk::lane_xor<J>((uint32_t)total, lane);
+    if (lane & J)
+        prefix += o;
+    total += o;
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off)
-            v += o;
-    }
-    return v;
+    int prefix = v, total = v;
+    scan_step<1>(prefix, total, lane);
+    scan_step<2>(prefix, total, lane);
+    scan_step<4>(prefix, total, lane);
+    scan_step<8>(prefix, total, lane);
+    scan_step<16>(prefix, total, lane);
+    scan_step<32>(prefix, total, lane);
+    return prefix;
 }
 
 // Where a plane column's keys are.
@@ -471,20 +493,24 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
     int64_t g_lo, g_hi;
     int b = 0;
     int64_t base = 0;
+    // batch <= 64: lane b holds seq_lens[b], and each request's length is
+    // taken from it (seq_next; -1: load it)
+    const int seq_lane = p.batch <= 64 && lane < p.batch ? p.seq_lens[lane] : 0;
+    int seq_next = -1;
     if (p.batch <= 64) {
         bool clamped;
-        const int gb = lane < p.batch
-                           ? written_cols(p.seq_lens[lane], p.cols, clamped, gm.col_stride) / kUnit
-                           : 0;
+        const int gb = lane < p.batch ? written_cols(seq_lane, p.cols, clamped, gm.col_stride) / kUnit
+                                      : 0;
         const int incl = wave_inclusive_scan(gb, lane);
-        const int64_t total = __shfl(incl, 63);
+        const int64_t total = __builtin_amdgcn_readlane(incl, 63);
         g_lo = total * (int64_t)slot / gridDim.x;
         g_hi = total * ((int64_t)slot + 1) / gridDim.x;
         if (g_lo >= g_hi)
             return;
         const int l = __ffsll((unsigned long long)__ballot(incl > g_lo)) - 1;
         b = l;
-        base = __shfl(incl - gb, l);
+        base = __builtin_amdgcn_readlane(incl - gb, l);
+        seq_next = __builtin_amdgcn_readlane(seq_lane, l);
     } else {
         int64_t total = 0;
         for (int b0 = 0; b0 < p.batch; b0 += 64) {
@@ -493,7 +519,7 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
             const int gb = bb < p.batch
                                ? written_cols(p.seq_lens[bb], p.cols, clamped, gm.col_stride) / kUnit
                                : 0;
-            total += wave_sum(gb);
+            total += wave_sum(gb, lane);
         }
         g_lo = total * (int64_t)slot / gridDim.x;
         g_hi = total * ((int64_t)slot + 1) / gridDim.x;
@@ -506,11 +532,11 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
                                ? written_cols(p.seq_lens[bb], p.cols, clamped, gm.col_stride) / kUnit
                                : 0;
             const int incl = wave_inclusive_scan(gb, lane);
-            const int chunk_total = __shfl(incl, 63);
+            const int chunk_total = __builtin_amdgcn_readlane(incl, 63);
             if (base + chunk_total > g_lo) {
                 const int l = __ffsll((unsigned long long)__ballot(base + incl > g_lo)) - 1;
                 b = b0 + l;
-                base += __shfl(incl - gb, l);
+                base += __builtin_amdgcn_readlane(incl - gb, l);
                 break;
             }
             base += chunk_total;
@@ -519,11 +545,14 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
 
     int64_t gcur = g_lo;
     while (gcur < g_hi) {
-        const int seq = p.seq_lens[b];
+        const int seq = seq_next >= 0 ? seq_next : p.seq_lens[b];
+        seq_next = -1;
         bool clamped;
         const int wcols = written_cols(seq, p.cols, clamped, gm.col_stride);
         if (wcols == 0) {  // requests with no columns own no groups
             ++b;
+            if (p.batch <= 64 && b < p.batch)
+                seq_next = __builtin_amdgcn_readlane(seq_lane, b);
             continue;
         }
         if (clamped && gcur == base && lane == 0 && p.errors)
@@ -567,6 +596,8 @@ __device__ __forceinline__ void score_wave_range(const ScoreParams& p, uint8_t* 
         gcur = min(g_hi, g_end_b);
         base = g_end_b;
         ++b;
+        if (p.batch <= 64 && b < p.batch)
+            seq_next = __builtin_amdgcn_readlane(seq_lane, b);
     }
 }
 
