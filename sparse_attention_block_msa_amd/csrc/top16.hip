@@ -28,25 +28,34 @@ namespace {
 
 using namespace topk;
 
-template <int V, int NW>
+// One workgroup per (row, range): blockIdx.x = t * 4 + h, blockIdx.y = the
+// range, so no integer division splits the job index. kMapped: column c
+// stands for global id index_scale * c + index_offset
+// (msa_top16_select_mapped); otherwise c is id c and the id arithmetic folds
+// at compile time (with the scale read at run time, the interval bounds
+// cost three integer divisions, dependent chains of about 30 instructions
+// each, at the head of every select).
+template <int V, int NW, bool kMapped>
 __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
 {
     __shared__ msa_top16_row part[NW];
     __shared__ CandBuf cand[NW];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t job = blockIdx.x;  // ((t * 4) + h) * R + r
-    const int r = (int)(job % p.num_ranges);
-    const int64_t th = job / p.num_ranges;
+    const int r = (int)blockIdx.y;
+    const int64_t th = blockIdx.x;
+    const int64_t job = th * p.num_ranges + r;  // the output row ((t * 4) + h) * R + r
     const int t = (int)(th / kHeads);
     const int lo = r * p.width;
     const int span_lo = lo + wave * (V * 64);
     float sv[V];
     load_span<V>(p.scores + th * p.cols, p.cols, span_lo, lane, sv);
 
+    const int scale = kMapped ? p.index_scale : 1;
+    const int offset = kMapped ? p.index_offset : 0;
     // valid global ids: [0, n); the largest this plane can name is
     // index_scale * (cols - 1) + index_offset
-    const int64_t n_max = (int64_t)p.index_scale * p.cols + p.index_offset;
+    const int64_t n_max = (int64_t)scale * p.cols + offset;
     int n = p.nvp[t];
     if (n < 0 || n > n_max) {
         if (r == 0 && (th % kHeads) == 0 && threadIdx.x == 0 && p.errors)
@@ -54,8 +63,7 @@ __global__ __launch_bounds__(NW * 64) void top16_select_kernel(SelectParams p)
         n = n < 0 ? 0 : (int)n_max;
     }
     const int hi = min(lo + p.width, p.cols);
-    const ColumnIds ci = column_ids(n, p.init_blocks, p.local_blocks, p.index_scale,
-                                    p.index_offset);
+    const ColumnIds ci = column_ids(n, p.init_blocks, p.local_blocks, scale, offset);
     msa_top16_row* dst = NW == 1 ? p.out + job : &part[wave];
     select_loaded<V>(sv, span_lo, hi, ci, dst, lane, &cand[wave]);
 
@@ -689,10 +697,13 @@ Shape pick_shape(int64_t span)
 template <int V, int NW>
 hipError_t launch_select_shape(const SelectParams& p, hipStream_t stream)
 {
-    const int64_t jobs = (int64_t)p.num_tokens * kHeads * p.num_ranges;
+    const int64_t rows = (int64_t)p.num_tokens * kHeads;
+    const bool mapped = p.index_scale != 1 || p.index_offset != 0;
+    const void* fn = mapped ? reinterpret_cast<const void*>(&top16_select_kernel<V, NW, true>)
+                            : reinterpret_cast<const void*>(&top16_select_kernel<V, NW, false>);
     void* args[] = {const_cast<SelectParams*>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&top16_select_kernel<V, NW>),
-                           dim3((unsigned)jobs), dim3(NW * 64), args, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)rows, (unsigned)p.num_ranges), dim3(NW * 64), args,
+                           0, stream);
 }
 
 template <int V, int NW>
@@ -820,7 +831,11 @@ hipError_t warmup_top16_kernels()
     hipError_t e = hipSuccess;
 #define X(V, NW)                                                                                  \
     if (e == hipSuccess)                                                                          \
-        e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_select_kernel<V, NW>)); \
+        e = hipFuncGetAttributes(&attr,                                                           \
+                                 reinterpret_cast<const void*>(&top16_select_kernel<V, NW, false>)); \
+    if (e == hipSuccess)                                                                          \
+        e = hipFuncGetAttributes(&attr,                                                           \
+                                 reinterpret_cast<const void*>(&top16_select_kernel<V, NW, true>)); \
     if (e == hipSuccess)                                                                          \
         e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&top16_merge_kernel<V, NW>));
     MSA_FOR_EACH_SHAPE(X)
