@@ -900,13 +900,21 @@ const void* score_latency_kernel_fn()
         &score_decode_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, 1, false>);
 }
 
+// Waves per SIMD a streaming instance of the fused kernel is built for (its
+// register budget). 32 values per lane do not fit the 3-waves-per-SIMD budget
+// of the 16-row scorer (spills), so that instance takes the 2-wave budget;
+// its grid is sized the same way, so that every wave of it is resident at
+// once (a grid sized for 3 waves per SIMD ran its last third as a second
+// round: 94 us against 82 us at the 2048-column workload).
+constexpr int score_select_waves_per_simd(int nt, int v)
+{
+    return nt == 1 ? (v >= 32 ? 2 : MSA_SCORE_REG_WAVES_16) : MSA_SCORE_REG_WAVES_32;
+}
+
 template <int NT, int V, bool kLatency>
 const void* score_select_kernel_fn()
 {
-    // 32 values per lane do not fit the 3-waves-per-SIMD register budget of
-    // the 16-row scorer (spills): that instance takes the 2-wave budget
-    constexpr int kRegWaves = NT == 1 ? (V >= 32 ? 2 : MSA_SCORE_REG_WAVES_16)
-                                      : MSA_SCORE_REG_WAVES_32;
+    constexpr int kRegWaves = score_select_waves_per_simd(NT, V);
     if constexpr (kLatency)  // one column per wave, a block per DMA round trip
         return reinterpret_cast<const void*>(
             &score_select_kernel<NT, 1, MSA_SCORE_LATENCY_WAVES_PER_SIMD, V, 1>);
@@ -988,7 +996,10 @@ hipError_t launch_score_select(const ScoreSelectParams& q, hipStream_t stream)
 #undef X
     if (fn == nullptr)
         return hipErrorInvalidValue;
-    const int64_t grid = latency ? max_cols : score_grid(q.score);
+    const int64_t groups = (int64_t)q.score.batch * (q.score.cols / 4);
+    const int64_t grid =
+        latency ? max_cols
+                : std::min(groups, (int64_t)device_cus() * 4 * score_select_waves_per_simd(nt, v));
     // Helpers wait for ranges; at most half of the waves the device holds at
     // once may, so that the rest of the grid always finds slots.
     int per_cu = 0;
