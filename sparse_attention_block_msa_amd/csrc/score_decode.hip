@@ -905,7 +905,7 @@ const void* score_latency_kernel_fn()
 // of the 16-row scorer (spills), so that instance takes the 2-wave budget;
 // its grid is sized the same way, so that every wave of it is resident at
 // once (a grid sized for 3 waves per SIMD ran its last third as a second
-// round: 94 us against 82 us at the 2048-column workload).
+// round: 92 us against 77 us per step at the 2048-column workload).
 constexpr int score_select_waves_per_simd(int nt, int v)
 {
     return nt == 1 ? (v >= 32 ? 2 : MSA_SCORE_REG_WAVES_16) : MSA_SCORE_REG_WAVES_32;
