@@ -579,7 +579,6 @@ def main():
                 ev_r[1].record(stream)
                 torch.cuda.synchronize()
                 rank_btb_ms = ev_r[0].elapsed_time(ev_r[1]) / args.steps
-            del shards
             # owner merge of every rank's rows (rank 0's rows stand in for all)
             all_rows = spart.repeat(1, 1, ws_n, 1).contiguous()
             merged = msa.new_rows(T, 4, device=dev)
@@ -596,20 +595,38 @@ def main():
             rank_mean = sum(rank_ms) / len(rank_ms)
             rank_bytes = rank_keys * 128
             # the rank's scorer alone, back to back, against a plain read of
-            # as many bytes (the ceiling at this size, ramp and tail included)
-            if flush is not None:
+            # as many bytes (the ceiling at this size, ramp and tail included),
+            # both over the rotating shard copies after the same warm-up when
+            # there are copies (one shard alone would sit in the Infinity
+            # Cache), else after a cache-evicting read
+            rank_bufs = shards if rotate_shards else [shard]
+
+            def rank_score_on(kk):
+                msa.msa_score_decode_sharded(q, kk, bt, sl, splane, page_size=w.page_size,
+                                             decode_query_len=w.dql, rank=0, world_size=ws_n,
+                                             errors=errors, stream=stream)
+
+            if rotate_shards:
+                for i in range(ROTATE_WARMUP_STEPS):
+                    rank_score_on(rank_bufs[i % len(rank_bufs)])
+            elif flush is not None:
                 flush.sum()
             ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev_s[0].record(stream)
-            for _ in range(args.steps):
-                msa.msa_score_decode_sharded(q, shard, bt, sl, splane, page_size=w.page_size,
-                                             decode_query_len=w.dql, rank=0, world_size=ws_n,
-                                             errors=errors, stream=stream)
+            for i in range(args.steps):
+                rank_score_on(rank_bufs[i % len(rank_bufs)])
             ev_s[1].record(stream)
             torch.cuda.synchronize()
             rank_score_ms = ev_s[0].elapsed_time(ev_s[1]) / args.steps
             rank_probe_bytes = min(rank_bytes, shard.numel()) // 16384 * 16384
-            rank_probe_ms, _ = probe_ms([shard], rank_probe_bytes, args.steps)
+            rank_probe_ms, _ = probe_ms(rank_bufs, rank_probe_bytes, args.steps,
+                                        ROTATE_WARMUP_STEPS if rotate_shards else 1)
+            rank_score_timing = (
+                f"{args.steps} launches back to back between one event pair over "
+                f"{len(rank_bufs)} rotating shard copies, after {ROTATE_WARMUP_STEPS} untimed"
+                if rotate_shards else
+                f"{args.steps} launches back to back after a cache-evicting read")
+            del shards, rank_bufs
             sharded[f"world_size_{ws_n}"] = {
                 "rank": 0, "rank_keys": rank_keys,
                 "rank_step_ms_back_to_back": rank_btb_ms,
@@ -624,6 +641,7 @@ def main():
                 "rank_hbm_gbps": rank_bytes / (rank_mean * 1e-3) / 1e9,
                 "rank_frac_of_peak": rank_bytes / (rank_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "rank_scorer_ms_back_to_back": rank_score_ms,
+                "rank_scorer_timing": rank_score_timing,
                 "rank_scorer_hbm_gbps": rank_bytes / (rank_score_ms * 1e-3) / 1e9,
                 "stream_read_probe_same_bytes_ms": rank_probe_ms,
                 "rank_scorer_frac_of_probe":

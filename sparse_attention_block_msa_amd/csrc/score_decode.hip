@@ -876,18 +876,15 @@ const void* score_kernel_fn()
     return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, false>);
 }
 
-// Row-sharded cache: one rank's share, streaming grid. A shard column of 64
-// or 128 rows is staged in 64-row pieces (kShardParts = 2), a 32-row one in
-// 32-row pieces.
-#ifndef MSA_SCORE_SHARD_WIDE_PARTS
-#define MSA_SCORE_SHARD_WIDE_PARTS 2
-#endif
-template <int NT, int kShardParts>
+// Row-sharded cache: one rank's share, streaming grid, its shard columns
+// (32, 64 or 128 rows) staged in the same 32-row pieces as whole blocks.
+// Measured over rotating shard copies of the 4 x 1 Mi-key cache, 64-row
+// pieces took 44.5 / 25.1 us at world sizes 2 / 4 against 43.8 / 24.8 us.
+template <int NT>
 const void* score_sharded_kernel_fn()
 {
     constexpr int kRegWaves = NT == 1 ? MSA_SCORE_REG_WAVES_16 : MSA_SCORE_REG_WAVES_32;
-    return reinterpret_cast<const void*>(
-        &score_decode_kernel<NT, kShardParts, kRegWaves, 4, true>);
+    return reinterpret_cast<const void*>(&score_decode_kernel<NT, kParts, kRegWaves, 4, true>);
 }
 
 // Small batches: one column per work unit and a whole block per DMA round
@@ -956,11 +953,7 @@ hipError_t launch_score_decode(const ScoreParams& p, hipStream_t stream)
     void* args[] = {const_cast<ScoreParams*>(&p)};
     const bool small_q = p.dql * kHeads <= 16;
     if (p.world_size > 1) {
-        const bool wide = (p.page_size / p.world_size) % (kBlockTokens / MSA_SCORE_SHARD_WIDE_PARTS) == 0;
-        const void* fn =
-            wide ? (small_q ? score_sharded_kernel_fn<1, MSA_SCORE_SHARD_WIDE_PARTS>()
-                            : score_sharded_kernel_fn<2, MSA_SCORE_SHARD_WIDE_PARTS>())
-                 : (small_q ? score_sharded_kernel_fn<1, 4>() : score_sharded_kernel_fn<2, 4>());
+        const void* fn = small_q ? score_sharded_kernel_fn<1>() : score_sharded_kernel_fn<2>();
         return hipLaunchKernel(fn, dim3((unsigned)score_grid(p)), dim3(64), args, 0, stream);
     }
     const int64_t max_cols = (int64_t)p.batch * p.cols;
@@ -1023,13 +1016,9 @@ hipError_t warmup_score_kernels()
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_kernel_fn<2>());
     if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1, 4>());
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1>());
     if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2, 4>());
-    if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<1, MSA_SCORE_SHARD_WIDE_PARTS>());
-    if (e == hipSuccess)
-        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2, MSA_SCORE_SHARD_WIDE_PARTS>());
+        e = hipFuncGetAttributes(&attr, score_sharded_kernel_fn<2>());
     if (e == hipSuccess)
         e = hipFuncGetAttributes(&attr, score_latency_kernel_fn<1>());
     if (e == hipSuccess)
