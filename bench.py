@@ -73,7 +73,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 FLUSH_BYTES = 1 << 30           # read before each step; > 256 MB Infinity Cache
 COPY_BYTES = 512 << 20          # calibration copy: reads and writes this many bytes
 PROBE_BIG_BYTES = 4 << 30       # the long streaming-read probe
-PROBE_SHAPES = (2, 4, 8, 16)    # the probe's blocks per wave; the ceiling is the best
+PROBE_SHAPES = (0, 2, 4, 8, 16)  # the probe's shapes (0: persistent); the ceiling is the best
 ROTATE_MIN_BYTES = 768 << 20    # other index-K bytes read between two uses of one copy
 MAX_COPIES = 4                  # index-K copies the headline rotates over, at most
 ROTATE_WARMUP_STEPS = 400       # untimed back-to-back steps before the headline's K
@@ -521,8 +521,8 @@ def main():
 
     def probe_ms(bufs, nbytes, launches, warm=1):
         """The fastest probe shape's launch time, and every shape's."""
-        shapes = {bpw: probe_shape_ms(bufs, nbytes, launches, bpw, warm)
-                  for bpw in PROBE_SHAPES}
+        shapes = {("persistent" if bpw == msa.STREAM_PROBE_PERSISTENT else bpw):
+                  probe_shape_ms(bufs, nbytes, launches, bpw, warm) for bpw in PROBE_SHAPES}
         return min(shapes.values()), shapes
 
     # Timed region 1d: one rank's share of the same workload on a cache whose
@@ -773,15 +773,17 @@ def main():
                          "what": "msa_stream_read_probe, a plain streaming read with no other "
                                  "work, launches back to back between one event pair (over "
                                  "as many bytes: the scorer's copies and warm-up); the "
-                                 "fastest of its shapes (16 KiB blocks per wave) at each size",
+                                 "fastest of its shapes at each size (persistent: one "
+                                 "contiguous run per wave, one wave per SIMD; 2-16: that "
+                                 "many 16 KiB blocks per wave over a grid covering the buffer)",
                          "same_bytes": {"bytes": probe_bytes, "launch_ms": probe_launch_ms,
                                         "achieved": probe_gbps,
                                         "frac_of_peak": probe_gbps / HBM_PEAK_GBPS,
-                                        "launch_ms_by_blocks_per_wave": probe_shapes},
+                                        "launch_ms_by_shape": probe_shapes},
                          "4_gib": {"bytes": PROBE_BIG_BYTES, "launch_ms": big_ms,
                                    "achieved": big_gbps,
                                    "frac_of_peak": big_gbps / HBM_PEAK_GBPS,
-                                   "launch_ms_by_blocks_per_wave": big_shapes},
+                                   "launch_ms_by_shape": big_shapes},
                          "scorer_frac_of_probe_same_bytes": achieved / probe_gbps,
                          "scorer_frac_of_probe_4_gib": achieved / big_gbps}},
         "prefill": prefill,

@@ -66,6 +66,7 @@ extern "C" {
 #define MSA_MAX_SELECT_COLS 12287 /* select scores: 0 < K < 12288                          */
 #define MSA_MAX_RANGES 768       /* column ranges per row (16 * 768 = 12288 merge entries) */
 #define MSA_STREAM_PROBE_SINK_WORDS 1024   /* uint32 words of msa_stream_read_probe's sink */
+#define MSA_STREAM_PROBE_PERSISTENT 0      /* msa_stream_read_probe's persistent shape     */
 #define MSA_PREFILL_WINDOW_TOKENS 64       /* query tokens per prefill window              */
 #define MSA_PREFILL_PLAN_HEADER_WORDS 8    /* int32 words before a prefill plan's items    */
 #define MSA_PREFILL_ITEM_WORDS 8           /* int32 words per prefill plan item            */
@@ -463,9 +464,15 @@ int msa_warmup(void);
  * a buffer large enough that a launch's ramp and tail weigh little.
  *
  * src              device, 16-byte aligned; bytes a positive multiple of 16384.
- * blocks_per_wave  2, 4, 8 or 16: consecutive 16 KiB blocks each wave reads.
- *                  The fastest shape depends on the size (measured: 2 on
- *                  512 MiB, 16 on 4 GiB), so a ceiling is the best of them.
+ * blocks_per_wave  the read's shape:
+ *                  MSA_STREAM_PROBE_PERSISTENT (0): a grid of one wave per
+ *                    SIMD of the device, each wave reading one contiguous run
+ *                    of blocks, one block in flight;
+ *                  2, 4, 8 or 16: a grid that covers the buffer at once, each
+ *                    wave reading that many consecutive 16 KiB blocks.
+ *                  The fastest shape depends on the size and the device, so
+ *                  a ceiling is the best of them (measured on MI355X: the
+ *                  persistent shape at 512 MiB and at 4 GiB).
  * sink             device uint32[MSA_STREAM_PROBE_SINK_WORDS]. The probe xors
  *                  every dword of the buffer into these words (each wave's
  *                  share into one of them), so a caller that zeroes them

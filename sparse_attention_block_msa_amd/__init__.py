@@ -34,6 +34,7 @@ TOPK = 16
 ROW_WORDS = 32  # one Top16 row: 16 float32 scores then 16 int32 ids (128 bytes)
 
 STREAM_PROBE_SINK_WORDS = 1024  # MSA_STREAM_PROBE_SINK_WORDS
+STREAM_PROBE_PERSISTENT = 0     # MSA_STREAM_PROBE_PERSISTENT
 
 EXPORTS = ("msa_score_decode", "msa_score_decode_sharded", "msa_score_select",
            "msa_top16_select", "msa_top16_select_mapped", "msa_top16_merge_dedup", "msa_top16_merge", "msa_top16_select_merge",
@@ -194,7 +195,8 @@ def msa_stream_read_probe(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int 
                           blocks_per_wave: int = 2, stream=None) -> None:
     """Measurement aid: a plain streaming read of the first `nbytes` (default
     all) of the contiguous device tensor `src`, `blocks_per_wave` (2, 4, 8 or
-    16) consecutive 16 KiB blocks per wave, xoring every dword into the words
+    16) consecutive 16 KiB blocks per wave, or STREAM_PROBE_PERSISTENT (one
+    contiguous run per wave, one wave per SIMD), xoring every dword into the words
     of `sink` (int32 [>= 1024] on the device; the xor of its words is the xor
     of the bytes read)."""
     _dev(src, sink)

@@ -529,9 +529,10 @@ int msa_stream_read_probe(const void* src, int64_t bytes, int32_t blocks_per_wav
     MSA_CHECK(bytes > 0 && bytes % msa::kProbeBlockBytes == 0,
               "%s: bytes (%lld) must be a positive multiple of %lld", fn, (long long)bytes,
               (long long)msa::kProbeBlockBytes);
-    MSA_CHECK(blocks_per_wave == 2 || blocks_per_wave == 4 || blocks_per_wave == 8 ||
-                  blocks_per_wave == 16,
-              "%s: blocks_per_wave (%d) must be 2, 4, 8 or 16", fn, (int)blocks_per_wave);
+    MSA_CHECK(blocks_per_wave == MSA_STREAM_PROBE_PERSISTENT || blocks_per_wave == 2 ||
+                  blocks_per_wave == 4 || blocks_per_wave == 8 || blocks_per_wave == 16,
+              "%s: blocks_per_wave (%d) must be %d (persistent), 2, 4, 8 or 16", fn,
+              (int)blocks_per_wave, MSA_STREAM_PROBE_PERSISTENT);
     return launch_result(msa::launch_stream_read_probe(static_cast<const uint8_t*>(src),
                                                        bytes / msa::kProbeBlockBytes,
                                                        blocks_per_wave, sink, stream),

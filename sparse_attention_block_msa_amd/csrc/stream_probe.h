@@ -14,10 +14,11 @@ constexpr int64_t kProbeBlockBytes = 16384;  // one B128 block of index-K rows
 constexpr int kProbeSinkWords = MSA_STREAM_PROBE_SINK_WORDS;
 
 // Reads `blocks` contiguous 16 KiB blocks of src, blocks_per_wave (2, 4, 8
-// or 16; anything else: hipErrorInvalidValue) consecutive ones per wave, and
-// xors every dword of them into sink[0 .. kProbeSinkWords): wave w's share
-// goes to word w % kProbeSinkWords, so that no single word takes every
-// wave's atomic.
+// or 16) consecutive ones per wave, or with MSA_STREAM_PROBE_PERSISTENT one
+// contiguous run per wave of a grid of one wave per SIMD (anything else:
+// hipErrorInvalidValue), and xors every dword of them into sink[0 ..
+// kProbeSinkWords): wave w's share goes to word w % kProbeSinkWords, so that
+// no single word takes every wave's atomic.
 hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, int blocks_per_wave,
                                     uint32_t* sink, hipStream_t stream);
 

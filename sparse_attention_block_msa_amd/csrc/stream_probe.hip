@@ -52,11 +52,59 @@ void stream_read_probe_kernel(const uint8_t* src, int64_t blocks, uint32_t* sink
         atomicXor(sink + wave % kProbeSinkWords, acc);
 }
 
+// Persistent shape: a grid of one wave per SIMD, wave w reading blocks
+// [w * per, (w + 1) * per), one block in flight (its sixteen loads all issued
+// before any is consumed). Measured on MI355X, launches back to back over
+// three rotating 512 MiB buffers: 78.7-80.2 us against 82.4-82.9 us for the
+// same loop with two waves per SIMD, and 4 GiB at about 7.0 TB/s: fewer
+// concurrent streams of the same depth read faster.
+__global__ __launch_bounds__(64 * kProbeWavesPerGroup)
+void stream_read_probe_persistent_kernel(const uint8_t* src, int64_t blocks, int64_t per,
+                                         uint32_t* sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * kProbeWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t lo = wave * per;
+    const int64_t hi = lo + per < blocks ? lo + per : blocks;
+    uint32_t acc = 0;
+    for (int64_t b = lo; b < hi; ++b) {
+        const uint8_t* block = src + b * kProbeBlockBytes;
+        probe_v4i v[kProbeBlockBytes / 1024];
+#pragma unroll
+        for (int t = 0; t < (int)(kProbeBlockBytes / 1024); ++t)
+            v[t] = __builtin_nontemporal_load(
+                reinterpret_cast<const probe_v4i*>(block + t * 1024 + lane * 16));
+        __builtin_amdgcn_sched_barrier(0);  // every load of the block issued first
+#pragma unroll
+        for (int t = 0; t < (int)(kProbeBlockBytes / 1024); ++t)
+            acc ^= (uint32_t)(v[t].x ^ v[t].y ^ v[t].z ^ v[t].w);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        acc ^= (uint32_t)__shfl_xor((int)acc, off);
+    if (lane == 0 && lo < hi)
+        atomicXor(sink + wave % kProbeSinkWords, acc);
+}
+
 }  // namespace
 
 hipError_t launch_stream_read_probe(const uint8_t* src, int64_t blocks, int blocks_per_wave,
                                     uint32_t* sink, hipStream_t stream)
 {
+    if (blocks_per_wave == MSA_STREAM_PROBE_PERSISTENT) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        const int64_t waves = (int64_t)cus * 4;  // one per SIMD: groups of four, one per CU
+        int64_t per = (blocks + waves - 1) / waves;
+        void* args[] = {&src, &blocks, &per, &sink};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&stream_read_probe_persistent_kernel),
+                               dim3((unsigned)cus), dim3(64 * kProbeWavesPerGroup), args, 0,
+                               stream);
+    }
     const void* fn = nullptr;
     switch (blocks_per_wave) {
     case 2: fn = reinterpret_cast<const void*>(&stream_read_probe_kernel<2>); break;

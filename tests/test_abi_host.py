@@ -305,7 +305,8 @@ def test_merge_dedup_rejects(lib, kw, needle):
     (dict(nbytes=0), "multiple"),
     (dict(nbytes=-16384), "multiple"),
     (dict(nbytes=16384 + 16), "multiple"),
-    (dict(bpw=0), "blocks_per_wave"),
+    (dict(bpw=-1), "blocks_per_wave"),
+    (dict(bpw=1), "blocks_per_wave"),
     (dict(bpw=3), "blocks_per_wave"),
     (dict(bpw=32), "blocks_per_wave"),
 ])
@@ -321,6 +322,8 @@ def test_probe_sink_words_match_header():
     text = open(HEADER).read()
     m = re.search(r"#define MSA_STREAM_PROBE_SINK_WORDS (\d+)", text)
     assert m and int(m.group(1)) == msa.STREAM_PROBE_SINK_WORDS
+    m = re.search(r"#define MSA_STREAM_PROBE_PERSISTENT (\d+)", text)
+    assert m and int(m.group(1)) == msa.STREAM_PROBE_PERSISTENT
 
 
 @pytest.mark.parametrize("args,needle", [

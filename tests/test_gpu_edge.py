@@ -417,7 +417,7 @@ def test_plane_beyond_2g_elements():
 
 
 @pytest.mark.parametrize("blocks", [1, 7, 3000])
-@pytest.mark.parametrize("bpw", [2, 4, 8, 16])
+@pytest.mark.parametrize("bpw", [msa.STREAM_PROBE_PERSISTENT, 2, 4, 8, 16])
 def test_stream_read_probe_reads_every_byte(blocks, bpw):
     """The streaming-read probe (the benchmark's ceiling for the scorer) reads
     every byte once at every shape: its xor of all the buffer's dwords equals
