@@ -1,19 +1,22 @@
 // Streaming-read probe: how fast this device streams a buffer that is read
 // once, with no other work.
 //
-// Each 64-lane wave reads kBlocks consecutive 16 KiB blocks (2, 4, 8 or 16).
 // Per block, every lane issues sixteen non-temporal 16-byte loads (1 KiB per
 // instruction across the wave), so a wave holds a whole block in flight, and
-// folds the loaded dwords into a running xor. Workgroups hold four waves and
-// the grid covers the buffer at once, so the hardware keeps as many waves
-// resident as fit. Measured on MI355X with an event pair around each launch
-// after a cache eviction, two blocks per wave streamed 512 MiB fastest
-// (80-82 us) among the plain read shapes tried (registers or LDS DMA,
-// persistent or not, one or four waves per workgroup, 2 to 32 blocks per
-// wave); over 4 GiB, sixteen blocks per wave streamed fastest. A wave xors its
-// lanes' values together and adds the result to one of the sink's words with
-// one atomic xor (spread over the words: one word taking all 16 384 atomics
-// of a 512 MiB read made the launch take 208 us instead of 85 us).
+// folds the loaded dwords into a running xor. Two kinds of grid, four waves
+// per workgroup:
+//  * covering: each wave reads kBlocks consecutive 16 KiB blocks (2, 4, 8 or
+//    16) and the grid covers the buffer at once, so the hardware keeps as
+//    many waves resident as fit;
+//  * persistent: one wave per SIMD, each reading one contiguous run.
+// Launched back to back over rotating buffers (the way the scorer is timed),
+// the persistent grid reads fastest at 512 MiB and at 4 GiB (figures at the
+// kernel). With an event pair around each launch after a cache eviction, two
+// blocks per wave had read 512 MiB fastest (80-82 us) among the covering
+// shapes. A wave xors its lanes' values together and adds the result to one
+// of the sink's words with one atomic xor (spread over the words: one word
+// taking all 16 384 atomics of a 512 MiB read made the launch take 208 us
+// instead of 85 us).
 #include "stream_probe.h"
 
 namespace msa {
